@@ -1,0 +1,323 @@
+"""Pins for the CPU oracle against things other than itself.
+
+Each check is chosen so that a plausible slip in the oracle fails at least
+one of them: a dropped 1/sqrt(128) or q_scale (brute force, SDPA, closed
+forms), a wrong query-to-KV head map (SDPA with enable_gqa, per-group
+constants), K and V swapped (length-1 closed form), an off-by-one length
+or rows read past the length (NaN beyond L, length-1/2 forms), a sign
+error in the scale (large +/- q_scale picks argmax / argmin), a missing
+max subtraction (large q_scale overflows), and double rounding in the final
+fp16 conversion.
+
+Definition followed: FlashInfer PR #5052 analysis page ("SM110 FP16 GQA
+decode"), section 1 docstring and section 3 SDPA comparator.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from oracle.reference import decode, decode_head, decode_ragged, effective_scale, round_fp16
+import workloads
+
+H, G, D = 32, 8, 128
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand_inputs(rng, B, C, sigma_k=1.0):
+    q = rng.standard_normal((B, H, D)).astype(np.float16)
+    kv = rng.standard_normal((B, 2, G, C, D)).astype(np.float16)
+    kv[:, 0] = (kv[:, 0].astype(np.float32) * sigma_k).astype(np.float16)
+    return q, kv
+
+
+# ---------------------------------------------------------------- P1 brute
+@pytest.mark.parametrize("C", [1, 2, 3, 5, 8])
+def test_matches_fsum_brute_force_every_length(C):
+    rng = np.random.default_rng(100 + C)
+    lens = list(range(C + 1)) + [-3, C + 5]      # every L in [0, C] plus clamping
+    B = len(lens)
+    q, kv = _rand_inputs(rng, B, C)
+    qf = q.astype(np.float64).tolist()
+    kvf = kv.astype(np.float64).tolist()
+    for q_scale in (0.0, 0.5, 1.0, 3.7, -1.0):
+        got = decode(q, kv, np.array(lens, np.int32), q_scale)
+        ref = np.array(brute.decode_brute(qf, kvf, lens, q_scale))
+        scale = max(1.0, float(np.abs(ref).max()))
+        assert np.abs(got - ref).max() <= 1e-12 * scale, (C, q_scale)
+
+
+def test_matches_mpmath_at_40_digits():
+    rng = np.random.default_rng(7)
+    q, kv = _rand_inputs(rng, 1, 9, sigma_k=2.0)
+    lens = np.array([9], np.int32)
+    for q_scale in (1.0, 2.5):
+        got = decode(q, kv, lens, q_scale)
+        for h in (0, 5, 31):
+            g = h // 4
+            ref = brute.decode_head_mp(q[0, h].astype(float).tolist(),
+                                       kv[0, 0, g].astype(float).tolist(),
+                                       kv[0, 1, g].astype(float).tolist(), q_scale)
+            assert np.abs(got[0, h] - np.array(ref)).max() <= 1e-14
+
+
+# ---------------------------------------------------------------- P2 library routine
+def _sdpa_f64(q, kv, lens, q_scale):
+    import torch
+    import torch.nn.functional as F
+
+    B, C = q.shape[0], kv.shape[3]
+    tq = torch.from_numpy(q.astype(np.float64)).unsqueeze(2)          # [B,32,1,128]
+    tk = torch.from_numpy(kv[:, 0].astype(np.float64))                # [B,8,C,128]
+    tv = torch.from_numpy(kv[:, 1].astype(np.float64))
+    L = torch.from_numpy(np.clip(np.asarray(lens, np.int64), 0, C))
+    mask = (torch.arange(C)[None, :] < L[:, None])[:, None, None, :]  # [B,1,1,C]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                       scale=effective_scale(q_scale), enable_gqa=True)
+    return o.squeeze(2).numpy()
+
+
+@pytest.mark.parametrize("name", workloads.PAGE_SHAPES)
+def test_matches_torch_sdpa_float64_page_shapes(name):
+    w = workloads.get(name)
+    kv = w.dense_kv()
+    got = decode(w.q, kv, w.seq_lens, w.q_scale)
+    ref = _sdpa_f64(w.q, kv, w.seq_lens, w.q_scale)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_matches_torch_sdpa_float64_odd_capacity():
+    rng = np.random.default_rng(11)
+    q, kv = _rand_inputs(rng, 3, 257, sigma_k=2.0)
+    lens = np.array([257, 1, 130], np.int32)
+    for q_scale in (1.0, 0.5, -2.0):
+        got = decode(q, kv, lens, q_scale)
+        ref = _sdpa_f64(q, kv, lens, q_scale)
+        assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_sdpa_and_oracle_agree_that_empty_prefix_gives_zeros():
+    import torch
+
+    rng = np.random.default_rng(12)
+    q, kv = _rand_inputs(rng, 2, 16)
+    lens = np.array([0, 16], np.int32)
+    got = decode(q, kv, lens, 1.0)
+    assert np.all(got[0] == 0.0)
+    ref = _sdpa_f64(q, kv, lens, 1.0)
+    if not np.all(np.isfinite(ref[0])):
+        pytest.skip(f"torch {torch.__version__} SDPA returns non-finite rows for an empty mask")
+    assert np.all(ref[0] == 0.0)
+    assert np.abs(got[1] - ref[1]).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- P3 closed forms
+def test_length_one_returns_v_row_exactly():
+    rng = np.random.default_rng(13)
+    q, kv = _rand_inputs(rng, 2, 5)
+    got = decode(q, kv, np.array([1, 1], np.int32), 3.0)
+    for b in range(2):
+        for h in range(H):
+            assert np.array_equal(got[b, h], kv[b, 1, h // 4, 0].astype(np.float64))
+
+
+def test_length_two_is_a_sigmoid_mix():
+    rng = np.random.default_rng(14)
+    q, kv = _rand_inputs(rng, 1, 4)
+    q_scale = 1.7
+    got = decode(q, kv, np.array([2], np.int32), q_scale)
+    c = float(np.float32(q_scale)) / math.sqrt(128)
+    for h in range(H):
+        g = h // 4
+        qv = q[0, h].astype(float)
+        k0, k1 = kv[0, 0, g, 0].astype(float), kv[0, 0, g, 1].astype(float)
+        d = c * (math.fsum(qv * k0) - math.fsum(qv * k1))   # s0 - s1
+        w0 = 1.0 / (1.0 + math.exp(-d))
+        w1 = 1.0 / (1.0 + math.exp(d))
+        ref = w0 * kv[0, 1, g, 0].astype(float) + w1 * kv[0, 1, g, 1].astype(float)
+        assert np.abs(got[0, h] - ref).max() <= 1e-13
+
+
+def test_zero_scale_gives_mean_of_valid_rows():
+    rng = np.random.default_rng(15)
+    q, kv = _rand_inputs(rng, 2, 40)
+    lens = np.array([37, 40], np.int32)
+    got = decode(q, kv, lens, 0.0)
+    for b in range(2):
+        for g in range(G):
+            V = kv[b, 1, g, :lens[b]].astype(float)
+            mean = np.array([math.fsum(V[:, d]) / lens[b] for d in range(D)])
+            for h in range(4 * g, 4 * g + 4):
+                assert np.abs(got[b, h] - mean).max() <= 1e-14
+
+
+def test_equal_keys_give_mean_of_valid_rows():
+    rng = np.random.default_rng(16)
+    q, kv = _rand_inputs(rng, 1, 33)
+    kv[0, 0, :, :, :] = kv[0, 0, :, :1, :]           # every key row equal
+    got = decode(q, kv, np.array([33], np.int32), 2.0)
+    for g in range(G):
+        V = kv[0, 1, g].astype(float)
+        mean = np.array([math.fsum(V[:, d]) / 33 for d in range(D)])
+        assert np.abs(got[0, 4 * g:4 * g + 4] - mean).max() <= 1e-14
+
+
+def test_constant_v_rows_return_the_constant():
+    rng = np.random.default_rng(17)
+    q, kv = _rand_inputs(rng, 2, 64, sigma_k=2.0)
+    const = rng.standard_normal((2, G, 1, D)).astype(np.float16)
+    kv[:, 1] = np.broadcast_to(const, (2, G, 64, D))
+    got = decode(q, kv, np.array([64, 50], np.int32), 1.0)
+    for b in range(2):
+        for h in range(H):
+            ref = const[b, h // 4, 0].astype(float)
+            assert np.abs(got[b, h] - ref).max() <= 1e-15 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_large_scale_selects_extreme_score_row(sign):
+    # With a huge |q_scale| the softmax becomes a hard max over q.k (or a
+    # hard min for a negative scale). Integer-valued q and K make the dot
+    # products exact and distinct.
+    rng = np.random.default_rng(18)
+    C = 24
+    q = rng.integers(-3, 4, (1, H, D)).astype(np.float16)
+    kv = np.zeros((1, 2, G, C, D), np.float16)
+    kv[0, 0] = rng.integers(-3, 4, (G, C, D)).astype(np.float16)
+    kv[0, 1] = rng.standard_normal((G, C, D)).astype(np.float16)
+    got = decode(q, kv, np.array([C], np.int32), sign * 1e5)
+    for h in range(H):
+        g = h // 4
+        dots = [int(np.dot(q[0, h].astype(np.int64), kv[0, 0, g, i].astype(np.int64)))
+                for i in range(C)]
+        order = sorted(range(C), key=lambda i: sign * dots[i], reverse=True)
+        if sign * dots[order[0]] == sign * dots[order[1]]:
+            continue  # tie: the max is shared by two rows
+        assert np.abs(got[0, h] - kv[0, 1, g, order[0]].astype(float)).max() <= 1e-12
+
+
+def test_each_query_head_reads_kv_head_h_div_4():
+    # V of KV head g is the constant g+1; output head h must read h//4 + 1.
+    rng = np.random.default_rng(19)
+    q, kv = _rand_inputs(rng, 1, 8)
+    for g in range(G):
+        kv[0, 1, g] = np.float16(g + 1)
+    got = decode(q, kv, np.array([8], np.int32), 1.0)
+    for h in range(H):
+        assert np.abs(got[0, h] - float(h // 4 + 1)).max() <= 1e-14
+
+
+# ---------------------------------------------------------------- P4 invariants
+def test_permuting_valid_positions_is_invariant():
+    rng = np.random.default_rng(20)
+    q, kv = _rand_inputs(rng, 2, 100)
+    lens = np.array([100, 77], np.int32)
+    ref = decode(q, kv, lens, 1.0)
+    kv2 = kv.copy()
+    for b in range(2):
+        perm = rng.permutation(lens[b])
+        kv2[b][:, :, :lens[b]] = kv[b][:, :, perm]
+    got = decode(q, kv2, lens, 1.0)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_contents_beyond_length_have_no_effect():
+    rng = np.random.default_rng(21)
+    q, kv = _rand_inputs(rng, 3, 50)
+    lens = np.array([1, 25, 49], np.int32)
+    ref = decode(q, kv, lens, 1.0)
+    kv2 = kv.copy()
+    for b in range(3):
+        kv2[b, :, :, lens[b]:] = np.float16(np.nan)
+        kv2[b, 0, :, lens[b]:][..., ::7] = np.float16(np.inf)
+    got = decode(q, kv2, lens, 1.0)
+    assert np.array_equal(got, ref)
+
+
+def test_scaling_v_by_two_scales_output_exactly():
+    rng = np.random.default_rng(22)
+    q, kv = _rand_inputs(rng, 1, 64)
+    lens = np.array([61], np.int32)
+    ref = decode(q, kv, lens, 1.0)
+    kv2 = kv.copy()
+    kv2[:, 1] *= np.float16(2)
+    assert np.array_equal(decode(q, kv2, lens, 1.0), 2.0 * ref)
+
+
+def test_doubling_k_and_halving_scale_is_exact():
+    rng = np.random.default_rng(23)
+    q, kv = _rand_inputs(rng, 1, 64)
+    lens = np.array([64], np.int32)
+    ref = decode(q, kv, lens, 1.5)
+    kv2 = kv.copy()
+    kv2[:, 0] *= np.float16(2)
+    assert np.array_equal(decode(q, kv2, lens, 0.75), ref)
+
+
+def test_batch_entries_are_independent_and_ragged_form_agrees():
+    w = workloads.get("page_b4_c256")
+    full = decode(w.q, w.dense_kv(), w.seq_lens, w.q_scale)
+    rag = decode_ragged(w.q, w.k_valid, w.v_valid, w.q_scale)
+    assert np.array_equal(full, rag)
+    for b in range(w.batch):
+        one = decode(w.q[b:b + 1], w.dense_kv()[b:b + 1], w.seq_lens[b:b + 1], w.q_scale)
+        assert np.array_equal(one[0], full[b])
+
+
+def test_sampled_rows_match_full_decode():
+    w = workloads.get("page_b4_c256")
+    kv = w.dense_kv()
+    full = decode(w.q, kv, w.seq_lens, w.q_scale)
+    rows = [(0, 3), (2, 17), (3, 31)]
+    part = decode(w.q, kv, w.seq_lens, w.q_scale, rows=rows)
+    for b, h in rows:
+        assert np.array_equal(part[b, h], full[b, h])
+
+
+# ---------------------------------------------------------------- final rounding
+def test_fp16_rounding_is_single_and_nearest_even():
+    # 1 + 2^-11 + 2^-40 lies just above the midpoint of 1 and 1 + 2^-10:
+    # a direct conversion rounds up; going through float32 would first drop
+    # the 2^-40 and then tie-break down to 1.0.
+    x = 1.0 + 2.0 ** -11 + 2.0 ** -40
+    assert round_fp16(np.array([x])).view(np.uint16)[0] == 0x3C01
+    assert np.float16(np.float32(x)).view(np.uint16) == 0x3C00
+    assert round_fp16(np.array([1.0 + 2.0 ** -11])).view(np.uint16)[0] == 0x3C00  # tie -> even
+    assert round_fp16(np.array([65520.0]))[0] == np.inf                            # overflow
+
+
+# ---------------------------------------------------------------- inputs
+def test_generator_is_reproducible_and_follows_recipe():
+    a, b = workloads.get("b8_c4096_nanfill"), workloads.get("b8_c4096_nanfill")
+    assert np.array_equal(a.q.view(np.uint16), b.q.view(np.uint16))
+    assert np.array_equal(a.seq_lens, b.seq_lens)
+    for x, y in zip(a.k_valid, b.k_valid):
+        assert np.array_equal(x.view(np.uint16), y.view(np.uint16))
+    assert a.batch == 8 and a.capacity == 4096 and a.fill == "nan"
+    assert np.all((a.seq_lens >= 1) & (a.seq_lens <= 4096))
+    kv = a.dense_kv()
+    for i in range(8):
+        L = int(a.seq_lens[i])
+        assert np.all(np.isnan(kv[i, :, :, L:].astype(np.float32)))
+        assert not np.any(np.isnan(kv[i, :, :, :L].astype(np.float32)))
+
+
+def test_skewed_lengths_recipe():
+    rng = np.random.default_rng(4)
+    lens = workloads._cfg4_lengths(rng)
+    assert lens.shape == (64,)
+    assert np.sum((lens >= 16) & (lens <= 512)) == 58
+    assert np.sum((lens >= 8192) & (lens <= 16384)) == 6
+
+
+def test_page_shapes_match_golden_fixture():
+    with open(os.path.join(HERE, "golden", "page4_shapes.json")) as f:
+        gold = json.load(f)
+    for s in gold["shapes"]:
+        w = workloads.get(s["name"])
+        assert w.batch == s["batch"] and w.capacity == s["capacity"]
+        assert w.seq_lens.tolist() == s["lengths"]

@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for single-token FP16 GQA decode.
+
+This module only draws and lays out inputs; it holds none of the decode
+arithmetic. Both the CPU oracle (through the tests and the benchmark's CPU
+leg) and the HIP path consume what it produces.
+
+Shapes follow the decode API documented on the FlashInfer PR #5052 analysis
+page ("SM110 FP16 GQA decode", section 1, the ``sm110_gqa_decode``
+docstring): ``q [batch, 32, 128]`` fp16, stacked ``kv [batch, 2, 8,
+capacity, 128]`` fp16 (index 0 of axis 1 is K, 1 is V), int32
+``sequence_lengths [batch]``. The named workloads are the five synthetic
+configurations of this library plus the four benchmark shapes printed in the
+same page's performance tables.
+
+Draw order (fixed, so a seed reproduces the same bytes):
+  1. sequence lengths (if random),
+  2. q = standard_normal((B, 32, 128), float32) * sigma_q -> fp16 (RNE),
+  3. for b in 0..B-1: K_b = standard_normal((8, L_b, 128)) * sigma_k -> fp16,
+     then V_b the same way with sigma_v.
+Only the valid prefix [0, L_b) of each sequence is drawn. Slots beyond L_b
+are filled with zeros, or with fp16 quiet NaN (0x7E00) when the workload says
+so; a correct decode never reads them.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Dict, List, Optional
+
+import numpy as np
+
+NUM_Q_HEADS = 32
+NUM_KV_HEADS = 8
+HEAD_DIM = 128
+
+FP16_QNAN_BITS = 0x7E00
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode step's inputs, with the valid K/V prefixes kept ragged.
+
+    ``k_valid[b]`` and ``v_valid[b]`` are fp16 arrays of shape
+    ``[8, L_b, 128]``; the dense stacked cache is materialised on demand by
+    :meth:`dense_kv` (host) or :meth:`kv_to_device` (GPU), so that a 4 GiB
+    cache is never built on the host unless asked for.
+    """
+
+    name: str
+    q: np.ndarray                 # fp16 [B, 32, 128]
+    seq_lens: np.ndarray          # int32 [B]
+    capacity: int
+    q_scale: float
+    k_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
+    v_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
+    fill: str = "zero"            # "zero" or "nan": contents beyond L_b
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def valid_lengths(self) -> np.ndarray:
+        """Lengths clamped to [0, capacity], as the decode interprets them."""
+        return np.clip(self.seq_lens.astype(np.int64), 0, self.capacity)
+
+    @property
+    def kv_bytes_read(self) -> int:
+        """K+V bytes of the valid prefixes: sum(L_b) * 2 * 8 * 128 * 2 B."""
+        return int(self.valid_lengths.sum()) * 2 * NUM_KV_HEADS * HEAD_DIM * 2
+
+    def fill_value_bits(self) -> int:
+        return FP16_QNAN_BITS if self.fill == "nan" else 0
+
+    def dense_kv(self) -> np.ndarray:
+        """Host fp16 ``[B, 2, 8, C, 128]`` cache with the fill beyond L_b."""
+        B, C = self.batch, self.capacity
+        kv = np.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=np.float16)
+        kv.view(np.uint16)[...] = self.fill_value_bits()
+        for b in range(B):
+            L = self.k_valid[b].shape[1]
+            kv[b, 0, :, :L, :] = self.k_valid[b]
+            kv[b, 1, :, :L, :] = self.v_valid[b]
+        return kv
+
+    def kv_to_device(self, device):
+        """Build the dense cache directly in device memory (torch tensor)."""
+        import torch
+
+        B, C = self.batch, self.capacity
+        kv = torch.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=torch.float16, device=device)
+        kv.view(torch.int16).fill_(np.int16(np.uint16(self.fill_value_bits())).item())
+        for b in range(B):
+            L = self.k_valid[b].shape[1]
+            if L:
+                kv[b, 0, :, :L, :].copy_(torch.from_numpy(self.k_valid[b]))
+                kv[b, 1, :, :L, :].copy_(torch.from_numpy(self.v_valid[b]))
+        return kv
+
+
+def _normal_fp16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x = x * np.float32(sigma)
+    return x.astype(np.float16)
+
+
+def build(
+    name: str,
+    seed: int,
+    capacity: int,
+    lengths: Callable[[np.random.Generator], np.ndarray] | List[int] | np.ndarray,
+    *,
+    q_scale: float = 1.0,
+    sigma_q: float = 1.0,
+    sigma_k: float = 1.0,
+    sigma_v: float = 1.0,
+    fill: str = "zero",
+) -> Workload:
+    """Draw a workload. ``lengths`` is a list or a callable taking the rng.
+
+    Lengths may lie outside [0, capacity] (tests of clamping); only
+    ``clip(L_b, 0, capacity)`` rows are drawn.
+    """
+    rng = np.random.default_rng(seed)
+    if callable(lengths):
+        lens = np.asarray(lengths(rng), dtype=np.int64)
+    else:
+        lens = np.asarray(lengths, dtype=np.int64)
+    B = int(lens.shape[0])
+    q = _normal_fp16(rng, (B, NUM_Q_HEADS, HEAD_DIM), sigma_q)
+    k_valid, v_valid = [], []
+    for b in range(B):
+        L = int(min(max(lens[b], 0), capacity))
+        k_valid.append(_normal_fp16(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_k))
+        v_valid.append(_normal_fp16(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_v))
+    return Workload(name, q, lens.astype(np.int32), int(capacity), float(q_scale),
+                    k_valid, v_valid, fill)
+
+
+def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
+    # 90% short-prefix sequences, 10% long ones: 58 + 6 of 64, then shuffled.
+    short = rng.integers(16, 512, 58, endpoint=True)
+    long_ = rng.integers(8192, 16384, 6, endpoint=True)
+    return rng.permutation(np.concatenate([short, long_]))
+
+
+# Name -> (description, factory). The five synthetic decode workloads, then
+# the four benchmark shapes printed in the PR #5052 page's timing tables
+# (batch/capacity/valid lengths exactly as printed there).
+WORKLOADS: Dict[str, tuple] = {
+    "b1_c256_len200": (
+        "batch 1, capacity 256, length 200, N(0,1), q_scale 1.0",
+        lambda: build("b1_c256_len200", 1, 256, [200]),
+    ),
+    "b8_c4096_nanfill": (
+        "batch 8, capacity 4096, lengths U[1,4096], N(0,1), NaN beyond each length, q_scale 1.0",
+        lambda: build("b8_c4096_nanfill", 2, 4096,
+                      lambda r: r.integers(1, 4096, 8, endpoint=True), fill="nan"),
+    ),
+    "b32_c8192_qs05": (
+        "batch 32, capacity 8192, lengths U[1024,8192], N(0,1), q_scale 0.5",
+        lambda: build("b32_c8192_qs05", 3, 8192,
+                      lambda r: r.integers(1024, 8192, 32, endpoint=True), q_scale=0.5),
+    ),
+    "b64_c16384_skewed": (
+        "batch 64, capacity 16384, 58 lengths U[16,512] + 6 lengths U[8192,16384] shuffled, "
+        "q,V ~ N(0,1), K ~ N(0, std 2), q_scale 1.0",
+        lambda: build("b64_c16384_skewed", 4, 16384, _cfg4_lengths, sigma_k=2.0),
+    ),
+    "b2_c131072_long": (
+        "batch 2, capacity 131072, lengths [131072, 65537], N(0,1), q_scale 1.0",
+        lambda: build("b2_c131072_long", 5, 131072, [131072, 65537]),
+    ),
+    "page_b1_c64": (
+        "page shape: batch 1, capacity 64, lengths [1]",
+        lambda: build("page_b1_c64", 11, 64, [1]),
+    ),
+    "page_b4_c256": (
+        "page shape: batch 4, capacity 256, lengths [64, 127, 191, 256]",
+        lambda: build("page_b4_c256", 12, 256, [64, 127, 191, 256]),
+    ),
+    "page_b1_c1024": (
+        "page shape: batch 1, capacity 1024, lengths [1024]",
+        lambda: build("page_b1_c1024", 13, 1024, [1024]),
+    ),
+    "page_b1_c4096": (
+        "page shape: batch 1, capacity 4096, lengths [3968]",
+        lambda: build("page_b1_c4096", 14, 4096, [3968]),
+    ),
+}
+
+# The five synthetic workloads in order (small first).
+SYNTHETIC = ["b1_c256_len200", "b8_c4096_nanfill", "b32_c8192_qs05",
+             "b64_c16384_skewed", "b2_c131072_long"]
+PAGE_SHAPES = ["page_b1_c64", "page_b4_c256", "page_b1_c1024", "page_b1_c4096"]
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name][1]()
+
+
+def describe(name: str) -> str:
+    return WORKLOADS[name][0]
