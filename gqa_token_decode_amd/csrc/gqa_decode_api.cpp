@@ -1,0 +1,353 @@
+// C-ABI layer of libgqa_decode.so: argument validation, per-device set-up,
+// workspace cache, launch, error reporting. Declarations and the contract
+// are in include/gqa_decode.h.
+//
+// Conventions taken from the binding launchers described on the FlashInfer
+// PR #5563 analysis page (section 2, launcher changes): every buffer must be
+// on one device, the launch is scoped to that device rather than requiring
+// it to be current (the previous current device is restored), and bad
+// arguments are reported as errors before anything is launched. The exact-
+// architecture gate mirrors the "exact SM110" loading rule of the PR #5052
+// page (section 2): here the kernels are built for gfx950 only.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <cmath>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "gqa_decode.h"
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kQBytesPerSeq = (size_t)GQA_NUM_Q_HEADS * GQA_HEAD_DIM * 2;           // 8 KiB
+constexpr size_t kKvBytesPerPos = (size_t)2 * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * 2;    // 4 KiB
+constexpr int kItemsPerCuDefault = 4;
+constexpr int kMinChunkDefault = 64;
+// Forced chunk lengths may not make the workspace exceed this.
+constexpr size_t kMaxForcedWorkspace = (size_t)4 << 30;
+
+thread_local std::string t_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return code;
+}
+
+struct DeviceInfo {
+  bool ready = false;
+  int status = GQA_OK;
+  int cus = 0;
+  std::string arch;
+};
+
+struct Workspace {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+
+struct ProfileRecord {
+  hipEvent_t ev[3];
+};
+
+std::mutex g_mu;
+std::vector<DeviceInfo> g_devices;
+std::vector<Workspace> g_workspaces;
+bool g_profiling = false;
+std::vector<ProfileRecord> g_profile;
+
+int env_int(const char* name, int fallback, int lo, int hi) {
+  const char* s = getenv(name);
+  if (!s || !*s) return fallback;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  if (*end || v < lo || v > hi) return fallback;
+  return (int)v;
+}
+
+// Per-device facts, cached. Caller holds g_mu.
+const DeviceInfo& device_info(int dev) {
+  if ((int)g_devices.size() <= dev) g_devices.resize(dev + 1);
+  DeviceInfo& di = g_devices[dev];
+  if (di.ready) return di;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    di.status = GQA_ERR_LAUNCH;
+    di.arch = "?";
+  } else {
+    di.arch = prop.gcnArchName;
+    di.cus = prop.multiProcessorCount;
+    // gcnArchName looks like "gfx950:sramecc+:xnack-".
+    di.status = strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                        (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':')
+                    ? GQA_OK
+                    : GQA_ERR_UNSUPPORTED_ARCH;
+  }
+  di.ready = true;
+  return di;
+}
+
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_chunk) {
+  gqa::SplitConfig cfg;
+  const int per_cu = env_int("GQA_DECODE_ITEMS_PER_CU", kItemsPerCuDefault, 1, 64);
+  cfg.target_items = (di.cus > 0 ? di.cus : 256) * per_cu;
+  cfg.min_chunk = env_int("GQA_DECODE_MIN_CHUNK", kMinChunkDefault, 1, 1 << 30);
+  cfg.forced_chunk = forced_chunk;
+  return cfg;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Device that owns `p`, or -1 if `p` is not device-accessible memory.
+int pointer_device(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return -1;
+  return attr.device;
+}
+
+// Workspace for (dev, stream) of at least `bytes`. Caller holds g_mu and
+// has made `dev` current.
+void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
+  for (Workspace& w : g_workspaces) {
+    if (w.device == dev && w.stream == stream) {
+      if (w.bytes >= bytes) return w.ptr;
+      // Earlier calls on this stream may still read the old buffer.
+      if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
+        *status = fail(GQA_ERR_LAUNCH, "gqa_decode: could not release the old workspace");
+        w.ptr = nullptr;
+        w.bytes = 0;
+        return nullptr;
+      }
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        w.ptr = nullptr;
+        *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu workspace bytes failed", bytes);
+        return nullptr;
+      }
+      w.bytes = bytes;
+      return w.ptr;
+    }
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu workspace bytes failed", bytes);
+    return nullptr;
+  }
+  g_workspaces.push_back(Workspace{dev, stream, p, bytes});
+  return p;
+}
+
+int check_args(const void* q, const void* kv, const int32_t* seq_lens, const void* out, int batch,
+               int capacity, int chunk_len) {
+  if (!q || !kv || !seq_lens || !out)
+    return fail(GQA_ERR_NULL, "gqa_decode: q, kv, seq_lens and out must be non-NULL");
+  if (batch <= 0 || capacity <= 0)
+    return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: batch (%d) and capacity (%d) must be positive",
+                batch, capacity);
+  if (batch > (1 << 24))
+    return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: batch %d exceeds the supported 2^24", batch);
+  // kv bytes = batch * capacity * 4096 must fit in int64 (it always does for
+  // int batch and capacity, but keep the guard explicit).
+  const double kv_bytes = (double)batch * (double)capacity * (double)kKvBytesPerPos;
+  if (kv_bytes >= 9.2e18)
+    return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: kv size overflows 64-bit offsets");
+  if (chunk_len < 0)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode: chunk_len must be >= 0, got %d", chunk_len);
+  if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)out) & 15u)
+    return fail(GQA_ERR_MISALIGNED, "gqa_decode: q, kv and out must be 16-byte aligned");
+  if ((uintptr_t)seq_lens & 3u)
+    return fail(GQA_ERR_MISALIGNED, "gqa_decode: seq_lens must be 4-byte aligned");
+  const size_t qb = (size_t)batch * kQBytesPerSeq;
+  const size_t kvb = (size_t)batch * (size_t)capacity * kKvBytesPerPos;
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, kv, kvb) ||
+      overlaps(out, qb, seq_lens, (size_t)batch * 4))
+    return fail(GQA_ERR_ALIAS, "gqa_decode: out must not overlap q, kv or seq_lens");
+  return GQA_OK;
+}
+
+int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* out, float q_scale,
+                int batch, int capacity, int chunk_len, hipStream_t stream) {
+  int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len);
+  if (st != GQA_OK) return st;
+  if (!std::isfinite(q_scale))
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_scale must be finite");
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return fail(GQA_ERR_NO_DEVICE, "gqa_decode: no HIP device is visible");
+  }
+  const int dev = pointer_device(q);
+  if (dev < 0) return fail(GQA_ERR_DEVICE_MISMATCH, "gqa_decode: q is not device memory");
+  if (pointer_device(kv) != dev || pointer_device(out) != dev || pointer_device(seq_lens) != dev)
+    return fail(GQA_ERR_DEVICE_MISMATCH,
+                "gqa_decode: q, kv, seq_lens and out must be device memory on one device");
+
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+  if (prev != dev && hipSetDevice(dev) != hipSuccess)
+    return fail(GQA_ERR_LAUNCH, "gqa_decode: hipSetDevice(%d) failed", dev);
+
+  st = GQA_OK;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    const DeviceInfo& di = device_info(dev);
+    if (di.status != GQA_OK) {
+      st = fail(di.status, "gqa_decode: device %d is %s; this library is built for gfx950", dev,
+                di.arch.c_str());
+    } else {
+      const gqa::SplitConfig cfg = split_config(di, chunk_len);
+      const long long items = gqa::max_work_items(batch, capacity, cfg);
+      const size_t ws_bytes = items > 0 ? gqa::workspace_bytes_for_items(items) : 0;
+      if (items <= 0) {
+        st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs more than 2^31 work items");
+      } else if (chunk_len > 0 && ws_bytes > kMaxForcedWorkspace) {
+        st = fail(GQA_ERR_BAD_ARG,
+                  "gqa_decode: chunk_len %d is too small for batch %d and capacity %d "
+                  "(workspace would be %zu bytes)",
+                  chunk_len, batch, capacity, ws_bytes);
+      } else {
+        void* ws = get_workspace(dev, stream, ws_bytes, &st);
+        if (ws) {
+          // Scores are formed as dot * q_scale / sqrt(128) * log2(e), so the
+          // kernels can use the hardware base-2 exponential.
+          const double scale = (double)q_scale / std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
+          hipEvent_t* ev = nullptr;
+          if (g_profiling) {
+            ProfileRecord rec;
+            bool ok = true;
+            for (int i = 0; i < 3; ++i) ok = ok && hipEventCreate(&rec.ev[i]) == hipSuccess;
+            if (ok) {
+              g_profile.push_back(rec);
+              ev = g_profile.back().ev;
+            }
+          }
+          const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, (float)scale, batch,
+                                                  capacity, cfg, items, ws, stream, ev);
+          if (e != hipSuccess)
+            st = fail(GQA_ERR_LAUNCH, "gqa_decode: kernel launch failed: %s", hipGetErrorString(e));
+        }
+      }
+    }
+  }
+  if (prev >= 0 && prev != dev) (void)hipSetDevice(prev);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out, float q_scale,
+               int batch, int capacity, hipStream_t stream) {
+  return decode_impl(q, kv, seq_lens, out, q_scale, batch, capacity, 0, stream);
+}
+
+int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, void* out,
+                       float q_scale, int batch, int capacity, int chunk_len, hipStream_t stream) {
+  return decode_impl(q, kv, seq_lens, out, q_scale, batch, capacity, chunk_len, stream);
+}
+
+size_t gqa_decode_workspace_bytes(int batch, int capacity) {
+  if (batch <= 0 || capacity <= 0) return 0;
+  int dev = 0, ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0 || hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  const DeviceInfo& di = device_info(dev);
+  const long long items = gqa::max_work_items(batch, capacity, split_config(di, 0));
+  return items > 0 ? gqa::workspace_bytes_for_items(items) : 0;
+}
+
+void gqa_decode_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+  for (Workspace& w : g_workspaces) {
+    if (hipSetDevice(w.device) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(w.ptr);
+    }
+  }
+  g_workspaces.clear();
+  if (prev >= 0) (void)hipSetDevice(prev);
+  (void)hipGetLastError();
+}
+
+const char* gqa_decode_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "success";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_BAD_SHAPE: return "invalid batch or capacity";
+    case GQA_ERR_MISALIGNED: return "misaligned buffer";
+    case GQA_ERR_ALIAS: return "output overlaps an input";
+    case GQA_ERR_NO_DEVICE: return "no HIP device";
+    case GQA_ERR_UNSUPPORTED_ARCH: return "device is not gfx950";
+    case GQA_ERR_ALLOC: return "workspace allocation failed";
+    case GQA_ERR_LAUNCH: return "kernel launch or HIP runtime call failed";
+    case GQA_ERR_BAD_ARG: return "invalid scalar argument";
+    case GQA_ERR_DEVICE_MISMATCH: return "buffer not device memory or on another device";
+    default: return "unknown status";
+  }
+}
+
+const char* gqa_decode_last_error(void) { return t_last_error.c_str(); }
+
+int gqa_decode_profile_begin(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_profiling = true;
+  return GQA_OK;
+}
+
+int gqa_decode_profile_end(double* partial_ms, double* combine_ms, int* calls) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  double p = 0.0, c = 0.0;
+  int n = 0, st = GQA_OK;
+  for (ProfileRecord& r : g_profile) {
+    float a = 0.f, b = 0.f;
+    if (hipEventSynchronize(r.ev[2]) != hipSuccess ||
+        hipEventElapsedTime(&a, r.ev[0], r.ev[1]) != hipSuccess ||
+        hipEventElapsedTime(&b, r.ev[1], r.ev[2]) != hipSuccess) {
+      st = fail(GQA_ERR_LAUNCH, "gqa_decode_profile_end: event query failed");
+    } else {
+      p += a;
+      c += b;
+      ++n;
+    }
+    for (int i = 0; i < 3; ++i) (void)hipEventDestroy(r.ev[i]);
+  }
+  g_profile.clear();
+  g_profiling = false;
+  if (partial_ms) *partial_ms = p;
+  if (combine_ms) *combine_ms = c;
+  if (calls) *calls = n;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+/*
+ * gqa_decode.h -- C ABI of the MI355X (gfx950) FP16 grouped-query-attention
+ * single-token decode library (libgqa_decode.so).
+ *
+ * The operation is the one documented for `sm110_gqa_decode` on the
+ * FlashInfer PR #5052 analysis page ("SM110 FP16 GQA decode"):
+ *   - section 1 (docstring): q is a contiguous FP16 [batch, 32, 128] tensor,
+ *     kv is a contiguous FP16 stacked cache [batch, 2, 8, capacity, 128],
+ *     sequence lengths are a contiguous device int32 [batch] tensor, the
+ *     output has q's shape and is owned by the caller, and q_scale is an
+ *     extra query scale applied before the standard 1/sqrt(128);
+ *   - section 2: 32 query heads, 8 KV heads, head dim 128, 4:1 grouping;
+ *   - section 3 (benchmark): the result equals PyTorch SDPA with a boolean
+ *     length mask, scale 1/sqrt(128) and enable_gqa=True.
+ *
+ * For every batch entry b and query head h (g = h / 4):
+ *   L   = clamp(seq_lens[b], 0, capacity)
+ *   s_i = (q_scale / sqrt(128)) * dot(q[b,h,:], kv[b,0,g,i,:])   for i < L
+ *   out[b,h,:] = sum_i softmax(s)_i * kv[b,1,g,i,:]               (fp16, RNE)
+ * Rows i >= L are never read. L == 0 yields a zero row.
+ *
+ * Arithmetic: fp16 inputs, fp32 accumulation for the dot products, the
+ * softmax and the weighted sum, one round-to-nearest-even to fp16 at the end.
+ *
+ * All entry points are thread-safe. Compute entry points only enqueue work
+ * on `stream` (no host synchronisation); a device-side fault surfaces at the
+ * caller's next synchronisation. Every call reports its outcome as a
+ * gqa_status; the thread-local text of the last failure is available from
+ * gqa_decode_last_error().
+ */
+#ifndef GQA_DECODE_H_
+#define GQA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_NUM_Q_HEADS 32
+#define GQA_NUM_KV_HEADS 8
+#define GQA_HEAD_DIM 128
+
+/* Status codes returned by the entry points (0 = success). */
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_NULL = -1,             /* a required pointer is NULL                        */
+  GQA_ERR_BAD_SHAPE = -2,        /* batch <= 0, capacity <= 0, or sizes overflow       */
+  GQA_ERR_MISALIGNED = -3,       /* q, kv or out not 16-byte aligned; seq_lens not 4   */
+  GQA_ERR_ALIAS = -4,            /* out overlaps q, kv or seq_lens                     */
+  GQA_ERR_NO_DEVICE = -5,        /* no HIP device visible                              */
+  GQA_ERR_UNSUPPORTED_ARCH = -6, /* the device is not gfx950 (MI355X class)            */
+  GQA_ERR_ALLOC = -7,            /* workspace allocation failed                        */
+  GQA_ERR_LAUNCH = -8,           /* a kernel launch or runtime call failed             */
+  GQA_ERR_BAD_ARG = -9,          /* an out-of-range scalar argument (e.g. chunk_len)   */
+  GQA_ERR_DEVICE_MISMATCH = -10  /* a pointer is not device memory, or buffers live on
+                                    different devices                                  */
+} gqa_status;
+
+/*
+ * gqa_decode -- decode one token of FP16 GQA for every sequence in a batch.
+ *
+ * q        device, fp16 [batch, 32, 128], contiguous, 16-byte aligned (read).
+ * kv       device, fp16 [batch, 2, 8, capacity, 128], contiguous, 16-byte
+ *          aligned; kv[b,0] holds K and kv[b,1] holds V (read). Offsets are
+ *          computed in 64 bits, so caches above 2^31 elements are supported.
+ * seq_lens device, int32 [batch] (read on the device only; values are clamped
+ *          to [0, capacity]; the host never reads them, so the call can be
+ *          captured in a HIP graph once the workspace exists).
+ * out      device, fp16 [batch, 32, 128], contiguous, 16-byte aligned,
+ *          caller-allocated; must not overlap q, kv or seq_lens (written).
+ * q_scale  extra score scale, applied together with 1/sqrt(128).
+ * batch, capacity  positive sizes.
+ * stream   HIP stream to enqueue on (NULL = the device's null stream).
+ *
+ * All buffers must live on one device; the kernels run on that device and
+ * the caller's current device is restored before returning. The library
+ * keeps a cached fp32 workspace per (device, stream) for split-KV partial
+ * results; it is grown with hipMalloc on first need (so the first call on a
+ * new stream, or with a larger batch, must not be under graph capture).
+ * Calls that overlap on one stream are ordered by the stream; calls on
+ * different streams use different workspaces.
+ *
+ * Returns GQA_OK, or a negative gqa_status with nothing enqueued.
+ */
+int gqa_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
+               float q_scale, int batch, int capacity, hipStream_t stream);
+
+/*
+ * gqa_decode_chunked -- gqa_decode with an explicit split-KV chunk length.
+ *
+ * Same arguments and semantics as gqa_decode, plus:
+ * chunk_len  0 selects the automatic, length-driven split (identical to
+ *            gqa_decode). A positive value caps the chunk length: sequence b
+ *            is split into n_b = ceil(L_b / chunk_len) chunks of near-equal
+ *            length, each reduced by one workgroup, then combined by a
+ *            log-sum-exp merge. Negative values return GQA_ERR_BAD_ARG.
+ * Used to exercise specific chunk counts (1, 2, many) and to study the split.
+ */
+int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, void* out,
+                       float q_scale, int batch, int capacity, int chunk_len,
+                       hipStream_t stream);
+
+/*
+ * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace
+ * the automatic split needs for (batch, capacity) on the current device.
+ * Returns 0 for invalid sizes or when no device is available.
+ */
+size_t gqa_decode_workspace_bytes(int batch, int capacity);
+
+/*
+ * gqa_decode_release_workspace -- free every cached workspace (all devices
+ * and streams). Synchronises each device that held one. Safe to call at any
+ * time no decode is in flight on another host thread.
+ */
+void gqa_decode_release_workspace(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* gqa_decode_status_string(int status);
+
+/* Text of the calling thread's last failure ("" if none). Valid until the
+ * thread's next failing call. */
+const char* gqa_decode_last_error(void);
+
+/*
+ * Kernel timing aid. gqa_decode_profile_begin() makes subsequent decode
+ * calls (any thread) record HIP events around each of their two kernels on
+ * the call's stream. gqa_decode_profile_end() waits for the recorded events,
+ * returns the summed durations in milliseconds of the split-KV partial
+ * kernel and of the combine kernel and the number of calls recorded, then
+ * stops recording. Any output pointer may be NULL.
+ */
+int gqa_decode_profile_begin(void);
+int gqa_decode_profile_end(double* partial_ms, double* combine_ms, int* calls);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* GQA_DECODE_H_ */

@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libgqa_decode.so loads and exports every function declared in
+  include/gqa_decode.h.
+* Argument errors are reported with the documented status codes before any
+  device work; with no device visible a valid-looking call reports
+  GQA_ERR_NO_DEVICE instead of crashing.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+OK, NULL, BAD_SHAPE, MISALIGNED, ALIAS, NO_DEVICE, ARCH, ALLOC, LAUNCH, BAD_ARG, MISMATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def _status_codes():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(GQA_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import gqa_token_decode_amd as g
+    from gqa_token_decode_amd import build as b
+
+    srcs = [os.path.join(b.CSRC, s) for s in b.SOURCES] + [HEADER, os.path.join(b.CSRC, "launch.h")]
+    if (not os.path.exists(b.LIB_PATH)
+            or os.path.getmtime(b.LIB_PATH) < max(os.path.getmtime(s) for s in srcs)):
+        b.build()
+    return g.load_library()
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_header_declares_the_documented_entry_points():
+    names = _declared_functions()
+    assert names == sorted([
+        "gqa_decode", "gqa_decode_chunked", "gqa_decode_workspace_bytes",
+        "gqa_decode_release_workspace", "gqa_decode_status_string", "gqa_decode_last_error",
+        "gqa_decode_profile_begin", "gqa_decode_profile_end"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from gqa_token_decode_amd import build as b
+
+    nm = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", nm, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_codes_match_header_and_have_text(lib):
+    codes = _status_codes()
+    assert codes["GQA_OK"] == OK and codes["GQA_ERR_NO_DEVICE"] == NO_DEVICE
+    assert codes["GQA_ERR_DEVICE_MISMATCH"] == MISMATCH and codes["GQA_ERR_BAD_ARG"] == BAD_ARG
+    texts = set()
+    for v in codes.values():
+        t = lib.gqa_decode_status_string(v).decode()
+        assert t and t != "unknown status"
+        texts.add(t)
+    assert len(texts) == len(codes)
+    assert lib.gqa_decode_status_string(12345).decode() == "unknown status"
+
+
+def _call(lib, q=0x10000, kv=0x20000000, lens=0x30000, out=0x40000, scale=1.0, B=2, C=64,
+          chunk=None):
+    if chunk is None:
+        return lib.gqa_decode(q, kv, lens, out, scale, B, C, None)
+    return lib.gqa_decode_chunked(q, kv, lens, out, scale, B, C, chunk, None)
+
+
+def test_argument_errors_are_reported_before_device_work(lib):
+    assert _call(lib, q=None) == NULL
+    assert _call(lib, kv=None) == NULL
+    assert _call(lib, lens=None) == NULL
+    assert _call(lib, out=None) == NULL
+    assert "non-NULL" in lib.gqa_decode_last_error().decode()
+    assert _call(lib, B=0) == BAD_SHAPE
+    assert _call(lib, C=0) == BAD_SHAPE
+    assert _call(lib, B=-3) == BAD_SHAPE
+    assert _call(lib, q=0x10008) == MISALIGNED
+    assert _call(lib, out=0x40004) == MISALIGNED
+    assert _call(lib, lens=0x30002) == MISALIGNED
+    # out inside q (q is 2 * 8 KiB long), inside kv, or covering seq_lens
+    assert _call(lib, out=0x10000 + 0x2000) == ALIAS
+    assert _call(lib, out=0x20000000 + 4096 * 64) == ALIAS
+    assert _call(lib, out=0x30000 - 0x10) == ALIAS
+    assert _call(lib, chunk=-1) == BAD_ARG
+    assert _call(lib, scale=float("nan")) == BAD_ARG
+    assert _call(lib, scale=float("inf")) == BAD_ARG
+
+
+def test_valid_looking_call_without_device_memory(lib):
+    # No GPU here: the library must say so. With a GPU, these made-up
+    # addresses are not device memory.
+    expected = MISMATCH if _gpu_visible() else NO_DEVICE
+    assert _call(lib) == expected
+    assert _call(lib, chunk=7) == expected
+    assert lib.gqa_decode_last_error().decode()
+
+
+def test_helpers_without_device(lib):
+    if _gpu_visible():
+        pytest.skip("host-only behaviour")
+    assert lib.gqa_decode_workspace_bytes(4, 256) == 0
+    assert lib.gqa_decode_workspace_bytes(0, 256) == 0
+    lib.gqa_decode_release_workspace()          # no-op, must not crash
+    p, c, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    assert lib.gqa_decode_profile_begin() == OK
+    assert lib.gqa_decode_profile_end(ctypes.byref(p), ctypes.byref(c), ctypes.byref(n)) == OK
+    assert n.value == 0
+
+
+def test_python_binding_rejects_bad_tensors_before_the_library():
+    import torch
+
+    import gqa_token_decode_amd as g
+
+    q = torch.zeros(2, 32, 128, dtype=torch.float16)
+    kv = torch.zeros(2, 2, 8, 16, 128, dtype=torch.float16)
+    lens = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        g.gqa_decode(q, kv, lens)
+    with pytest.raises(TypeError):
+        g.gqa_decode(q.float(), kv, lens)
+    with pytest.raises(TypeError):
+        g.gqa_decode(q, kv, lens.long())
+    with pytest.raises(ValueError):
+        g.gqa_decode(q[:, :16], kv, lens)
+    with pytest.raises(ValueError):
+        g.gqa_decode(q, kv.transpose(3, 4), lens)
+
+
+def test_product_path_never_imports_the_oracle():
+    # The binding, the build script and the C/HIP sources must not reach
+    # the oracle package.
+    pkg = os.path.join(ROOT, "gqa_token_decode_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (element-wise over every output, rows of empty sequences included):
+max |gpu - fp16(oracle)| <= 2e-3 and mean |gpu - fp16(oracle)| <= 2e-4,
+where fp16(oracle) is one nearest-even rounding of the float64 result.
+Exact properties of the method (length-1 rows, contents beyond a length,
+power-of-two scaling of V, fixed-split reproducibility) are checked bitwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.reference import decode_ragged, round_fp16
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+MAX_TOL, MEAN_TOL = 2e-3, 2e-4
+DEV = "cuda:0"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _g():
+    import gqa_token_decode_amd as g
+    return g
+
+
+def _device_inputs(w, kv=None):
+    torch = _torch()
+    q = torch.from_numpy(w.q).to(DEV)
+    lens = torch.from_numpy(w.seq_lens).to(DEV)
+    if kv is None:
+        kv = w.kv_to_device(DEV)
+    return q, kv, lens
+
+
+def run(w, chunk_len=0, kv=None, q_scale=None):
+    torch = _torch()
+    q, kv, lens = _device_inputs(w, kv)
+    out = _g().gqa_decode(q, kv, lens, q_scale=w.q_scale if q_scale is None else q_scale,
+                          chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(got, ref64, label):
+    ref16 = round_fp16(ref64).astype(np.float64)
+    g64 = got.astype(np.float64)
+    assert np.all(np.isfinite(g64)), f"{label}: non-finite output"
+    d = np.abs(g64 - ref16)
+    print(f"{label}: max|d|={d.max():.3e} mean|d|={d.mean():.3e} "
+          f"max|gpu-oracle64|={np.abs(g64 - ref64).max():.3e}", flush=True)
+    assert d.max() <= MAX_TOL, f"{label}: max |d| {d.max():.3e} at {np.unravel_index(d.argmax(), d.shape)}"
+    assert d.mean() <= MEAN_TOL, f"{label}: mean |d| {d.mean():.3e}"
+
+
+def oracle_of(w, q_scale=None):
+    return decode_ragged(w.q, w.k_valid, w.v_valid, w.q_scale if q_scale is None else q_scale)
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("name", workloads.SYNTHETIC)
+def test_parity_synthetic_workloads_full_size(name):
+    print(f"case {name}", flush=True)
+    w = workloads.get(name)
+    check(run(w), oracle_of(w), name)
+
+
+@pytest.mark.parametrize("name", workloads.PAGE_SHAPES)
+def test_parity_page_shapes(name):
+    w = workloads.get(name)
+    check(run(w), oracle_of(w), name)
+
+
+@pytest.mark.parametrize("chunk_len,expected_chunks", [(1000, 1), (500, 2), (143, 7), (1, 1000)])
+def test_forced_chunk_counts(chunk_len, expected_chunks):
+    w = workloads.build("forced", 31, 1024, [1000], sigma_k=2.0)
+    assert -(-1000 // chunk_len) == expected_chunks
+    check(run(w, chunk_len=chunk_len), oracle_of(w), f"chunk_len={chunk_len}")
+
+
+@pytest.mark.parametrize("chunk_len", [0, 7, 64])
+def test_ragged_lengths_odd_capacity_and_clamping(chunk_len):
+    lens = [0, 1, 2, 3, 4, 5, 15, 16, 17, 63, 64, 65, 255, 256, 257, -5, 1000]
+    w = workloads.build("ragged", 32, 257, lens, fill="nan")
+    got = run(w, chunk_len=chunk_len)
+    for b in (0, 15):                    # L = 0 and L < 0: zero rows
+        assert np.all(got[b] == 0)
+    check(got, oracle_of(w), f"ragged chunk_len={chunk_len}")
+
+
+def test_long_sequence_with_one_row_tail():
+    w = workloads.build("tail", 33, 65600, [65537, 65600, 1])
+    check(run(w), oracle_of(w), "65537-row tail")
+
+
+@pytest.mark.parametrize("q_scale", [0.0, -1.0, 4.0, 30.0])
+def test_scale_variants(q_scale):
+    w = workloads.build("scales", 34, 700, [700, 333, 129])
+    check(run(w, q_scale=q_scale), oracle_of(w, q_scale), f"q_scale={q_scale}")
+
+
+# ---------------------------------------------------------------- exact properties
+def test_length_one_returns_v_row_bitwise():
+    w = workloads.build("len1", 35, 96, [1, 1, 1], fill="nan")
+    got = run(w)
+    for b in range(3):
+        for h in range(32):
+            assert np.array_equal(got[b, h].view(np.uint16), w.v_valid[b][h // 4, 0].view(np.uint16))
+
+
+@pytest.mark.parametrize("chunk_len", [0, 100])
+def test_contents_beyond_length_have_no_effect_bitwise(chunk_len):
+    base = workloads.build("fill", 36, 3000, [2999, 1500, 17, 3000])
+    nanw = workloads.build("fill", 36, 3000, [2999, 1500, 17, 3000], fill="nan")
+    torch = _torch()
+    garbage = base.kv_to_device(DEV)
+    # Random finite garbage (incl. huge values) beyond each length.
+    for b, L in enumerate(base.seq_lens):
+        tail = garbage[b, :, :, L:]
+        tail.copy_((torch.randn_like(tail, dtype=torch.float32) * 3e4).to(torch.float16))
+    a = run(base, chunk_len=chunk_len)
+    b_ = run(nanw, chunk_len=chunk_len)
+    c = run(base, chunk_len=chunk_len, kv=garbage)
+    assert np.array_equal(a.view(np.uint16), b_.view(np.uint16))
+    assert np.array_equal(a.view(np.uint16), c.view(np.uint16))
+
+
+def test_repeated_runs_are_bitwise_identical():
+    w = workloads.get("b8_c4096_nanfill")
+    torch = _torch()
+    q, kv, lens = _device_inputs(w)
+    g = _g()
+    outs = []
+    for _ in range(5):
+        outs.append(g.gqa_decode(q, kv, lens, q_scale=w.q_scale).cpu().numpy().view(np.uint16))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_batch_entries_independent_bitwise_with_fixed_split():
+    w = workloads.build("indep", 37, 2048, [2048, 5, 1031, 777])
+    full = run(w, chunk_len=256)
+    for b in range(w.batch):
+        one = workloads.Workload("one", w.q[b:b + 1], w.seq_lens[b:b + 1], w.capacity, w.q_scale,
+                                 w.k_valid[b:b + 1], w.v_valid[b:b + 1])
+        assert np.array_equal(run(one, chunk_len=256)[0].view(np.uint16), full[b].view(np.uint16))
+
+
+def test_doubling_v_doubles_output_bitwise():
+    w = workloads.build("v2", 38, 1500, [1500, 999])
+    w2 = workloads.Workload("v2x", w.q, w.seq_lens, w.capacity, w.q_scale, w.k_valid,
+                            [(v.astype(np.float32) * 2).astype(np.float16) for v in w.v_valid])
+    a, b = run(w), run(w2)
+    assert np.array_equal((a.astype(np.float32) * 2).astype(np.float16).view(np.uint16),
+                          b.view(np.uint16))
+
+
+def test_permuting_positions_stays_within_bar():
+    w = workloads.build("perm", 39, 2000, [2000, 1234])
+    rng = np.random.default_rng(5)
+    k2, v2 = [], []
+    for b in range(w.batch):
+        p = rng.permutation(w.k_valid[b].shape[1])
+        k2.append(w.k_valid[b][:, p].copy())
+        v2.append(w.v_valid[b][:, p].copy())
+    wp = workloads.Workload("permuted", w.q, w.seq_lens, w.capacity, w.q_scale, k2, v2)
+    ref = oracle_of(w)
+    check(run(w), ref, "original order")
+    check(run(wp), ref, "permuted order")
+
+
+def test_constant_v_returns_constant_within_one_ulp():
+    w = workloads.build("constv", 40, 900, [900, 450], sigma_k=2.0)
+    rng = np.random.default_rng(6)
+    const = rng.standard_normal((w.batch, 8, 1, 128)).astype(np.float16)
+    vv = [np.broadcast_to(const[b], w.v_valid[b].shape).copy() for b in range(w.batch)]
+    wc = workloads.Workload("constv", w.q, w.seq_lens, w.capacity, w.q_scale, w.k_valid, vv)
+    got = run(wc).astype(np.float64)
+    for b in range(w.batch):
+        for h in range(32):
+            c = const[b, h // 4, 0]
+            ulp = np.spacing(np.abs(c)).astype(np.float64)
+            assert np.all(np.abs(got[b, h] - c.astype(np.float64)) <= ulp)
+
+
+# ---------------------------------------------------------------- API behaviour
+def test_out_argument_and_side_stream():
+    torch = _torch()
+    g = _g()
+    w = workloads.get("page_b4_c256")
+    q, kv, lens = _device_inputs(w)
+    out = torch.full_like(q, float("nan"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        r = g.gqa_decode(q, kv, lens, out=out, q_scale=w.q_scale)
+    s.synchronize()
+    assert r.data_ptr() == out.data_ptr()
+    check(out.cpu().numpy(), oracle_of(w), "side stream")
+
+
+def test_workspace_reuse_after_a_larger_call():
+    # A large multi-chunk call leaves partials in the cached workspace; a
+    # following small call must not see them.
+    big = workloads.get("b2_c131072_long")
+    small = workloads.build("small", 41, 4096, [4096, 3000, 1])
+    run(big)
+    check(run(small), oracle_of(small), "after large call")
+
+
+def test_errors_are_raised_on_gpu():
+    torch = _torch()
+    g = _g()
+    w = workloads.get("page_b1_c64")
+    q, kv, lens = _device_inputs(w)
+    with pytest.raises(g.GqaDecodeError) as e:
+        g.gqa_decode(q, kv, lens, out=q)             # out aliases q
+    assert e.value.status == -4
+    buf = torch.empty(q.numel() + 4, dtype=torch.float16, device=DEV)
+    qmis = buf[4:].view(q.shape)                     # 8-byte offset: not 16-byte aligned
+    qmis.copy_(q)
+    with pytest.raises(g.GqaDecodeError) as e:
+        g.gqa_decode(qmis, kv, lens)
+    assert e.value.status == -3
+    assert g.workspace_bytes(64, 16384) > 0
+
+
+def test_kernel_timer_reports_both_kernels():
+    torch = _torch()
+    g = _g()
+    w = workloads.get("b32_c8192_qs05")
+    q, kv, lens = _device_inputs(w)
+    g.gqa_decode(q, kv, lens, q_scale=w.q_scale)
+    with g.KernelTimer() as t:
+        for _ in range(3):
+            g.gqa_decode(q, kv, lens, q_scale=w.q_scale)
+    torch.cuda.synchronize()
+    assert t.calls == 3 and t.partial_ms > 0 and t.combine_ms > 0
