@@ -157,6 +157,9 @@ def main(argv=None):
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
+            # The workspace is cached per stream: create it before capture.
+            g.gqa_decode(q, kvs[0], lens, out=out, q_scale=w.q_scale)
+            s.synchronize()
             with torch.cuda.graph(gr, stream=s):
                 for i in range(rot):
                     g.gqa_decode(q, kvs[i], lens, out=out, q_scale=w.q_scale)

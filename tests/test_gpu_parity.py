@@ -153,12 +153,18 @@ def test_batch_entries_independent_bitwise_with_fixed_split():
 
 
 def test_doubling_v_doubles_output_bitwise():
+    # Doubling V doubles every fp32 accumulator exactly, so the fp16 result
+    # doubles exactly wherever it is a normal fp16 number. (In the fp16
+    # subnormal range, rounding 2x and doubling round(x) can differ.)
     w = workloads.build("v2", 38, 1500, [1500, 999])
     w2 = workloads.Workload("v2x", w.q, w.seq_lens, w.capacity, w.q_scale, w.k_valid,
                             [(v.astype(np.float32) * 2).astype(np.float16) for v in w.v_valid])
     a, b = run(w), run(w2)
-    assert np.array_equal((a.astype(np.float32) * 2).astype(np.float16).view(np.uint16),
-                          b.view(np.uint16))
+    normal = np.abs(b.astype(np.float32)) >= 2.0 ** -13
+    assert normal.mean() > 0.99
+    doubled = (a.astype(np.float32) * 2).astype(np.float16)
+    bad = int(np.sum(doubled.view(np.uint16)[normal] != b.view(np.uint16)[normal]))
+    assert bad == 0, f"{bad} normal outputs differ from exactly doubled ones"
 
 
 def test_permuting_positions_stays_within_bar():
