@@ -3,7 +3,7 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                 [--no-cpu-baseline] [--graph]
 
-One step = one gqa_decode call (split-KV partial kernel + combine kernel)
+One step = one gqa_decode call (split-KV pieces kernel + combine kernel)
 over one batch of the named synthetic workload, inputs resident in HBM.
 To keep every step reading from HBM rather than from the 256 MB
 Infinity Cache, the step cycles through R copies of the KV cache whose
@@ -11,7 +11,7 @@ valid bytes add up to at least 1 GiB.
 
 Prints ONE JSON line:
   value       KV-read throughput: sum(L_b) * 4096 B / step time (GB/s)
-  roofline    the partial kernel's algorithmic KV bytes per launch divided
+  roofline    the pieces kernel's algorithmic KV bytes per launch divided
               by its average duration (HIP events recorded by the library
               on the launch stream, inside the timed region), against the
               8 TB/s HBM peak; `traffic` is the measured HBM bytes per launch
@@ -148,7 +148,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    partial_us = kt.partial_ms / kt.calls * 1e3
+    pieces_us = kt.pieces_ms / kt.calls * 1e3
     combine_us = kt.combine_ms / kt.calls * 1e3
 
     graph_us = None
@@ -178,7 +178,7 @@ def main(argv=None):
     res = out.float().cpu().numpy()
     assert np.all(np.isfinite(res)), "non-finite decode output"
 
-    achieved = kv_bytes / (partial_us * 1e-6) / 1e9
+    achieved = kv_bytes / (pieces_us * 1e-6) / 1e9
     traffic = traffic_from_profiles(args.workload)
     line = {
         "metric": METRIC,
@@ -201,13 +201,13 @@ def main(argv=None):
             "head_dim": 128, "sum_valid_len": sum_len, "kv_bytes_per_step": kv_bytes,
             "kv_copies_rotated": rot, "accumulate": "f32",
         },
-        "kernel_us": {"partial": round(partial_us, 3), "combine": round(combine_us, 3),
-                      "sum": round(partial_us + combine_us, 3)},
+        "kernel_us": {"pieces": round(pieces_us, 3), "combine": round(combine_us, 3),
+                      "sum": round(pieces_us + combine_us, 3)},
         "hbm_frac_of_step": round(kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "wall_ms_timed_region": round(wall_ms, 3),
         "roofline": {
             "bound": "hbm",
-            "kernel": "split_partial",
+            "kernel": "gqa_decode_pieces",
             "achieved": round(achieved, 3),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -159,11 +159,11 @@ def release_workspace() -> None:
 
 
 class KernelTimer:
-    """Context manager: per-kernel HIP-event timing of the decode calls inside.
+    """Context manager: HIP-event timing of the decode kernels launched inside.
 
-    After exit, ``partial_ms`` and ``combine_ms`` hold the summed durations of
-    the split-KV partial kernel and of the combine kernel, ``calls`` the
-    number of decode calls recorded.
+    After exit, ``pieces_ms`` and ``combine_ms`` hold the summed durations of
+    the split-KV pieces kernel and of the combine kernel (events recorded by
+    the library on each call's stream), and ``calls`` the number of calls.
     """
 
     def __enter__(self):
@@ -177,7 +177,7 @@ class KernelTimer:
         lib = load_library()
         p, c, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
         st = lib.gqa_decode_profile_end(ctypes.byref(p), ctypes.byref(c), ctypes.byref(n))
-        self.partial_ms, self.combine_ms, self.calls = p.value, c.value, n.value
+        self.pieces_ms, self.combine_ms, self.calls = p.value, c.value, n.value
         if st != 0 and exc[0] is None:
             _raise(lib, st)
         return False

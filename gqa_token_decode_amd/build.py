@@ -1,6 +1,6 @@
 """Compile libgqa_decode.so (HIP, gfx950 only) in-tree.
 
-The shared library holds the split-KV partial kernel, the log-sum-exp
+The shared library holds the split-KV pieces kernel, the log-sum-exp
 combine kernel and the C-ABI declared in include/gqa_decode.h. It is built
 ahead of time for gfx950 (MI355X); there is no JIT path and no other target.
 """

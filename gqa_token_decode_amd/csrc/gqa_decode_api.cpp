@@ -29,8 +29,8 @@ namespace {
 
 constexpr size_t kQBytesPerSeq = (size_t)GQA_NUM_Q_HEADS * GQA_HEAD_DIM * 2;           // 8 KiB
 constexpr size_t kKvBytesPerPos = (size_t)2 * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * 2;    // 4 KiB
-constexpr int kItemsPerCuDefault = 4;
-constexpr int kMinChunkDefault = 64;
+constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
+constexpr int kMinPieceDefault = 128;      // rows; keeps tiny decodes from over-splitting
 // Forced chunk lengths may not make the workspace exceed this.
 constexpr size_t kMaxForcedWorkspace = (size_t)4 << 30;
 
@@ -50,9 +50,11 @@ struct DeviceInfo {
   bool ready = false;
   int status = GQA_OK;
   int cus = 0;
+  int resident = 0;   // decode workgroups per CU
   std::string arch;
 };
 
+// fp32 partial results, cached per (device, stream).
 struct Workspace {
   int device;
   hipStream_t stream;
@@ -96,17 +98,23 @@ const DeviceInfo& device_info(int dev) {
                         (prop.gcnArchName[6] == 0 || prop.gcnArchName[6] == ':')
                     ? GQA_OK
                     : GQA_ERR_UNSUPPORTED_ARCH;
+    if (di.status == GQA_OK) {
+      di.resident = gqa::resident_workgroups_per_cu();
+      if (di.resident <= 0) di.resident = 1;
+    }
   }
   di.ready = true;
   return di;
 }
 
-gqa::SplitConfig split_config(const DeviceInfo& di, int forced_chunk) {
+// One equal piece per workgroup that can be resident at once (times an
+// optional factor), so the whole decode runs in a single round.
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece) {
   gqa::SplitConfig cfg;
-  const int per_cu = env_int("GQA_DECODE_ITEMS_PER_CU", kItemsPerCuDefault, 1, 64);
-  cfg.target_items = (di.cus > 0 ? di.cus : 256) * per_cu;
-  cfg.min_chunk = env_int("GQA_DECODE_MIN_CHUNK", kMinChunkDefault, 1, 1 << 30);
-  cfg.forced_chunk = forced_chunk;
+  const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
+  cfg.pieces = (di.cus > 0 ? di.cus : 256) * (di.resident > 0 ? di.resident : 1) * per_slot;
+  cfg.min_piece = env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30);
+  cfg.forced_piece = forced_piece;
   return cfg;
 }
 
@@ -126,39 +134,36 @@ int pointer_device(const void* p) {
   return attr.device;
 }
 
-// Workspace for (dev, stream) of at least `bytes`. Caller holds g_mu and
-// has made `dev` current.
+// Workspace of at least `bytes` for (dev, stream). Caller holds g_mu and
+// has made `dev` current. Sets *status on error.
 void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
-  for (Workspace& w : g_workspaces) {
-    if (w.device == dev && w.stream == stream) {
-      if (w.bytes >= bytes) return w.ptr;
-      // Earlier calls on this stream may still read the old buffer.
-      if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
-        *status = fail(GQA_ERR_LAUNCH, "gqa_decode: could not release the old workspace");
-        w.ptr = nullptr;
-        w.bytes = 0;
-        return nullptr;
-      }
-      w.ptr = nullptr;
-      w.bytes = 0;
-      if (hipMalloc(&w.ptr, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        w.ptr = nullptr;
-        *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu workspace bytes failed", bytes);
-        return nullptr;
-      }
-      w.bytes = bytes;
-      return w.ptr;
+  Workspace* ws = nullptr;
+  for (Workspace& w : g_workspaces)
+    if (w.device == dev && w.stream == stream) ws = &w;
+  if (ws && ws->bytes >= bytes) return ws->ptr;
+  if (!ws) {
+    g_workspaces.push_back(Workspace{dev, stream, nullptr, 0});
+    ws = &g_workspaces.back();
+  }
+  if (ws->ptr) {
+    // Earlier calls on this stream may still use the old buffer.
+    const bool ok = hipStreamSynchronize(stream) == hipSuccess && hipFree(ws->ptr) == hipSuccess;
+    ws->ptr = nullptr;
+    ws->bytes = 0;
+    if (!ok) {
+      (void)hipGetLastError();
+      *status = fail(GQA_ERR_LAUNCH, "gqa_decode: could not release the old workspace");
+      return nullptr;
     }
   }
-  void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) {
+  if (hipMalloc(&ws->ptr, bytes) != hipSuccess) {
     (void)hipGetLastError();
+    ws->ptr = nullptr;
     *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu workspace bytes failed", bytes);
     return nullptr;
   }
-  g_workspaces.push_back(Workspace{dev, stream, p, bytes});
-  return p;
+  ws->bytes = bytes;
+  return ws->ptr;
 }
 
 int check_args(const void* q, const void* kv, const int32_t* seq_lens, const void* out, int batch,
@@ -221,20 +226,20 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
                 di.arch.c_str());
     } else {
       const gqa::SplitConfig cfg = split_config(di, chunk_len);
-      const long long items = gqa::max_work_items(batch, capacity, cfg);
-      const size_t ws_bytes = items > 0 ? gqa::workspace_bytes_for_items(items) : 0;
-      if (items <= 0) {
-        st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs more than 2^31 work items");
-      } else if (chunk_len > 0 && ws_bytes > kMaxForcedWorkspace) {
+      const long long grid = gqa::grid_for(batch, capacity, cfg);
+      const size_t pbytes = grid > 0 ? gqa::partial_bytes_for_grid(grid) : 0;
+      if (grid <= 0 || grid > 0x7fffffffLL) {
+        st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs more than 2^31 workgroups");
+      } else if (chunk_len > 0 && pbytes > kMaxForcedWorkspace) {
         st = fail(GQA_ERR_BAD_ARG,
                   "gqa_decode: chunk_len %d is too small for batch %d and capacity %d "
-                  "(workspace would be %zu bytes)",
-                  chunk_len, batch, capacity, ws_bytes);
+                  "(partials would need %zu bytes)",
+                  chunk_len, batch, capacity, pbytes);
       } else {
-        void* ws = get_workspace(dev, stream, ws_bytes, &st);
+        void* ws = get_workspace(dev, stream, pbytes, &st);
         if (ws) {
           // Scores are formed as dot * q_scale / sqrt(128) * log2(e), so the
-          // kernels can use the hardware base-2 exponential.
+          // kernel can use the hardware base-2 exponential.
           const double scale = (double)q_scale / std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
           hipEvent_t* ev = nullptr;
           if (g_profiling) {
@@ -247,7 +252,7 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
             }
           }
           const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, (float)scale, batch,
-                                                  capacity, cfg, items, ws, stream, ev);
+                                                  capacity, cfg, grid, ws, stream, ev);
           if (e != hipSuccess)
             st = fail(GQA_ERR_LAUNCH, "gqa_decode: kernel launch failed: %s", hipGetErrorString(e));
         }
@@ -281,8 +286,9 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   }
   std::lock_guard<std::mutex> lock(g_mu);
   const DeviceInfo& di = device_info(dev);
-  const long long items = gqa::max_work_items(batch, capacity, split_config(di, 0));
-  return items > 0 ? gqa::workspace_bytes_for_items(items) : 0;
+  if (di.status != GQA_OK) return 0;
+  const long long grid = gqa::grid_for(batch, capacity, split_config(di, 0));
+  return gqa::partial_bytes_for_grid(grid);
 }
 
 void gqa_decode_release_workspace(void) {
@@ -325,27 +331,28 @@ int gqa_decode_profile_begin(void) {
   return GQA_OK;
 }
 
-int gqa_decode_profile_end(double* partial_ms, double* combine_ms, int* calls) {
+int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls) {
   std::lock_guard<std::mutex> lock(g_mu);
-  double p = 0.0, c = 0.0;
+  double tp = 0.0, tc = 0.0;
   int n = 0, st = GQA_OK;
   for (ProfileRecord& r : g_profile) {
-    float a = 0.f, b = 0.f;
+    float a = 0.f, c = 0.f;
     if (hipEventSynchronize(r.ev[2]) != hipSuccess ||
         hipEventElapsedTime(&a, r.ev[0], r.ev[1]) != hipSuccess ||
-        hipEventElapsedTime(&b, r.ev[1], r.ev[2]) != hipSuccess) {
+        hipEventElapsedTime(&c, r.ev[1], r.ev[2]) != hipSuccess) {
+      (void)hipGetLastError();
       st = fail(GQA_ERR_LAUNCH, "gqa_decode_profile_end: event query failed");
     } else {
-      p += a;
-      c += b;
+      tp += a;
+      tc += c;
       ++n;
     }
     for (int i = 0; i < 3; ++i) (void)hipEventDestroy(r.ev[i]);
   }
   g_profile.clear();
   g_profiling = false;
-  if (partial_ms) *partial_ms = p;
-  if (combine_ms) *combine_ms = c;
+  if (pieces_ms) *pieces_ms = tp;
+  if (combine_ms) *combine_ms = tc;
   if (calls) *calls = n;
   return st;
 }

@@ -1,38 +1,42 @@
-// Split-KV FP16 GQA single-token decode for gfx950 (MI355X, CDNA4, wave64).
+// FP16 GQA single-token decode for gfx950 (MI355X, CDNA4, wave64).
 //
 // Operation (FlashInfer PR #5052 analysis page, "SM110 FP16 GQA decode":
 // section 1 docstring, section 2 specialisation, section 3 SDPA comparator):
 // for batch entry b and query head h, with g = h / 4 and L = clamp(len, 0, C),
-//   out[b,h] = softmax_i(scale * q[b,h] . K[b,g,i]) . V[b,g,i],  i < L.
+//   out[b,h] = softmax_i(q_scale / sqrt(128) * q[b,h] . K[b,g,i]) . V[b,g,i],  i < L.
 //
-// Two kernels on one stream:
-//   1. split_partial: one 256-thread workgroup per work item (b, g, chunk).
-//      The four query heads of KV head g share every K/V row the workgroup
-//      loads, so each row of the cache crosses HBM exactly once. A sequence
-//      with a single chunk writes its fp16 output directly; otherwise the
-//      workgroup writes an fp32 partial (running max, softmax denominator,
-//      unnormalised weighted sum of V) for each of its four heads.
-//   2. split_combine: one workgroup per (b, h) merges the partials of a
-//      multi-chunk sequence with a log-sum-exp rescale, and writes zeros
-//      for empty sequences.
-// Both kernels derive the same split from seq_lens on the device (the host
-// never reads the lengths): chunk target T from the total valid length,
-// n_b = ceil(L_b / T) near-equal chunks per sequence, items numbered
-// b-major, then KV head, then chunk.
+// Work split (decided on the device from seq_lens; the host never reads them)
+//   The valid rows of all (b, g) pairs are laid end to end, b-major then g:
+//   segment (b, g) covers flat rows [8*P_b + g*L_b, +L_b), P_b = L_0 + ... +
+//   L_{b-1}. That flat range of 8*sum(L) rows is cut into equal pieces of Q
+//   rows, one per workgroup, so every workgroup streams the same number of
+//   K/V bytes and all finish together. A piece covers the tail of one
+//   segment, any number of whole segments and the head of another.
+//   A segment inside one piece is finished by that workgroup (normalised
+//   fp16 output). A segment cut by piece boundaries gets one fp32 partial
+//   (running max, softmax denominator, unnormalised weighted V sum) per
+//   piece, and a second kernel (one workgroup per sequence and query head)
+//   merges them with a log-sum-exp rescale. The kernel boundary makes the partials visible
+//   across XCDs; merging inside the first kernel would need device-scope
+//   release fences (an L2 write-back per workgroup), which cost far more.
 //
-// Register layout inside the partial kernel (per wave of 64 lanes):
-//   lane = 16 * r + j: row slot r in 0..3, column block j in 0..15.
-//   One 16-byte load per lane moves 4 consecutive 256-byte rows (1 KiB,
-//   fully coalesced); lane (r, j) holds elements 8j..8j+7 of row r.
-//   q for the four heads is held the same way (8 fp16 per head per lane).
-//   QK: 4 packed fp16 dot products (fp32 accumulate) per head, then a
-//   16-lane DPP butterfly leaves the full score in every lane of the row.
-//   Each row slot keeps its own online-softmax state (m, l) and its own
-//   fp32 accumulators acc[head][8]; the 16 row states of the workgroup
-//   (4 waves x 4 slots) are merged through LDS at the end.
-// Rows at or beyond the chunk end are never loaded: their scores are set to
-// -inf and their weights to 0 by selects, so no garbage or NaN stored beyond
-// a sequence's length can reach the arithmetic.
+// Per-wave compute on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
+// accumulate), 32 rows per iteration; the 4 waves of a workgroup take
+// interleaved 32-row tiles of their range:
+//   QK: A = 16 K rows x 32 depth, loaded from HBM straight into registers
+//       (lane (G, j) takes row j, depth 32kk + 8G .. +7, for kk = 0..3);
+//       B = q^T with the group's 4 heads in columns 0..3 and zero columns
+//       4..15. D gives lane (G, j) the scores of rows 4G..4G+3 for head j.
+//   Online softmax in base 2 (scores carry log2(e)); rows at or beyond the
+//   range end are never loaded and get score -inf and weight 0 by selects.
+//   PV: A = weights (rows = heads, k = 32 rows), B = 32 V rows x 16 head-dim
+//       columns. Two QK tiles' D layout already is one PV step's A layout
+//       (lane (G, j) holds head j at rows 4G+r and 16+4G+r), so the weights
+//       stay in their lanes; V takes the same row order through a per-wave
+//       LDS tile read back transposed (ds_read_b64_tr_b16).
+//   Weights are split into fp16 high and low parts (two MFMAs) so the sum
+//   keeps fp32-level accuracy; the denominator sums the fp32 weights.
+// Each K/V row crosses HBM once, for all 4 query heads of its group.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,6 +47,12 @@ namespace gqa {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef unsigned uint4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 constexpr int kQHeads = 32;
 constexpr int kKvHeads = 8;
@@ -50,45 +60,36 @@ constexpr int kGroup = kQHeads / kKvHeads;   // 4 query heads per KV head
 constexpr int kDim = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRowSlots = 4;                 // rows covered by one wave-wide 16-byte load
-constexpr int kUnroll = 4;                   // K (and V) loads per lane per iteration
-constexpr int kWaveRows = kRowSlots * kUnroll;    // 16 positions per wave per iteration
-constexpr int kBlockRows = kWaves * kWaveRows;    // 64 positions per workgroup per iteration
-constexpr int kStates = kWaves * kRowSlots;       // 16 softmax states per workgroup
+constexpr int kTile = 32;                    // rows per wave per iteration
+constexpr int kVStride = kDim + 8;           // LDS row stride of a V tile, in halves
+constexpr int kSlotFloats = kGroup * (2 + kDim);   // one partial: 4 x (max, den) + 4 x 128 sums
 
-struct PlanParams {
+struct Params {
+  const _Float16* q;
+  const _Float16* kv;
   const int32_t* seq_lens;
+  _Float16* out;
+  float2* ws_ml;       // [2 * grid][4] (max, denominator) per partial and head
+  float* ws_acc;       // [2 * grid][4][128] unnormalised weighted V sums
   int batch;
   int capacity;
-  int target_items;
-  int min_chunk;
-  int forced_chunk;
+  int pieces;          // automatic split: number of equal pieces
+  int min_piece;       // automatic split: lower bound on the piece length
+  int forced_piece;    // > 0: fixed piece length
+  float scale_log2;    // q_scale / sqrt(128) * log2(e)
 };
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xF, 0xF, false));
+__device__ __forceinline__ uint4_t load_nt(const _Float16* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint4_t*>(p));
 }
-
-// Sum over the 16 lanes of a DPP row; every lane receives the same value
-// (each step adds a pair of equal operands in either order).
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f32<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
-  x += dpp_f32<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
-  x += dpp_f32<0x141>(x);   // row_half_mirror: lane i <- 7 - i within 8
-  x += dpp_f32<0x140>(x);   // row_mirror: lane i <- 15 - i within 16
-  return x;
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- planning
 // Workgroup-wide helpers; every thread of the workgroup must call them.
 
-__device__ long long block_sum_ll(long long v, long long* red) {
+__device__ long long block_sum(long long v, long long* red) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -99,17 +100,17 @@ __device__ long long block_sum_ll(long long v, long long* red) {
   return t;
 }
 
-// Inclusive prefix sum over the workgroup's 256 threads; also returns the total.
-__device__ int block_incl_scan(int v, int* red, int* total) {
+// Inclusive prefix sum over the workgroup; *total receives the sum of all.
+__device__ long long block_scan(long long v, long long* red, long long* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o);
+    const long long t = __shfl_up(v, o);
     if (lane >= o) v += t;
   }
   __syncthreads();
   if (lane == 63) red[wv] = v;
   __syncthreads();
-  int before = 0, all = 0;
+  long long before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
     before += (i < wv) ? red[i] : 0;
@@ -119,334 +120,432 @@ __device__ int block_incl_scan(int v, int* red, int* total) {
   return v + before;
 }
 
-// Chunk-length cap T for this call, from the total valid length.
-__device__ int chunk_cap(const PlanParams& p, long long* red) {
-  long long part = 0;
-  for (int b = threadIdx.x; b < p.batch; b += kThreads) part += clamp_len(p.seq_lens[b], p.capacity);
-  const long long total = block_sum_ll(part, red);
-  if (p.forced_chunk > 0) return p.forced_chunk;
-  long long t = (8 * total + p.target_items - 1) / p.target_items;
-  if (t < p.min_chunk) t = p.min_chunk;
-  if (t > p.capacity) t = p.capacity;
-  return (int)(t < 1 ? 1 : t);
-}
-
-__device__ __forceinline__ int num_chunks(int len, int cap) {
-  return len == 0 ? 0 : (int)(((long long)len + cap - 1) / cap);
-}
-
-struct Item {
-  int b, g, c, n, len;
-};
-
-// Locate work item w. Returns false (uniformly) if w is past the last item.
-__device__ bool find_item(int w, const PlanParams& p, int cap, Item* out, int* scan_red,
-                          int* found) {
-  if (threadIdx.x == 0) found[0] = -1;
-  long long before = 0;   // chunks of all sequences before this block of b
-  for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
+// Batch entry b whose flat rows [8*P_b, 8*P_{b+1}) hold flat row p, and
+// 8*P_b. p must be below 8 * sum(L).
+__device__ void locate(long long p, const Params& P, long long* red, long long* found,
+                       int* found_b) {
+  if (threadIdx.x == 0) *found_b = -1;
+  long long before = 0;
+  for (int b0 = 0; b0 < P.batch; b0 += kThreads) {
     const int b = b0 + threadIdx.x;
-    const int len = b < p.batch ? clamp_len(p.seq_lens[b], p.capacity) : 0;
-    const int n = num_chunks(len, cap);
-    int total;
-    const int incl = block_incl_scan(n, scan_red, &total);
-    const long long lo = 8 * (before + incl - n), hi = 8 * (before + incl);
-    if (n > 0 && w >= lo && w < hi) {
-      found[0] = b;
-      found[1] = (int)(w - lo);
-      found[2] = n;
-      found[3] = len;
+    const long long len = b < P.batch ? clamp_len(P.seq_lens[b], P.capacity) : 0;
+    long long total;
+    const long long incl = block_scan(8 * len, red, &total);
+    const long long lo = before + incl - 8 * len;
+    if (len > 0 && p >= lo && p < lo + 8 * len) {
+      *found_b = b;
+      *found = lo;
     }
     before += total;
     __syncthreads();
-    if (found[0] >= 0) break;
+    if (*found_b >= 0) break;
   }
-  if (found[0] < 0) return false;
-  out->b = found[0];
-  out->n = found[2];
-  out->len = found[3];
-  out->g = found[1] / out->n;
-  out->c = found[1] - out->g * out->n;
-  return true;
+}
+
+struct Segment {
+  int b, g, len;
+  long long off;     // first flat row of the segment
+};
+
+// ---------------------------------------------------------------- compute
+struct WaveAcc {
+  float4_t O[8];     // PV accumulators (D layout): lane (0, j), reg r = head r, column 16*db + j
+  float m;           // running max of head j (same in the 4 lane groups)
+  float l;           // this lane group's share of head j's denominator
+};
+
+// Accumulate rows [lo, hi) of one (b, g) segment into the wave's state. The
+// waves of the workgroup take interleaved 32-row tiles.
+__device__ __forceinline__ void accumulate_rows(const _Float16* kbase, const _Float16* vbase,
+                                                int lo, int hi, const half8_t qb[4],
+                                                float scale_log2, _Float16* vt, WaveAcc& acc) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int G = lane >> 4, j = lane & 15;
+  const float kNegInf = -__builtin_inff();
+  const int tr_row = 4 * G + (j >> 2);
+  const int tr_col = 4 * (j & 3);
+
+  for (int t0 = lo + wv * kTile; t0 < hi; t0 += kWaves * kTile) {
+    uint4_t kr[2][4], vr[8];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int pos = t0 + 16 * st + j;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        kr[st][kk] = (uint4_t){0u, 0u, 0u, 0u};
+        if (pos < hi) kr[st][kk] = load_nt(kbase + (size_t)pos * kDim + 32 * kk + 8 * G);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pos = t0 + 4 * u + G;
+      vr[u] = (uint4_t){0u, 0u, 0u, 0u};
+      if (pos < hi) vr[u] = load_nt(vbase + (size_t)pos * kDim + 8 * j);
+    }
+
+    float4_t sc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sc[st] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        sc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[st][kk]),
+                                                        qb[kk], sc[st], 0, 0, 0);
+    }
+
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      *reinterpret_cast<uint4_t*>(vt + (4 * u + G) * kVStride + 8 * j) = vr[u];
+
+    float sv[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = t0 + 16 * st + 4 * G + r;
+        const float x = pos < hi ? sc[st][r] * scale_log2 : kNegInf;
+        sv[4 * st + r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // Row t0 is below hi, so mx (and m_new) is finite; alpha is 0 on the
+    // first tile, where acc.m is still -inf.
+    const float m_new = fmaxf(acc.m, mx);
+    const float alpha = exp2_hw(acc.m - m_new);
+    acc.m = m_new;
+
+    half8_t ph, pl;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = (sv[e] == kNegInf) ? 0.f : exp2_hw(sv[e] - m_new);
+      psum += p;
+      const _Float16 hi16 = (_Float16)p;
+      ph[e] = hi16;
+      pl[e] = (_Float16)(p - (float)hi16);
+    }
+    acc.l = acc.l * alpha + psum;
+
+    // Row r of every PV tile is head r; lane h holds head h's alpha.
+    const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2),
+                a3 = __shfl(alpha, 3);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      acc.O[db][0] *= a0;
+      acc.O[db][1] *= a1;
+      acc.O[db][2] *= a2;
+      acc.O[db][3] *= a3;
+    }
+
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4_t*)(vt + tr_row * kVStride + 16 * db + tr_col));
+      const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4_t*)(vt + (16 + tr_row) * kVStride + 16 * db + tr_col));
+      half8_t vb;
+      vb.lo = __builtin_bit_cast(half4_t, b0);
+      vb.hi = __builtin_bit_cast(half4_t, b1);
+      acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vb, acc.O[db], 0, 0, 0);
+      acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, acc.O[db], 0, 0, 0);
+    }
+  }
+}
+
+struct MergeLds {
+  float m[kWaves][kGroup];
+  float l[kWaves][kGroup];
+  float acc[kWaves][kGroup][kDim];
+};
+
+// Merge the 4 waves' states. Thread t ends with head hh = t / 64 and the
+// columns d, d+1 (d = 2 * (t % 64)): max M, denominator den, sums n0, n1.
+__device__ __forceinline__ void merge_waves(const WaveAcc& acc, MergeLds& sm, float& M,
+                                            float& den, float& n0, float& n1) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int G = lane >> 4, j = lane & 15;
+  const float kNegInf = -__builtin_inff();
+  float l = acc.l + __shfl_xor(acc.l, 16);
+  l += __shfl_xor(l, 32);
+  __syncthreads();   // earlier readers of sm are done
+  if (lane < kGroup) {
+    sm.m[wv][lane] = acc.m;
+    sm.l[wv][lane] = l;
+  }
+  if (G == 0) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.acc[wv][r][16 * db + j] = acc.O[db][r];
+    }
+  }
+  __syncthreads();
+  const int hh = tid >> 6, d = (tid & 63) * 2;
+  M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][hh]);
+  den = 0.f;
+  n0 = 0.f;
+  n1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float ms = sm.m[w][hh];
+    const float wt = (ms == kNegInf) ? 0.f : exp2_hw(ms - M);   // waves without rows
+    den += wt * sm.l[w][hh];
+    n0 += wt * sm.acc[w][hh][d];
+    n1 += wt * sm.acc[w][hh][d + 1];
+  }
+}
+
+// Partial slot of a segment in piece w: 2w for the piece's first segment,
+// 2w + 1 for a segment that starts strictly inside the piece (at most one of
+// those is cut by the piece's end).
+__device__ __forceinline__ long long slot_of(long long seg_off, long long piece_start, int w) {
+  return 2LL * w + (seg_off > piece_start ? 1 : 0);
+}
+
+// Piece length Q for this call (same value in both kernels).
+__device__ __forceinline__ long long piece_len(const Params& P, long long total) {
+  if (P.forced_piece > 0) return P.forced_piece;
+  long long Q = (total + P.pieces - 1) / P.pieces;
+  return Q < P.min_piece ? P.min_piece : Q;
 }
 
 // ---------------------------------------------------------------- kernel 1
-__global__ __launch_bounds__(kThreads) void split_partial(
-    const _Float16* __restrict__ q, const _Float16* __restrict__ kv, _Float16* __restrict__ out,
-    float2* __restrict__ ws_ml, float* __restrict__ ws_acc, PlanParams pp, float scale_log2) {
-  __shared__ long long red_ll[kWaves];
-  __shared__ int red_i[kWaves];
-  __shared__ int found[4];
-  __shared__ float st_m[kStates][kGroup];
-  __shared__ float st_l[kStates][kGroup];
-  __shared__ float st_acc[kStates][kGroup][kDim];
-
-  const int cap = chunk_cap(pp, red_ll);
-  Item it;
-  if (!find_item(blockIdx.x, pp, cap, &it, red_i, found)) return;
-
-  // Near-equal chunks: every chunk is non-empty because (n-1)*cs < len.
-  const int cs = (int)(((long long)it.len + it.n - 1) / it.n);
-  const int start = it.c * cs;
-  const int end = min(start + cs, it.len);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gqa_decode_pieces(Params P) {
+  __shared__ long long red[kWaves];
+  __shared__ long long sh_found;
+  __shared__ int sh_found_b;
+  __shared__ __attribute__((aligned(16))) _Float16 vtile[kWaves][kTile * kVStride];
+  __shared__ __attribute__((aligned(16))) MergeLds sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r = lane >> 4, j = lane & 15;
+  const int G = lane >> 4, j = lane & 15;
+  const int w = blockIdx.x;
 
-  const size_t C = (size_t)pp.capacity;
-  const _Float16* kbase = kv + ((size_t)(it.b * 2 + 0) * kKvHeads + it.g) * C * kDim + 8 * j;
-  const _Float16* vbase = kv + ((size_t)(it.b * 2 + 1) * kKvHeads + it.g) * C * kDim + 8 * j;
+  long long part = 0;
+  for (int b = tid; b < P.batch; b += kThreads) part += clamp_len(P.seq_lens[b], P.capacity);
+  const long long total = 8 * block_sum(part, red);   // valid rows over all (b, g)
 
-  half2_t qf[kGroup][4];
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4*>(
-        q + ((size_t)it.b * kQHeads + it.g * kGroup + h) * kDim + 8 * j);
-    qf[h][0] = __builtin_bit_cast(half2_t, v.x);
-    qf[h][1] = __builtin_bit_cast(half2_t, v.y);
-    qf[h][2] = __builtin_bit_cast(half2_t, v.z);
-    qf[h][3] = __builtin_bit_cast(half2_t, v.w);
-  }
-
-  const float kNegInf = -__builtin_inff();
-  float m[kGroup], l[kGroup], acc[kGroup][8];
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  }
-
-  for (int base = start + wv * kWaveRows; base < end; base += kBlockRows) {
-    uint4 kr[kUnroll], vr[kUnroll];
-    bool valid[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int pos = base + kRowSlots * u + r;
-      valid[u] = pos < end;
-      kr[u] = make_uint4(0, 0, 0, 0);
-      vr[u] = make_uint4(0, 0, 0, 0);
-      if (valid[u]) {
-        kr[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)pos * kDim);
-        vr[u] = *reinterpret_cast<const uint4*>(vbase + (size_t)pos * kDim);
-      }
-    }
-
-    float s[kUnroll][kGroup];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const half2_t k0 = __builtin_bit_cast(half2_t, kr[u].x);
-      const half2_t k1 = __builtin_bit_cast(half2_t, kr[u].y);
-      const half2_t k2 = __builtin_bit_cast(half2_t, kr[u].z);
-      const half2_t k3 = __builtin_bit_cast(half2_t, kr[u].w);
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) {
-        float a = __builtin_amdgcn_fdot2(qf[h][0], k0, 0.f, false);
-        a = __builtin_amdgcn_fdot2(qf[h][1], k1, a, false);
-        a = __builtin_amdgcn_fdot2(qf[h][2], k2, a, false);
-        a = __builtin_amdgcn_fdot2(qf[h][3], k3, a, false);
-        s[u][h] = row16_sum(a);
-      }
-    }
-
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      float mx = m[h];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        s[u][h] = valid[u] ? s[u][h] * scale_log2 : kNegInf;
-        mx = fmaxf(mx, s[u][h]);
-      }
-      // mx == -inf only while this row slot has seen no valid position.
-      const float alpha = (mx == kNegInf) ? 1.f : exp2_fast(m[h] - mx);
-      m[h] = mx;
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        s[u][h] = valid[u] ? exp2_fast(s[u][h] - mx) : 0.f;
-        psum += s[u][h];
-      }
-      l[h] = l[h] * alpha + psum;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-    }
-
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const half2_t v0 = __builtin_bit_cast(half2_t, vr[u].x);
-      const half2_t v1 = __builtin_bit_cast(half2_t, vr[u].y);
-      const half2_t v2 = __builtin_bit_cast(half2_t, vr[u].z);
-      const half2_t v3 = __builtin_bit_cast(half2_t, vr[u].w);
-      const float vf[8] = {(float)v0.x, (float)v0.y, (float)v1.x, (float)v1.y,
-                           (float)v2.x, (float)v2.y, (float)v3.x, (float)v3.y};
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(s[u][h], vf[e], acc[h][e]);
-      }
+  // Empty sequences get zero rows (workgroup w takes b = w, w + grid, ...).
+  for (int b = w; b < P.batch; b += gridDim.x) {
+    if (clamp_len(P.seq_lens[b], P.capacity) == 0) {
+      uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * kQHeads * kDim);
+      dst[tid] = (uint4_t){0u, 0u, 0u, 0u};
+      dst[tid + kThreads] = (uint4_t){0u, 0u, 0u, 0u};
     }
   }
 
-  // Merge the 16 row-slot states of the workgroup.
-  const int k = wv * kRowSlots + r;
-  if (j == 0) {
+  const long long Q = piece_len(P, total);
+  const long long p0 = (long long)w * Q;
+  if (p0 >= total) return;                          // uniform: this piece is empty
+  const long long p1 = p0 + Q < total ? p0 + Q : total;
+
+  locate(p0, P, red, &sh_found, &sh_found_b);
+  Segment s;
+  s.b = sh_found_b;
+  s.len = clamp_len(P.seq_lens[s.b], P.capacity);
+  s.g = (int)((p0 - sh_found) / s.len);
+  s.off = sh_found + (long long)s.g * s.len;
+
+  _Float16* vt = vtile[wv];
+  const size_t C = (size_t)P.capacity;
+  long long cur = p0;
+  while (true) {
+    const long long seg_end = s.off + s.len;
+    const long long hi_flat = seg_end < p1 ? seg_end : p1;
+    const int lo = (int)(cur - s.off), hi = (int)(hi_flat - s.off);
+
+    // q^T as the B operand, one 32-deep slice per kk; columns >= 4 are zero.
+    half8_t qb[4];
 #pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      st_m[k][h] = m[h];
-      st_l[k][h] = l[h];
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4_t v = {0u, 0u, 0u, 0u};
+      if (j < kGroup)
+        v = *reinterpret_cast<const uint4_t*>(
+            P.q + ((size_t)s.b * kQHeads + s.g * kGroup + j) * kDim + 32 * kk + 8 * G);
+      qb[kk] = __builtin_bit_cast(half8_t, v);
     }
-  }
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    float4* dst = reinterpret_cast<float4*>(&st_acc[k][h][8 * j]);
-    dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-    dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-  }
-  __syncthreads();
+    const _Float16* kbase = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * C * kDim;
+    const _Float16* vbase = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * C * kDim;
 
-  const int hh = tid >> 6;          // head within the group
-  const int d = (tid & 63) * 2;     // two output elements per thread
-  float M = kNegInf;
+    WaveAcc acc;
 #pragma unroll
-  for (int s2 = 0; s2 < kStates; ++s2) M = fmaxf(M, st_m[s2][hh]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-#pragma unroll
-  for (int s2 = 0; s2 < kStates; ++s2) {
-    const float ms = st_m[s2][hh];
-    const float w = (ms == kNegInf) ? 0.f : exp2_fast(ms - M);
-    den += w * st_l[s2][hh];
-    n0 += w * st_acc[s2][hh][d];
-    n1 += w * st_acc[s2][hh][d + 1];
-  }
+    for (int db = 0; db < 8; ++db) acc.O[db] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    acc.m = -__builtin_inff();
+    acc.l = 0.f;
+    accumulate_rows(kbase, vbase, lo, hi, qb, P.scale_log2, vt, acc);
 
-  const int head = it.g * kGroup + hh;
-  if (it.n == 1) {
-    half2_t o;
-    o.x = (_Float16)(n0 / den);
-    o.y = (_Float16)(n1 / den);
-    *reinterpret_cast<half2_t*>(out + ((size_t)it.b * kQHeads + head) * kDim + d) = o;
-  } else {
-    const size_t slot = (size_t)blockIdx.x * kGroup + hh;
-    *reinterpret_cast<float2*>(ws_acc + slot * kDim + d) = make_float2(n0, n1);
-    if (d == 0) ws_ml[slot] = make_float2(M, den);
+    float M, den, n0, n1;
+    merge_waves(acc, sm, M, den, n0, n1);
+    const int hh = tid >> 6, d = (tid & 63) * 2;
+
+    if (s.off / Q == (seg_end - 1) / Q) {            // the segment lies in this piece
+      half2_t o;
+      o.x = (_Float16)(n0 / den);
+      o.y = (_Float16)(n1 / den);
+      *reinterpret_cast<half2_t*>(P.out + ((size_t)s.b * kQHeads + s.g * kGroup + hh) * kDim + d) = o;
+    } else {
+      const long long slot = slot_of(s.off, p0, w);
+      *reinterpret_cast<float2*>(P.ws_acc + (slot * kGroup + hh) * kDim + d) = make_float2(n0, n1);
+      if (d == 0) P.ws_ml[slot * kGroup + hh] = make_float2(M, den);
+    }
+
+    cur = hi_flat;
+    if (cur >= p1) break;
+    // Next segment: next KV head of b, else the next non-empty sequence
+    // (one exists, because rows remain below p1 <= total).
+    if (s.g + 1 < kKvHeads) {
+      s.g += 1;
+    } else {
+      int nb = s.b + 1;
+      int nl = clamp_len(P.seq_lens[nb], P.capacity);
+      while (nl == 0) {
+        ++nb;
+        nl = clamp_len(P.seq_lens[nb], P.capacity);
+      }
+      s.b = nb;
+      s.len = nl;
+      s.g = 0;
+    }
+    s.off = seg_end;
   }
 }
 
 // ---------------------------------------------------------------- kernel 2
-constexpr int kCombineSubsets = kThreads / 64;   // chunk subsets reduced in parallel
+constexpr int kCombineSubsets = kThreads / 32;   // 8 subsets x 32 four-column groups
 
-__global__ __launch_bounds__(kThreads) void split_combine(
-    _Float16* __restrict__ out, const float2* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-    PlanParams pp) {
-  __shared__ long long red_ll[kWaves];
-  __shared__ float red_f[kWaves];
-  __shared__ float part[kCombineSubsets][3][64];
+// One workgroup per (b, query head): if kernel 1 cut the segment (b, h / 4)
+// into several pieces, merge their partials for head h and write the output
+// row; otherwise exit. The max over the partials is found first, so the
+// weighted sums need no running rescale and their loads are independent.
+__global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
+  __shared__ long long red[kWaves];
+  __shared__ float redf[kWaves];
+  __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][32][5];
 
-  const int b = blockIdx.x / kQHeads;
-  const int head = blockIdx.x - b * kQHeads;
-  const int g = head / kGroup, hh = head - g * kGroup;
   const int tid = threadIdx.x;
+  const int b = blockIdx.x / kQHeads, head = blockIdx.x - b * kQHeads;
+  const int g = head / kGroup, hh = head - g * kGroup;
 
-  const int cap = chunk_cap(pp, red_ll);
-  long long before = 0;
-  for (int b2 = tid; b2 < b; b2 += kThreads)
-    before += num_chunks(clamp_len(pp.seq_lens[b2], pp.capacity), cap);
-  before = block_sum_ll(before, red_ll);
-  const int len = clamp_len(pp.seq_lens[b], pp.capacity);
-  const int n = num_chunks(len, cap);
-
-  _Float16* dst = out + ((size_t)b * kQHeads + head) * kDim;
-  if (n == 1) return;                       // written by the partial kernel
-  if (n == 0) {                             // empty prefix: zero row
-    if (tid < kDim / 2) {
-      half2_t z;
-      z.x = (_Float16)0.f;
-      z.y = (_Float16)0.f;
-      reinterpret_cast<half2_t*>(dst)[tid] = z;
-    }
-    return;
+  long long part = 0, before = 0;
+  for (int i = tid; i < P.batch; i += kThreads) {
+    const int len = clamp_len(P.seq_lens[i], P.capacity);
+    part += len;
+    if (i < b) before += len;
   }
+  const long long total = 8 * block_sum(part, red);
+  const long long off = 8 * block_sum(before, red);   // first flat row of sequence b
+  const int len = clamp_len(P.seq_lens[b], P.capacity);
+  if (len == 0) return;                                // zero row written by kernel 1
+  const long long Q = piece_len(P, total);
+  const long long s_off = off + (long long)g * len;
+  const int first_w = (int)(s_off / Q);
+  const int n = (int)((s_off + len - 1) / Q) - first_w + 1;
+  if (n == 1) return;                                  // written by kernel 1
 
-  const long long item0 = 8 * before + (long long)g * n;
-  float M = -__builtin_inff();
-  for (int c = tid; c < n; c += kThreads) M = fmaxf(M, ws_ml[(item0 + c) * kGroup + hh].x);
+  // Partial i lives in piece first_w + i; the first piece may hold it in its
+  // second slot, every later piece holds it as its first segment.
+  const long long slot0 = slot_of(s_off, (long long)first_w * Q, first_w);
+  auto slot = [&](int i) { return i == 0 ? slot0 : 2LL * (first_w + i); };
+
+  const float kNegInf = -__builtin_inff();
+  float M = kNegInf;
+  for (int i = tid; i < n; i += kThreads) M = fmaxf(M, P.ws_ml[slot(i) * kGroup + hh].x);
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) red_f[tid >> 6] = M;
+  if ((tid & 63) == 0) redf[tid >> 6] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+  M = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
 
-  const int sub = tid >> 6, dp = tid & 63;
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-  for (int c = sub; c < n; c += kCombineSubsets) {
-    const size_t slot = (size_t)(item0 + c) * kGroup + hh;
-    const float2 ml = ws_ml[slot];
-    const float2 a = *reinterpret_cast<const float2*>(ws_acc + slot * kDim + 2 * dp);
-    const float w = exp2_fast(ml.x - M);
-    den += w * ml.y;
-    n0 += w * a.x;
-    n1 += w * a.y;
+  const int sub = tid >> 5, c4 = (tid & 31) * 4;
+  float den = 0.f;
+  float4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int i = sub; i < n; i += kCombineSubsets) {
+    const long long sl = slot(i);
+    const float2 ml = P.ws_ml[sl * kGroup + hh];
+    const float4_t a = *reinterpret_cast<const float4_t*>(P.ws_acc + (sl * kGroup + hh) * kDim + c4);
+    const float wt = exp2_hw(ml.x - M);
+    den += wt * ml.y;
+    num += wt * a;
   }
-  part[sub][0][dp] = den;
-  part[sub][1][dp] = n0;
-  part[sub][2][dp] = n1;
+  xs[sub][tid & 31][0] = den;
+  xs[sub][tid & 31][1] = num[0];
+  xs[sub][tid & 31][2] = num[1];
+  xs[sub][tid & 31][3] = num[2];
+  xs[sub][tid & 31][4] = num[3];
   __syncthreads();
-  if (sub == 0) {
-    den = part[0][0][dp] + part[1][0][dp] + part[2][0][dp] + part[3][0][dp];
-    n0 = part[0][1][dp] + part[1][1][dp] + part[2][1][dp] + part[3][1][dp];
-    n1 = part[0][2][dp] + part[1][2][dp] + part[2][2][dp] + part[3][2][dp];
-    half2_t o;
-    o.x = (_Float16)(n0 / den);
-    o.y = (_Float16)(n1 / den);
-    reinterpret_cast<half2_t*>(dst)[dp] = o;
+  if (tid < 32) {
+    float d = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCombineSubsets; ++k) {
+      d += xs[k][tid][0];
+      o0 += xs[k][tid][1];
+      o1 += xs[k][tid][2];
+      o2 += xs[k][tid][3];
+      o3 += xs[k][tid][4];
+    }
+    half4_t o;
+    o[0] = (_Float16)(o0 / d);
+    o[1] = (_Float16)(o1 / d);
+    o[2] = (_Float16)(o2 / d);
+    o[3] = (_Float16)(o3 / d);
+    *reinterpret_cast<half4_t*>(P.out + ((size_t)b * kQHeads + head) * kDim + 4 * tid) = o;
   }
 }
 
 }  // namespace
 
-long long max_work_items(int batch, int capacity, const SplitConfig& cfg) {
-  const long long per_seq_cap =
-      cfg.forced_chunk > 0 ? ((long long)capacity + cfg.forced_chunk - 1) / cfg.forced_chunk
-                           : ((long long)capacity + cfg.min_chunk - 1) / cfg.min_chunk;
-  long long items = 8LL * batch * per_seq_cap;
-  if (cfg.forced_chunk <= 0) {
-    const long long bound = (long long)cfg.target_items + 8LL * batch;
-    if (bound < items) items = bound;
+int resident_workgroups_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_decode_pieces, kThreads, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
   }
-  return items > 0x7fffffffLL ? -1 : items;
+  return n;
 }
 
-size_t workspace_bytes_for_items(long long items) {
-  return (size_t)items * kGroup * (sizeof(float2) + kDim * sizeof(float));
+long long grid_for(int batch, int capacity, const SplitConfig& cfg) {
+  if (cfg.forced_piece > 0) {
+    const long long rows = 8LL * batch * capacity;
+    return (rows + cfg.forced_piece - 1) / cfg.forced_piece;
+  }
+  return cfg.pieces;
+}
+
+size_t partial_bytes_for_grid(long long grid) {
+  return (size_t)(2 * grid) * kSlotFloats * sizeof(float);
 }
 
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
-                         float score_scale_log2, int batch, int capacity,
-                         const SplitConfig& cfg, long long grid_items, void* workspace,
-                         hipStream_t stream, hipEvent_t* events) {
-  PlanParams pp;
-  pp.seq_lens = seq_lens;
-  pp.batch = batch;
-  pp.capacity = capacity;
-  pp.target_items = cfg.target_items;
-  pp.min_chunk = cfg.min_chunk;
-  pp.forced_chunk = cfg.forced_chunk;
-
-  float2* ws_ml = reinterpret_cast<float2*>(workspace);
-  float* ws_acc = reinterpret_cast<float*>(ws_ml + (size_t)grid_items * kGroup);
+                         float score_scale_log2, int batch, int capacity, const SplitConfig& cfg,
+                         long long grid, void* partials, hipStream_t stream, hipEvent_t* events) {
+  Params P;
+  P.q = static_cast<const _Float16*>(q);
+  P.kv = static_cast<const _Float16*>(kv);
+  P.seq_lens = seq_lens;
+  P.out = static_cast<_Float16*>(out);
+  P.ws_ml = reinterpret_cast<float2*>(partials);
+  P.ws_acc = reinterpret_cast<float*>(P.ws_ml + (size_t)(2 * grid) * kGroup);
+  P.batch = batch;
+  P.capacity = capacity;
+  P.pieces = (int)grid;
+  P.min_piece = cfg.min_piece;
+  P.forced_piece = cfg.forced_piece;
+  P.scale_log2 = score_scale_log2;
 
   hipError_t err = hipSuccess;
   if (events && (err = hipEventRecord(events[0], stream)) != hipSuccess) return err;
-  split_partial<<<dim3((unsigned)grid_items), dim3(kThreads), 0, stream>>>(
-      static_cast<const _Float16*>(q), static_cast<const _Float16*>(kv),
-      static_cast<_Float16*>(out), ws_ml, ws_acc, pp, score_scale_log2);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  gqa_decode_pieces<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   if (events && (err = hipEventRecord(events[1], stream)) != hipSuccess) return err;
-  split_combine<<<dim3((unsigned)(batch * kQHeads)), dim3(kThreads), 0, stream>>>(
-      static_cast<_Float16*>(out), ws_ml, ws_acc, pp);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  gqa_decode_combine<<<dim3((unsigned)(batch * kQHeads)), dim3(kThreads), 0, stream>>>(P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   if (events && (err = hipEventRecord(events[2], stream)) != hipSuccess) return err;
   return hipSuccess;
 }

@@ -9,26 +9,28 @@
 
 namespace gqa {
 
-// How the device-side planner splits the batch into work items.
+// How the device-side planner cuts the valid rows into pieces.
 struct SplitConfig {
-  int target_items;   // automatic split: aim for about this many (b, kv head, chunk) items
-  int min_chunk;      // automatic split: never cut chunks shorter than this many positions
-  int forced_chunk;   // > 0: fixed cap on chunk length (automatic rules ignored)
+  int pieces;         // automatic split: number of equal pieces (one workgroup each)
+  int min_piece;      // automatic split: lower bound on the piece length (rows)
+  int forced_piece;   // > 0: fixed piece length; the grid then covers batch*capacity rows
 };
 
-// Upper bound on the number of work items the planner can produce for any
-// seq_lens (each clamped to [0, capacity]). Returns -1 if it exceeds int.
-long long max_work_items(int batch, int capacity, const SplitConfig& cfg);
+// Workgroups of the pieces kernel that fit on one CU at once (0 on error).
+int resident_workgroups_per_cu();
 
-// Bytes of fp32 workspace needed for `items` work items.
-size_t workspace_bytes_for_items(long long items);
+// Number of workgroups launched for this shape and split.
+long long grid_for(int batch, int capacity, const SplitConfig& cfg);
 
-// Enqueue the split-KV partial kernel and the log-sum-exp combine kernel.
-// `events` (may be null) points at three events recorded before the partial
-// kernel, between the two kernels and after the combine kernel.
+// Bytes of fp32 partial-result storage for a grid (two slots per workgroup).
+size_t partial_bytes_for_grid(long long grid);
+
+// Enqueue the two decode kernels (pieces, then combine). `partials` must
+// hold partial_bytes_for_grid(grid) bytes. `events` (may be null) points at
+// three events recorded before, between and after the kernels.
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                          float score_scale_log2, int batch, int capacity,
-                         const SplitConfig& cfg, long long grid_items, void* workspace,
+                         const SplitConfig& cfg, long long grid, void* partials,
                          hipStream_t stream, hipEvent_t* events);
 
 }  // namespace gqa

@@ -77,12 +77,14 @@ typedef enum gqa_status {
  * stream   HIP stream to enqueue on (NULL = the device's null stream).
  *
  * All buffers must live on one device; the kernels run on that device and
- * the caller's current device is restored before returning. The library
- * keeps a cached fp32 workspace per (device, stream) for split-KV partial
- * results; it is grown with hipMalloc on first need (so the first call on a
- * new stream, or with a larger batch, must not be under graph capture).
- * Calls that overlap on one stream are ordered by the stream; calls on
- * different streams use different workspaces.
+ * the caller's current device is restored before returning. Two kernels are
+ * enqueued: the split-KV pieces kernel and the log-sum-exp combine kernel.
+ * The library keeps a cached fp32 workspace per (device, stream) for the
+ * partial results of sequences split across workgroups. It is allocated on
+ * first need, so the first call on a new stream, or one needing a larger
+ * workspace, must not be under graph capture; later calls allocate nothing
+ * and can be captured. Calls on one stream are ordered by the stream; calls
+ * on different streams use different workspaces.
  *
  * Returns GQA_OK, or a negative gqa_status with nothing enqueued.
  */
@@ -90,15 +92,17 @@ int gqa_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out
                float q_scale, int batch, int capacity, hipStream_t stream);
 
 /*
- * gqa_decode_chunked -- gqa_decode with an explicit split-KV chunk length.
+ * gqa_decode_chunked -- gqa_decode with an explicit split length.
  *
  * Same arguments and semantics as gqa_decode, plus:
- * chunk_len  0 selects the automatic, length-driven split (identical to
- *            gqa_decode). A positive value caps the chunk length: sequence b
- *            is split into n_b = ceil(L_b / chunk_len) chunks of near-equal
- *            length, each reduced by one workgroup, then combined by a
- *            log-sum-exp merge. Negative values return GQA_ERR_BAD_ARG.
- * Used to exercise specific chunk counts (1, 2, many) and to study the split.
+ * chunk_len  0 selects the automatic split (identical to gqa_decode). A
+ *            positive value fixes the piece length: the valid rows of all
+ *            (sequence, KV head) pairs, laid end to end, are cut into pieces
+ *            of chunk_len rows, one workgroup each; a pair cut into several
+ *            pieces is merged by a log-sum-exp combine. Negative values
+ *            return GQA_ERR_BAD_ARG; values so small that the partial results
+ *            would exceed 4 GiB also return GQA_ERR_BAD_ARG.
+ * Used to exercise specific split counts (1, 2, many) and to study the split.
  */
 int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                        float q_scale, int batch, int capacity, int chunk_len,
@@ -106,7 +110,8 @@ int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, v
 
 /*
  * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace
- * the automatic split needs for (batch, capacity) on the current device.
+ * the automatic split needs for (batch, capacity) on the current device
+ * (independent of batch and capacity: two slots per workgroup).
  * Returns 0 for invalid sizes or when no device is available.
  */
 size_t gqa_decode_workspace_bytes(int batch, int capacity);
@@ -127,14 +132,15 @@ const char* gqa_decode_last_error(void);
 
 /*
  * Kernel timing aid. gqa_decode_profile_begin() makes subsequent decode
- * calls (any thread) record HIP events around each of their two kernels on
- * the call's stream. gqa_decode_profile_end() waits for the recorded events,
- * returns the summed durations in milliseconds of the split-KV partial
- * kernel and of the combine kernel and the number of calls recorded, then
- * stops recording. Any output pointer may be NULL.
+ * calls (any thread) record HIP events before, between and after their two
+ * kernels on the call's stream. gqa_decode_profile_end() waits for the
+ * recorded events, returns the summed durations in milliseconds of the
+ * pieces kernel and of the combine kernel (each including its launch gap)
+ * and the number of calls recorded, then stops recording. Any output
+ * pointer may be NULL.
  */
 int gqa_decode_profile_begin(void);
-int gqa_decode_profile_end(double* partial_ms, double* combine_ms, int* calls);
+int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls);
 
 #ifdef __cplusplus
 }  /* extern "C" */
