@@ -1,20 +1,27 @@
 """Benchmark of the FP16 GQA single-token decode on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                [--no-cpu-baseline] [--graph]
+                [--no-cpu-baseline] [--graph] [--copy-calibration-mib N]
+python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--workload NAME]
 
 One step = one gqa_decode call (split-KV pieces kernel + combine kernel)
 over one batch of the named synthetic workload, inputs resident in HBM.
 To keep every step reading from HBM rather than from the 256 MB
-Infinity Cache, the step cycles through R copies of the KV cache whose
-valid bytes add up to at least 1 GiB.
+Infinity Cache, the steps cycle through R copies of the KV cache whose
+valid bytes add up to at least 1 GiB (R <= 32; smaller workloads stay
+partly cache-resident, reported as kv_copies_rotated).
+
+Timed region: K steps captured once in a HIP graph and replayed, bracketed
+by device synchronisation (a decode loop replays captured steps; this
+removes host launch cost, not GPU work). The same K steps issued as eager
+API calls are timed separately (api_us_per_step), with the library's HIP
+events around each kernel on the launch stream (kernel_us).
 
 Prints ONE JSON line:
   value       KV-read throughput: sum(L_b) * 4096 B / step time (GB/s)
   roofline    the pieces kernel's algorithmic KV bytes per launch divided
-              by its average duration (HIP events recorded by the library
-              on the launch stream, inside the timed region), against the
-              8 TB/s HBM peak; `traffic` is the measured HBM bytes per launch
+              by its average event-measured duration, against the 8 TB/s
+              HBM peak; `traffic` is the measured HBM bytes per launch
               from rocprofv3 counters when a committed summary matches the
               current kernel source, else null
   cpu_baseline  the float64 CPU oracle on the host cores, same workload
@@ -38,6 +45,8 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b8_c4096_nanfill"
 KERNEL_SOURCE = os.path.join(ROOT, "gqa_token_decode_amd", "csrc", "gqa_decode_kernels.hip")
 ROTATE_TARGET_BYTES = 1 << 30
+ROTATE_MAX_COPIES = 32
+CALIBRATION_COPIES = 5
 
 
 def kernel_source_hash() -> str:
@@ -92,6 +101,61 @@ def cpu_baseline(w, min_seconds: float):
             "seconds_per_step": round(el / reps, 4)}
 
 
+def _counter_rows(d: str):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, counter, match):
+    """(dispatch id, counter value summed over instances) for matching kernels."""
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not match(r.get("Kernel_Name", "")):
+            continue
+        key = int(r["Dispatch_Id"])
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    return sorted(vals.items())
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int) -> str:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, both of
+    `bench.py --copy-calibration-mib N`) into HBM bytes per pieces-kernel
+    launch. Each counter (KiB per dispatch) is scaled by what it reads for
+    the calibration copies, which move exactly N MiB each way."""
+    is_ours = lambda n: "gqa_decode_pieces" in n
+    is_copy = lambda n: ("copyBuffer" in n or "direct_copy" in n or "copy_kernel" in n)
+    out = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        rows = _counter_rows(d)
+        ours = _per_dispatch(rows, counter, is_ours)
+        if not ours:
+            raise SystemExit(f"{counter}: no decode dispatches in {d}")
+        # The calibration copies are the first copies after the last decode.
+        copies = [v for k, v in _per_dispatch(rows, counter, is_copy) if k > ours[-1][0]]
+        copies = copies[:CALIBRATION_COPIES]
+        if len(copies) < CALIBRATION_COPIES:
+            raise SystemExit(f"{counter}: found {len(copies)} calibration copies in {d}")
+        factor = copy_mib * 1048576 / (sum(copies) / len(copies) * 1024)
+        vals = [v for _, v in ours]
+        out[counter] = (sum(vals) / len(vals) * 1024 * factor, factor, len(vals))
+    traffic = int(out["FETCH_SIZE"][0] + out["WRITE_SIZE"][0])
+    return "\n".join([
+        f"# HBM traffic of gqa_decode_pieces on {workload}",
+        "",
+        f"kernel_source_sha256: {kernel_source_hash()}",
+        f"traffic_bytes_per_launch: {traffic}",
+        f"fetch_bytes_per_launch: {int(out['FETCH_SIZE'][0])} (copy scale factor {out['FETCH_SIZE'][1]:.4f}, {out['FETCH_SIZE'][2]} dispatches)",
+        f"write_bytes_per_launch: {int(out['WRITE_SIZE'][0])} (copy scale factor {out['WRITE_SIZE'][1]:.4f}, {out['WRITE_SIZE'][2]} dispatches)",
+        "",
+    ])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,9 +164,14 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the steps replayed from one captured HIP graph")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run plain device copies of this size (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc, args.workload, args.copy_calibration_mib or 256))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -127,52 +196,62 @@ def main(argv=None):
     lens = torch.from_numpy(w.seq_lens).to(dev)
     kv0 = w.kv_to_device(dev)
     rot = max(1, math.ceil(ROTATE_TARGET_BYTES / max(kv_bytes, 1)))
-    rot = min(rot, max(1, int(40e9 // kv0.numel() // 2)))     # keep the copies under ~40 GB
+    rot = min(rot, ROTATE_MAX_COPIES, max(1, int(40e9 // (kv0.numel() * 2))))
     kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
     out = torch.empty_like(q)
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
+    def step(i):
         g.gqa_decode(q, kvs[i % rot], lens, out=out, q_scale=w.q_scale)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
+    # Timed region: K steps replayed from one captured graph.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        step(0)                      # the workspace is cached per stream: create it first
+        gs.synchronize()
+        with torch.cuda.graph(graph, stream=gs):
+            for i in range(args.steps):
+                step(i)
+    torch.cuda.synchronize()
+    graph.replay()                   # untimed: the first replay uploads the graph
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    with g.KernelTimer() as kt:
-        for i in range(args.steps):
-            g.gqa_decode(q, kvs[i % rot], lens, out=out, q_scale=w.q_scale)
-    e1.record(stream)
+    e0.record(gs)
+    with torch.cuda.stream(gs):
+        graph.replay()
+    e1.record(gs)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # The same steps as eager API calls, with per-kernel events.
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    with g.KernelTimer() as kt:
+        for i in range(args.steps):
+            step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    api_ms_per_step = e0.elapsed_time(e1) / args.steps
     pieces_us = kt.pieces_ms / kt.calls * 1e3
     combine_us = kt.combine_ms / kt.calls * 1e3
 
-    graph_us = None
-    if args.graph:
-        gr = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            # The workspace is cached per stream: create it before capture.
-            g.gqa_decode(q, kvs[0], lens, out=out, q_scale=w.q_scale)
-            s.synchronize()
-            with torch.cuda.graph(gr, stream=s):
-                for i in range(rot):
-                    g.gqa_decode(q, kvs[i], lens, out=out, q_scale=w.q_scale)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1048576
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(CALIBRATION_COPIES):
+            dst.copy_(src)
         torch.cuda.synchronize()
-        reps = max(1, args.steps // rot)
-        gr.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            gr.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_us = e0.elapsed_time(e1) * 1e3 / (reps * rot)
+        del src, dst
 
     # Quick numerical sanity (full parity lives in the GPU tests).
     res = out.float().cpu().numpy()
@@ -189,6 +268,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "api_us_per_step": round(api_ms_per_step * 1e3, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -216,9 +296,6 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
-    if graph_us is not None:
-        line["graph_us_per_step"] = round(graph_us, 3)
-        line["graph_GBps"] = round(kv_bytes / (graph_us * 1e-6) / 1e9, 3)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

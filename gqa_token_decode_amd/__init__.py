@@ -109,42 +109,46 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
     same device (values clamped to [0, capacity]). ``out`` (optional,
     caller-owned, fp16, q's shape) receives the result and is returned;
     otherwise a new tensor is allocated. Scores are scaled by
-    ``q_scale / sqrt(128)``. ``chunk_len`` > 0 fixes the split-KV chunk cap
-    (0 = automatic). Enqueued on the current stream of q's device.
+    ``q_scale / sqrt(128)``. ``chunk_len`` > 0 fixes the split-KV piece
+    length (0 = automatic). Enqueued on the current stream of q's device.
     """
     _check_tensor("q", q, torch.float16, 3)
     _check_tensor("kv", kv, torch.float16, 5)
     _check_tensor("sequence_lengths", sequence_lengths, torch.int32, 1)
     B = q.shape[0]
-    if tuple(q.shape) != (B, NUM_Q_HEADS, HEAD_DIM):
+    kshape = kv.shape
+    if q.shape[1] != NUM_Q_HEADS or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must have shape [batch, 32, 128], got {tuple(q.shape)}")
-    if kv.shape[0] != B or kv.shape[1] != 2 or kv.shape[2] != NUM_KV_HEADS or kv.shape[4] != HEAD_DIM:
-        raise ValueError(f"kv must have shape [{B}, 2, 8, capacity, 128], got {tuple(kv.shape)}")
-    if tuple(sequence_lengths.shape) != (B,):
+    if kshape[0] != B or kshape[1] != 2 or kshape[2] != NUM_KV_HEADS or kshape[4] != HEAD_DIM:
+        raise ValueError(f"kv must have shape [{B}, 2, 8, capacity, 128], got {tuple(kshape)}")
+    if sequence_lengths.shape[0] != B:
         raise ValueError(f"sequence_lengths must have shape [{B}], got {tuple(sequence_lengths.shape)}")
-    for name, t in (("q", q), ("kv", kv), ("sequence_lengths", sequence_lengths)):
-        _check_device(name, t)
-    if kv.device != q.device or sequence_lengths.device != q.device:
+    dev = q.device
+    if dev.type != "cuda":
+        _check_device("q", q)
+    if kv.device != dev or sequence_lengths.device != dev:
+        for name, t in (("kv", kv), ("sequence_lengths", sequence_lengths)):
+            _check_device(name, t)
         raise ValueError("q, kv and sequence_lengths must be on the same device")
     if out is None:
         out = torch.empty_like(q)
     else:
         _check_tensor("out", out, torch.float16, 3)
-        _check_device("out", out)
-        if out.shape != q.shape or out.device != q.device:
+        if out.shape != q.shape or out.device != dev:
+            _check_device("out", out)
             raise ValueError("out must have q's shape and device")
-    if not isinstance(chunk_len, int) or chunk_len < 0:
+    if chunk_len.__class__ is not int or chunk_len < 0:
         raise ValueError("chunk_len must be a non-negative int")
-    lib = load_library()
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        if chunk_len:
-            st = lib.gqa_decode_chunked(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
-                                        out.data_ptr(), float(q_scale), B, kv.shape[3],
-                                        chunk_len, stream)
-        else:
-            st = lib.gqa_decode(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
-                                out.data_ptr(), float(q_scale), B, kv.shape[3], stream)
+    lib = _lib if _lib is not None else load_library()
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    stream = torch._C._cuda_getCurrentRawStream(index)
+    if chunk_len:
+        st = lib.gqa_decode_chunked(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
+                                    out.data_ptr(), float(q_scale), B, kshape[3], chunk_len,
+                                    stream)
+    else:
+        st = lib.gqa_decode(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
+                            out.data_ptr(), float(q_scale), B, kshape[3], stream)
     if st != 0:
         _raise(lib, st)
     return out

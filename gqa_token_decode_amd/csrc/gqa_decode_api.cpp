@@ -70,7 +70,10 @@ std::mutex g_mu;
 std::vector<DeviceInfo> g_devices;
 std::vector<Workspace> g_workspaces;
 bool g_profiling = false;
+// Event triples reused across profiling sessions; the first g_profile_used
+// belong to the current session.
 std::vector<ProfileRecord> g_profile;
+size_t g_profile_used = 0;
 
 int env_int(const char* name, int fallback, int lo, int hi) {
   const char* s = getenv(name);
@@ -227,7 +230,8 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
     } else {
       const gqa::SplitConfig cfg = split_config(di, chunk_len);
       const long long grid = gqa::grid_for(batch, capacity, cfg);
-      const size_t pbytes = grid > 0 ? gqa::partial_bytes_for_grid(grid) : 0;
+      const size_t pbytes =
+          grid > 0 ? gqa::segment_bytes_for_batch(batch) + gqa::partial_bytes_for_grid(grid) : 0;
       if (grid <= 0 || grid > 0x7fffffffLL) {
         st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs more than 2^31 workgroups");
       } else if (chunk_len > 0 && pbytes > kMaxForcedWorkspace) {
@@ -243,13 +247,13 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
           const double scale = (double)q_scale / std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
           hipEvent_t* ev = nullptr;
           if (g_profiling) {
-            ProfileRecord rec;
-            bool ok = true;
-            for (int i = 0; i < 3; ++i) ok = ok && hipEventCreate(&rec.ev[i]) == hipSuccess;
-            if (ok) {
-              g_profile.push_back(rec);
-              ev = g_profile.back().ev;
+            if (g_profile_used == g_profile.size()) {
+              ProfileRecord rec;
+              bool ok = true;
+              for (int i = 0; i < 3; ++i) ok = ok && hipEventCreate(&rec.ev[i]) == hipSuccess;
+              if (ok) g_profile.push_back(rec);
             }
+            if (g_profile_used < g_profile.size()) ev = g_profile[g_profile_used++].ev;
           }
           const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, (float)scale, batch,
                                                   capacity, cfg, grid, ws, stream, ev);
@@ -288,7 +292,7 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   const DeviceInfo& di = device_info(dev);
   if (di.status != GQA_OK) return 0;
   const long long grid = gqa::grid_for(batch, capacity, split_config(di, 0));
-  return gqa::partial_bytes_for_grid(grid);
+  return gqa::segment_bytes_for_batch(batch) + gqa::partial_bytes_for_grid(grid);
 }
 
 void gqa_decode_release_workspace(void) {
@@ -328,6 +332,7 @@ const char* gqa_decode_last_error(void) { return t_last_error.c_str(); }
 int gqa_decode_profile_begin(void) {
   std::lock_guard<std::mutex> lock(g_mu);
   g_profiling = true;
+  g_profile_used = 0;
   return GQA_OK;
 }
 
@@ -335,7 +340,8 @@ int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls) {
   std::lock_guard<std::mutex> lock(g_mu);
   double tp = 0.0, tc = 0.0;
   int n = 0, st = GQA_OK;
-  for (ProfileRecord& r : g_profile) {
+  for (size_t i = 0; i < g_profile_used; ++i) {
+    const ProfileRecord& r = g_profile[i];
     float a = 0.f, c = 0.f;
     if (hipEventSynchronize(r.ev[2]) != hipSuccess ||
         hipEventElapsedTime(&a, r.ev[0], r.ev[1]) != hipSuccess ||
@@ -347,9 +353,8 @@ int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls) {
       tc += c;
       ++n;
     }
-    for (int i = 0; i < 3; ++i) (void)hipEventDestroy(r.ev[i]);
   }
-  g_profile.clear();
+  g_profile_used = 0;
   g_profiling = false;
   if (pieces_ms) *pieces_ms = tp;
   if (combine_ms) *combine_ms = tc;

@@ -71,6 +71,7 @@ struct Params {
   _Float16* out;
   float2* ws_ml;       // [2 * grid][4] (max, denominator) per partial and head
   float* ws_acc;       // [2 * grid][4][128] unnormalised weighted V sums
+  int2* seg_desc;      // [8 * batch] per segment: first piece, 2 * pieces + second-slot bit
   int batch;
   int capacity;
   int pieces;          // automatic split: number of equal pieces
@@ -80,6 +81,13 @@ struct Params {
 };
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
+
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ long long uniform64(long long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint4_t load_nt(const _Float16* p) {
@@ -140,6 +148,33 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
     __syncthreads();
     if (*found_b >= 0) break;
   }
+}
+
+// Small batches (<= 64): every wave finds the total and the batch entry of
+// flat row p on its own (lane b holds sequence b), with no workgroup barrier.
+// Returns the total valid rows; *found_b = -1 if p is past them.
+__device__ long long wave_plan(const Params& P, long long (*piece_start)(const Params&, long long),
+                               long long* p_out, long long* found, int* found_b) {
+  const int lane = threadIdx.x & 63;
+  const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
+  long long incl = 8 * len;
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const long long total = __shfl(incl, 63);
+  const long long p = piece_start(P, total);
+  *p_out = p;
+  const long long lo = incl - 8 * len;
+  const unsigned long long hit = __ballot(len > 0 && p >= lo && p < incl);
+  if (hit == 0) {
+    *found_b = -1;
+    return total;
+  }
+  const int b = __ffsll((long long)hit) - 1;
+  *found_b = b;
+  *found = __shfl(lo, b);
+  return total;
 }
 
 struct Segment {
@@ -307,11 +342,15 @@ __device__ __forceinline__ long long slot_of(long long seg_off, long long piece_
   return 2LL * w + (seg_off > piece_start ? 1 : 0);
 }
 
-// Piece length Q for this call (same value in both kernels).
+// Piece length Q for this call.
 __device__ __forceinline__ long long piece_len(const Params& P, long long total) {
   if (P.forced_piece > 0) return P.forced_piece;
   long long Q = (total + P.pieces - 1) / P.pieces;
   return Q < P.min_piece ? P.min_piece : Q;
+}
+
+__device__ long long this_piece_start(const Params& P, long long total) {
+  return (long long)blockIdx.x * piece_len(P, total);
 }
 
 // ---------------------------------------------------------------- kernel 1
@@ -327,30 +366,47 @@ void gqa_decode_pieces(Params P) {
   const int G = lane >> 4, j = lane & 15;
   const int w = blockIdx.x;
 
-  long long part = 0;
-  for (int b = tid; b < P.batch; b += kThreads) part += clamp_len(P.seq_lens[b], P.capacity);
-  const long long total = 8 * block_sum(part, red);   // valid rows over all (b, g)
-
-  // Empty sequences get zero rows (workgroup w takes b = w, w + grid, ...).
+  // Empty sequences get zero rows and empty segment descriptors
+  // (workgroup w takes b = w, w + grid, ...).
   for (int b = w; b < P.batch; b += gridDim.x) {
     if (clamp_len(P.seq_lens[b], P.capacity) == 0) {
       uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * kQHeads * kDim);
       dst[tid] = (uint4_t){0u, 0u, 0u, 0u};
       dst[tid + kThreads] = (uint4_t){0u, 0u, 0u, 0u};
+      if (tid < kKvHeads) P.seg_desc[b * kKvHeads + tid] = make_int2(0, 0);
     }
   }
 
-  const long long Q = piece_len(P, total);
-  const long long p0 = (long long)w * Q;
+  long long total, p0, found;
+  int found_b;
+  if (P.batch <= 64) {
+    total = wave_plan(P, this_piece_start, &p0, &found, &found_b);
+  } else {
+    long long part = 0;
+    for (int b = tid; b < P.batch; b += kThreads) part += clamp_len(P.seq_lens[b], P.capacity);
+    total = 8 * block_sum(part, red);
+    p0 = this_piece_start(P, total);
+    found_b = -1;
+    if (p0 < total) {
+      locate(p0, P, red, &sh_found, &sh_found_b);
+      __syncthreads();
+      found_b = sh_found_b;
+      found = sh_found;
+    }
+  }
+  total = uniform64(total);
+  p0 = uniform64(p0);
   if (p0 >= total) return;                          // uniform: this piece is empty
+  found = uniform64(found);
+  found_b = __builtin_amdgcn_readfirstlane(found_b);
+  const long long Q = piece_len(P, total);
   const long long p1 = p0 + Q < total ? p0 + Q : total;
 
-  locate(p0, P, red, &sh_found, &sh_found_b);
   Segment s;
-  s.b = sh_found_b;
+  s.b = found_b;
   s.len = clamp_len(P.seq_lens[s.b], P.capacity);
-  s.g = (int)((p0 - sh_found) / s.len);
-  s.off = sh_found + (long long)s.g * s.len;
+  s.g = (int)((p0 - found) / s.len);
+  s.off = found + (long long)s.g * s.len;
 
   _Float16* vt = vtile[wv];
   const size_t C = (size_t)P.capacity;
@@ -384,7 +440,11 @@ void gqa_decode_pieces(Params P) {
     merge_waves(acc, sm, M, den, n0, n1);
     const int hh = tid >> 6, d = (tid & 63) * 2;
 
-    if (s.off / Q == (seg_end - 1) / Q) {            // the segment lies in this piece
+    const long long first_w = s.off / Q, last_w = (seg_end - 1) / Q;
+    if (first_w == w && tid == 0)                    // the segment starts in this piece
+      P.seg_desc[s.b * kKvHeads + s.g] =
+          make_int2(w, (int)(2 * (last_w - first_w + 1)) + (s.off > p0 ? 1 : 0));
+    if (first_w == last_w) {                         // the segment lies in this piece
       half2_t o;
       o.x = (_Float16)(n0 / den);
       o.y = (_Float16)(n1 / den);
@@ -421,73 +481,60 @@ constexpr int kCombineSubsets = kThreads / 32;   // 8 subsets x 32 four-column g
 
 // One workgroup per (b, query head): if kernel 1 cut the segment (b, h / 4)
 // into several pieces, merge their partials for head h and write the output
-// row; otherwise exit. The max over the partials is found first, so the
-// weighted sums need no running rescale and their loads are independent.
+// row; otherwise exit. Each of 8 thread subsets merges every 8th partial
+// with a running max (its loads do not depend on each other), then the
+// subsets are merged through LDS.
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
-  __shared__ long long red[kWaves];
-  __shared__ float redf[kWaves];
-  __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][32][5];
+  __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][32][6];
 
   const int tid = threadIdx.x;
   const int b = blockIdx.x / kQHeads, head = blockIdx.x - b * kQHeads;
   const int g = head / kGroup, hh = head - g * kGroup;
-
-  long long part = 0, before = 0;
-  for (int i = tid; i < P.batch; i += kThreads) {
-    const int len = clamp_len(P.seq_lens[i], P.capacity);
-    part += len;
-    if (i < b) before += len;
-  }
-  const long long total = 8 * block_sum(part, red);
-  const long long off = 8 * block_sum(before, red);   // first flat row of sequence b
-  const int len = clamp_len(P.seq_lens[b], P.capacity);
-  if (len == 0) return;                                // zero row written by kernel 1
-  const long long Q = piece_len(P, total);
-  const long long s_off = off + (long long)g * len;
-  const int first_w = (int)(s_off / Q);
-  const int n = (int)((s_off + len - 1) / Q) - first_w + 1;
-  if (n == 1) return;                                  // written by kernel 1
-
-  // Partial i lives in piece first_w + i; the first piece may hold it in its
+  const int2 desc = P.seg_desc[b * kKvHeads + g];
+  const int n = desc.y >> 1;
+  if (n <= 1) return;                  // empty (zero row) or finished by kernel 1
+  const int first_w = desc.x;
+  // Partial i lives in piece first_w + i: the first piece may hold it in its
   // second slot, every later piece holds it as its first segment.
-  const long long slot0 = slot_of(s_off, (long long)first_w * Q, first_w);
-  auto slot = [&](int i) { return i == 0 ? slot0 : 2LL * (first_w + i); };
-
-  const float kNegInf = -__builtin_inff();
-  float M = kNegInf;
-  for (int i = tid; i < n; i += kThreads) M = fmaxf(M, P.ws_ml[slot(i) * kGroup + hh].x);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) redf[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3]));
+  const long long slot0 = 2LL * first_w + (desc.y & 1);
 
   const int sub = tid >> 5, c4 = (tid & 31) * 4;
-  float den = 0.f;
+  const float kNegInf = -__builtin_inff();
+  float M = kNegInf, den = 0.f;
   float4_t num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 2
   for (int i = sub; i < n; i += kCombineSubsets) {
-    const long long sl = slot(i);
+    const long long sl = i == 0 ? slot0 : 2LL * (first_w + i);
     const float2 ml = P.ws_ml[sl * kGroup + hh];
     const float4_t a = *reinterpret_cast<const float4_t*>(P.ws_acc + (sl * kGroup + hh) * kDim + c4);
-    const float wt = exp2_hw(ml.x - M);
-    den += wt * ml.y;
-    num += wt * a;
+    const float Mn = fmaxf(M, ml.x);
+    const float s_old = exp2_hw(M - Mn), s_new = exp2_hw(ml.x - Mn);
+    den = den * s_old + ml.y * s_new;
+    num = num * s_old + a * s_new;
+    M = Mn;
   }
-  xs[sub][tid & 31][0] = den;
-  xs[sub][tid & 31][1] = num[0];
-  xs[sub][tid & 31][2] = num[1];
-  xs[sub][tid & 31][3] = num[2];
-  xs[sub][tid & 31][4] = num[3];
+  float* x = xs[sub][tid & 31];
+  x[0] = M;
+  x[1] = den;
+  x[2] = num[0];
+  x[3] = num[1];
+  x[4] = num[2];
+  x[5] = num[3];
   __syncthreads();
   if (tid < 32) {
+    float Mx = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kCombineSubsets; ++k) Mx = fmaxf(Mx, xs[k][tid][0]);
     float d = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
     for (int k = 0; k < kCombineSubsets; ++k) {
-      d += xs[k][tid][0];
-      o0 += xs[k][tid][1];
-      o1 += xs[k][tid][2];
-      o2 += xs[k][tid][3];
-      o3 += xs[k][tid][4];
+      const float* y = xs[k][tid];
+      const float wt = (y[0] == kNegInf) ? 0.f : exp2_hw(y[0] - Mx);   // subsets without partials
+      d += wt * y[1];
+      o0 += wt * y[2];
+      o1 += wt * y[3];
+      o2 += wt * y[4];
+      o3 += wt * y[5];
     }
     half4_t o;
     o[0] = (_Float16)(o0 / d);
@@ -522,6 +569,10 @@ size_t partial_bytes_for_grid(long long grid) {
   return (size_t)(2 * grid) * kSlotFloats * sizeof(float);
 }
 
+size_t segment_bytes_for_batch(int batch) {
+  return ((size_t)batch * kKvHeads * sizeof(int2) + 255) & ~(size_t)255;
+}
+
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                          float score_scale_log2, int batch, int capacity, const SplitConfig& cfg,
                          long long grid, void* partials, hipStream_t stream, hipEvent_t* events) {
@@ -530,7 +581,8 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.kv = static_cast<const _Float16*>(kv);
   P.seq_lens = seq_lens;
   P.out = static_cast<_Float16*>(out);
-  P.ws_ml = reinterpret_cast<float2*>(partials);
+  P.seg_desc = reinterpret_cast<int2*>(partials);
+  P.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) + segment_bytes_for_batch(batch));
   P.ws_acc = reinterpret_cast<float*>(P.ws_ml + (size_t)(2 * grid) * kGroup);
   P.batch = batch;
   P.capacity = capacity;

@@ -25,8 +25,11 @@ long long grid_for(int batch, int capacity, const SplitConfig& cfg);
 // Bytes of fp32 partial-result storage for a grid (two slots per workgroup).
 size_t partial_bytes_for_grid(long long grid);
 
+// Bytes of per-segment descriptors for a batch (rounded to 256).
+size_t segment_bytes_for_batch(int batch);
+
 // Enqueue the two decode kernels (pieces, then combine). `partials` must
-// hold partial_bytes_for_grid(grid) bytes. `events` (may be null) points at
+// hold segment_bytes_for_batch(batch) + partial_bytes_for_grid(grid) bytes. `events` (may be null) points at
 // three events recorded before, between and after the kernels.
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                          float score_scale_log2, int batch, int capacity,

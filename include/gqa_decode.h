@@ -111,7 +111,7 @@ int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, v
 /*
  * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace
  * the automatic split needs for (batch, capacity) on the current device
- * (independent of batch and capacity: two slots per workgroup).
+ * (a per-segment descriptor table plus two partial slots per workgroup).
  * Returns 0 for invalid sizes or when no device is available.
  */
 size_t gqa_decode_workspace_bytes(int batch, int capacity);
