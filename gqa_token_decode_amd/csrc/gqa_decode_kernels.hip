@@ -20,22 +20,30 @@
 //   across XCDs; merging inside the first kernel would need device-scope
 //   release fences (an L2 write-back per workgroup), which cost far more.
 //
-// Per-wave compute on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
-// accumulate), 32 rows per iteration; the 4 waves of a workgroup take
-// interleaved 32-row tiles of their range:
-//   QK: A = 16 K rows x 32 depth, loaded from HBM straight into registers
-//       (lane (G, j) takes row j, depth 32kk + 8G .. +7, for kk = 0..3);
-//       B = q^T with the group's 4 heads in columns 0..3 and zero columns
-//       4..15. D gives lane (G, j) the scores of rows 4G..4G+3 for head j.
+// Per-wave compute on the matrix cores (fp32 accumulate), 16 rows per step;
+// the 4 waves of a workgroup take interleaved 16-row tiles of each segment.
+// Each wave streams its tiles through a two-stage LDS pipeline that runs
+// across segment boundaries: while it computes tile i, the loads of tile
+// i+1 (its next tile, in this segment or a later one) are in flight.
+//   Buffer loads write K, V and the segment's q straight into LDS (no
+//   register staging; 16-byte chunks of K/V rows XOR-swizzled by row). The
+//   buffer resources are bounded by the segment's rows in this piece, so rows
+//   past the range read as zeros, never as stored data.
+//   QK (v_mfma_f32_16x16x32_f16): A = 16 K rows x 32 depth (lane (G, j)
+//   reads row j, depth 32kk + 8G .. +7), B = q^T with the group's 4 heads in
+//   columns 0..3 and zero columns 4..15; D gives lane (G, j) the scores of
+//   rows 4G..4G+3 for head j.
 //   Online softmax in base 2 (scores carry log2(e)); rows at or beyond the
-//   range end are never loaded and get score -inf and weight 0 by selects.
-//   PV: A = weights (rows = heads, k = 32 rows), B = 32 V rows x 16 head-dim
-//       columns. Two QK tiles' D layout already is one PV step's A layout
-//       (lane (G, j) holds head j at rows 4G+r and 16+4G+r), so the weights
-//       stay in their lanes; V takes the same row order through a per-wave
-//       LDS tile read back transposed (ds_read_b64_tr_b16).
-//   Weights are split into fp16 high and low parts (two MFMAs) so the sum
-//   keeps fp32-level accuracy; the denominator sums the fp32 weights.
+//   range end get score -inf and weight 0 by selects.
+//   PV (v_mfma_f32_16x16x16_f16): A = weights (rows = heads, k = 16 rows);
+//   the QK D layout already is this A layout, so the weights stay in their
+//   lanes. B = 16 V rows x 16 head-dim columns, read transposed from LDS with
+//   ds_read_b64_tr_b16. Weights are split into fp16 high and low parts (two
+//   MFMAs) so the sum keeps fp32-level accuracy; the denominator sums the
+//   fp32 weights.
+//   LDS reads of a stage are issued from asm blocks with their own waits: the
+//   compiler cannot tell the two stages apart and would otherwise wait for the
+//   next tile's loads, which are in flight by design.
 // Each K/V row crosses HBM once, for all 4 query heads of its group.
 
 #include <hip/hip_runtime.h>
@@ -49,6 +57,7 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef unsigned uint4_t __attribute__((ext_vector_type(4)));
@@ -60,8 +69,14 @@ constexpr int kGroup = kQHeads / kKvHeads;   // 4 query heads per KV head
 constexpr int kDim = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 32;                    // rows per wave per iteration
-constexpr int kVStride = kDim + 8;           // LDS row stride of a V tile, in halves
+constexpr int kTileRows = 16;                // rows per wave per step
+constexpr int kStepRows = kWaves * kTileRows;     // rows per workgroup step
+constexpr int kTileHalves = kTileRows * kDim;     // one K or V tile in LDS (4 KiB)
+constexpr int kStageHalves = 2 * kTileHalves;     // one pipeline stage: K then V
+constexpr int kQHalves = kGroup * kDim;           // the group's 4 query rows (1 KiB)
+constexpr int kLoadsPerTile = 9;             // per lane: q, 4 x K, 4 x V
+constexpr unsigned kBufferFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
+constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
 constexpr int kSlotFloats = kGroup * (2 + kDim);   // one partial: 4 x (max, den) + 4 x 128 sums
 
 struct Params {
@@ -82,6 +97,13 @@ struct Params {
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
+// Length of sequence b read through the scalar path (b must be uniform), so
+// waiting for it does not wait for vector loads in flight.
+__device__ __forceinline__ int seq_len_uniform(const int32_t* lens, int b, int cap) {
+  const __attribute__((address_space(4))) int32_t* c = (const __attribute__((address_space(4))) int32_t*)lens;
+  return clamp_len(c[b], cap);
+}
+
 // A wave-uniform 64-bit value moved to scalar registers.
 __device__ __forceinline__ long long uniform64(long long v) {
   const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)v);
@@ -89,10 +111,6 @@ __device__ __forceinline__ long long uniform64(long long v) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ uint4_t load_nt(const _Float16* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint4_t*>(p));
-}
 
 // ---------------------------------------------------------------- planning
 // Workgroup-wide helpers; every thread of the workgroup must call them.
@@ -183,111 +201,248 @@ struct Segment {
 };
 
 // ---------------------------------------------------------------- compute
+// Position of 16-byte chunk c of row r inside an LDS V stage.
+__device__ __forceinline__ int vchunk(int r, int c) { return c ^ (2 * (r & 7)); }
+
+// Rows [lo, hi) of segment (b, g) that lie in this workgroup's piece; the
+// segment covers flat rows [off, off + len). Wave-uniform.
+struct Seg {
+  int b, g, len, lo, hi;
+  long long off;
+};
+
+__device__ __forceinline__ void seg_set_range(Seg& s, long long p_begin, long long p_end) {
+  s.lo = (int)(p_begin > s.off ? p_begin - s.off : 0);
+  const long long e = p_end - s.off;
+  s.hi = (int)(e < s.len ? e : s.len);
+}
+
+// Advance to the next segment (next KV head of b, else the next non-empty
+// sequence). Only called while rows remain below p_end, so one exists.
+__device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end) {
+  const long long end = s.off + s.len;
+  if (s.g + 1 < kKvHeads) {
+    s.g += 1;
+  } else {
+    int nb = s.b + 1;
+    int nl = seq_len_uniform(P.seq_lens, nb, P.capacity);
+    while (nl == 0) {
+      ++nb;
+      nl = seq_len_uniform(P.seq_lens, nb, P.capacity);
+    }
+    s.b = nb;
+    s.len = nl;
+    s.g = 0;
+  }
+  s.off = end;
+  seg_set_range(s, end, p_end);
+}
+
+// Move (s, t) to this wave's next tile in the piece: the next 16-row tile of
+// the wave in s, else its first tile in a later segment. Returns false when
+// the piece has no more tiles for this wave.
+__device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long long p_end, int wv) {
+  t += kStepRows;
+  while (t >= s.hi) {
+    if (s.off + s.hi >= p_end) return false;
+    seg_next(P, s, p_end);
+    t = s.lo + kTileRows * wv;
+  }
+  return true;
+}
+
+// First tile of this wave at or after (s, t) (t = s.lo + 16 * wv).
+__device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long long p_end, int wv) {
+  while (t >= s.hi) {
+    if (s.off + s.hi >= p_end) return false;
+    seg_next(P, s, p_end);
+    t = s.lo + kTileRows * wv;
+  }
+  return true;
+}
+
+// Issue the loads of tile rows [t, t + 16) of segment s into an LDS stage
+// (K, then V) and the segment's 4 query rows into the wave's q slot, in this
+// order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros. With live ==
+// false the buffers are empty: the same 9 loads return zeros without
+// touching memory, so every pipeline step has the same shape.
+__device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
+                                           _Float16* stage, _Float16* qslot) {
+  const int lane = threadIdx.x & 63;
+  const size_t seg_elems = (size_t)P.capacity * kDim;
+  const _Float16* kb = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_elems;
+  const _Float16* vb = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_elems;
+  const _Float16* qg = P.q + ((size_t)s.b * kQHeads + s.g * kGroup) * kDim;
+  const int nbytes = live ? s.hi * (kDim * 2) : 0;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, live ? kQHalves * 2 : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nbytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)qslot, 16, 16 * lane, 0, 0, 0);
+  // DMA lane l writes 16 B at LDS offset 16*l: row 4u + l/16, physical chunk
+  // l%16, which holds logical chunk vchunk(row, l%16) (the swizzle is its own
+  // inverse).
+  const int rsub = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * u + rsub;
+    const int off = (t + r) * (kDim * 2) + 16 * vchunk(r, lane & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + u * 512), 16, off, 0, 0,
+                                             kNonTemporal);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * u + rsub;
+    const int off = (t + r) * (kDim * 2) + 16 * vchunk(r, lane & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + kTileHalves + u * 512), 16,
+                                             off, 0, 0, kNonTemporal);
+  }
+}
+
+__device__ __forceinline__ unsigned lds_addr(const _Float16* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const _Float16*)p;
+}
+
 struct WaveAcc {
   float4_t O[8];     // PV accumulators (D layout): lane (0, j), reg r = head r, column 16*db + j
   float m;           // running max of head j (same in the 4 lane groups)
   float l;           // this lane group's share of head j's denominator
 };
 
-// Accumulate rows [lo, hi) of one (b, g) segment into the wave's state. The
-// waves of the workgroup take interleaved 32-row tiles.
-__device__ __forceinline__ void accumulate_rows(const _Float16* kbase, const _Float16* vbase,
-                                                int lo, int hi, const half8_t qb[4],
-                                                float scale_log2, _Float16* vt, WaveAcc& acc) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int G = lane >> 4, j = lane & 15;
+// q^T as the QK B operand, read from the wave's q slot: lane (G, j) takes
+// head j, depth 32kk + 8G .. +7; columns j >= 4 are zero.
+__device__ __forceinline__ void read_q(const _Float16* qslot, half8_t (&qb)[4]) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
+  int row = j & 3;
+  asm volatile("" : "+v"(row));
+  const unsigned base = lds_addr(qslot) + 2 * (row * kDim + 8 * G);
+  uint4_t x0, x1, x2, x3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:64\n\t"
+      "ds_read_b128 %2, %4 offset:128\n\t"
+      "ds_read_b128 %3, %4 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(base)
+      : "memory");
+  const uint4_t zero = {0u, 0u, 0u, 0u};
+  qb[0] = __builtin_bit_cast(half8_t, j < kGroup ? x0 : zero);
+  qb[1] = __builtin_bit_cast(half8_t, j < kGroup ? x1 : zero);
+  qb[2] = __builtin_bit_cast(half8_t, j < kGroup ? x2 : zero);
+  qb[3] = __builtin_bit_cast(half8_t, j < kGroup ? x3 : zero);
+}
+
+// Fold tile rows [t, t + 16) held in an LDS stage into acc.
+__device__ __forceinline__ void compute_tile(const _Float16* stage, const half8_t (&qb)[4], int t,
+                                             int hi, float scale_log2, WaveAcc& acc) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
   const float kNegInf = -__builtin_inff();
-  const int tr_row = 4 * G + (j >> 2);
-  const int tr_col = 4 * (j & 3);
 
-  for (int t0 = lo + wv * kTile; t0 < hi; t0 += kWaves * kTile) {
-    uint4_t kr[2][4], vr[8];
+  // Per-lane LDS addresses, recomputed every step (a few VALU ops; the empty
+  // asm hides their loop invariance so they are not kept live).
+  int jj = j;
+  asm volatile("" : "+v"(jj));
+  const int rr = 4 * G + (jj >> 2);
+  const unsigned kbase = lds_addr(stage);
+  const unsigned vbase = kbase + 2 * kTileHalves;
+  unsigned ka[4], va[8];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int pos = t0 + 16 * st + j;
+  for (int kk = 0; kk < 4; ++kk) ka[kk] = kbase + 2 * (jj * kDim + 8 * vchunk(jj, 4 * kk + G));
+  // Transposed reads: lane (G, j) supplies the address of row 4G + j/4,
+  // columns 16*db + 4*(j%4) .. +3 and receives column 16*db + j of rows
+  // 4G .. 4G+3.
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        kr[st][kk] = (uint4_t){0u, 0u, 0u, 0u};
-        if (pos < hi) kr[st][kk] = load_nt(kbase + (size_t)pos * kDim + 32 * kk + 8 * G);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int pos = t0 + 4 * u + G;
-      vr[u] = (uint4_t){0u, 0u, 0u, 0u};
-      if (pos < hi) vr[u] = load_nt(vbase + (size_t)pos * kDim + 8 * j);
-    }
+  for (int db = 0; db < 8; ++db)
+    va[db] = vbase + 2 * (rr * kDim + 8 * vchunk(rr, 2 * db + ((jj & 3) >> 1)) + 4 * (jj & 1));
+  uint4_t k0, k1, k2, k3;
+  short4_t v0, v1, v2, v3, v4, v5, v6, v7;
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3),
+        "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+      : "memory");
 
-    float4_t sc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sc[st] = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        sc[st] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[st][kk]),
-                                                        qb[kk], sc[st], 0, 0, 0);
-    }
+  float4_t sc = {0.f, 0.f, 0.f, 0.f};
+  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k0), qb[0], sc, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k1), qb[1], sc, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k2), qb[2], sc, 0, 0, 0);
+  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k3), qb[3], sc, 0, 0, 0);
 
+  float sv[4];
+  float mx = kNegInf;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<uint4_t*>(vt + (4 * u + G) * kVStride + 8 * j) = vr[u];
-
-    float sv[8];
-    float mx = kNegInf;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = t0 + 16 * st + 4 * G + r;
-        const float x = pos < hi ? sc[st][r] * scale_log2 : kNegInf;
-        sv[4 * st + r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Row t0 is below hi, so mx (and m_new) is finite; alpha is 0 on the
-    // first tile, where acc.m is still -inf.
-    const float m_new = fmaxf(acc.m, mx);
-    const float alpha = exp2_hw(acc.m - m_new);
-    acc.m = m_new;
-
-    half8_t ph, pl;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = (sv[e] == kNegInf) ? 0.f : exp2_hw(sv[e] - m_new);
-      psum += p;
-      const _Float16 hi16 = (_Float16)p;
-      ph[e] = hi16;
-      pl[e] = (_Float16)(p - (float)hi16);
-    }
-    acc.l = acc.l * alpha + psum;
-
-    // Row r of every PV tile is head r; lane h holds head h's alpha.
-    const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2),
-                a3 = __shfl(alpha, 3);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      acc.O[db][0] *= a0;
-      acc.O[db][1] *= a1;
-      acc.O[db][2] *= a2;
-      acc.O[db][3] *= a3;
-    }
-
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const short4_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4_t*)(vt + tr_row * kVStride + 16 * db + tr_col));
-      const short4_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_short4_t*)(vt + (16 + tr_row) * kVStride + 16 * db + tr_col));
-      half8_t vb;
-      vb.lo = __builtin_bit_cast(half4_t, b0);
-      vb.hi = __builtin_bit_cast(half4_t, b1);
-      acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vb, acc.O[db], 0, 0, 0);
-      acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, acc.O[db], 0, 0, 0);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const float x = (t + 4 * G + r) < hi ? sc[r] * scale_log2 : kNegInf;
+    sv[r] = x;
+    mx = fmaxf(mx, x);
   }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
+  // tile, where acc.m is still -inf.
+  const float m_new = fmaxf(acc.m, mx);
+  const float alpha = exp2_hw(acc.m - m_new);
+  acc.m = m_new;
+
+  half4_t ph, pl;
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float p = (sv[r] == kNegInf) ? 0.f : exp2_hw(sv[r] - m_new);
+    psum += p;
+    const _Float16 h = (_Float16)p;
+    ph[r] = h;
+    pl[r] = (_Float16)(p - (float)h);
+  }
+  acc.l = acc.l * alpha + psum;
+
+  // Row r of every PV tile is head r; lane h holds head h's alpha.
+  const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2),
+              a3 = __shfl(alpha, 3);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    acc.O[db][0] *= a0;
+    acc.O[db][1] *= a1;
+    acc.O[db][2] *= a2;
+    acc.O[db][3] *= a3;
+  }
+
+  const short4_t vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const half4_t vb = __builtin_bit_cast(half4_t, vv[db]);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, acc.O[db], 0, 0, 0);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, acc.O[db], 0, 0, 0);
+  }
+}
+
+// One pipeline step for the tile held in `cur`: take its q from the q slot,
+// issue the next tile (or an empty load group) into `nxt` and the q slot,
+// wait for the current tile, fold it in. Loads complete in issue order, so
+// "all but the newest N" waits are exact.
+__device__ __forceinline__ void tile_step(const Params& P, _Float16* cur, _Float16* nxt,
+                                          _Float16* qslot, bool has_next, const Seg& nseg, int nt,
+                                          int t, int hi, WaveAcc& acc) {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
+  half8_t qb[4];
+  read_q(qslot, qb);
+  issue_tile(P, nseg, nt, has_next, nxt, qslot);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
+  compute_tile(cur, qb, t, hi, P.scale_log2, acc);
 }
 
 struct MergeLds {
@@ -354,15 +509,17 @@ __device__ long long this_piece_start(const Params& P, long long total) {
 }
 
 // ---------------------------------------------------------------- kernel 1
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(Params P) {
   __shared__ long long red[kWaves];
   __shared__ long long sh_found;
   __shared__ int sh_found_b;
-  __shared__ __attribute__((aligned(16))) _Float16 vtile[kWaves][kTile * kVStride];
+  __shared__ __attribute__((aligned(16))) _Float16 stages[kWaves][2][kStageHalves];
+  __shared__ __attribute__((aligned(16))) _Float16 qslots[kWaves][kQHalves];
   __shared__ __attribute__((aligned(16))) MergeLds sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
   const int G = lane >> 4, j = lane & 15;
   const int w = blockIdx.x;
 
@@ -402,44 +559,45 @@ void gqa_decode_pieces(Params P) {
   const long long Q = piece_len(P, total);
   const long long p1 = p0 + Q < total ? p0 + Q : total;
 
-  Segment s;
+  Seg s;
   s.b = found_b;
-  s.len = clamp_len(P.seq_lens[s.b], P.capacity);
+  s.len = seq_len_uniform(P.seq_lens, s.b, P.capacity);
   s.g = (int)((p0 - found) / s.len);
   s.off = found + (long long)s.g * s.len;
+  seg_set_range(s, p0, p1);
 
-  _Float16* vt = vtile[wv];
-  const size_t C = (size_t)P.capacity;
-  long long cur = p0;
+  // Prime the pipeline with this wave's first tile.
+  _Float16* st0 = stages[wv][0];
+  _Float16* st1 = stages[wv][1];
+  _Float16* qslot = qslots[wv];
+  Seg pf = s;
+  int pt = s.lo + kTileRows * wv;
+  const bool pf_ok = tile_first(P, pf, pt, p1, wv);
+  issue_tile(P, pf, pt, pf_ok, st0, qslot);
+  int par = 0;
+
   while (true) {
-    const long long seg_end = s.off + s.len;
-    const long long hi_flat = seg_end < p1 ? seg_end : p1;
-    const int lo = (int)(cur - s.off), hi = (int)(hi_flat - s.off);
-
-    // q^T as the B operand, one 32-deep slice per kk; columns >= 4 are zero.
-    half8_t qb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4_t v = {0u, 0u, 0u, 0u};
-      if (j < kGroup)
-        v = *reinterpret_cast<const uint4_t*>(
-            P.q + ((size_t)s.b * kQHeads + s.g * kGroup + j) * kDim + 32 * kk + 8 * G);
-      qb[kk] = __builtin_bit_cast(half8_t, v);
-    }
-    const _Float16* kbase = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * C * kDim;
-    const _Float16* vbase = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * C * kDim;
-
     WaveAcc acc;
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc.O[db] = (float4_t){0.f, 0.f, 0.f, 0.f};
     acc.m = -__builtin_inff();
     acc.l = 0.f;
-    accumulate_rows(kbase, vbase, lo, hi, qb, P.scale_log2, vt, acc);
+    // This wave's tiles of s; the prefetch cursor (pf, pt) is on the first.
+    for (int t = s.lo + kTileRows * wv; t < s.hi; t += kStepRows) {
+      Seg nf = pf;
+      int nt = pt;
+      const bool n_ok = tile_next(P, nf, nt, p1, wv);
+      tile_step(P, par ? st1 : st0, par ? st0 : st1, qslot, n_ok, nf, nt, t, s.hi, acc);
+      pf = nf;
+      pt = nt;
+      par ^= 1;
+    }
 
     float M, den, n0, n1;
     merge_waves(acc, sm, M, den, n0, n1);
     const int hh = tid >> 6, d = (tid & 63) * 2;
 
+    const long long seg_end = s.off + s.len;
     const long long first_w = s.off / Q, last_w = (seg_end - 1) / Q;
     if (first_w == w && tid == 0)                    // the segment starts in this piece
       P.seg_desc[s.b * kKvHeads + s.g] =
@@ -455,24 +613,8 @@ void gqa_decode_pieces(Params P) {
       if (d == 0) P.ws_ml[slot * kGroup + hh] = make_float2(M, den);
     }
 
-    cur = hi_flat;
-    if (cur >= p1) break;
-    // Next segment: next KV head of b, else the next non-empty sequence
-    // (one exists, because rows remain below p1 <= total).
-    if (s.g + 1 < kKvHeads) {
-      s.g += 1;
-    } else {
-      int nb = s.b + 1;
-      int nl = clamp_len(P.seq_lens[nb], P.capacity);
-      while (nl == 0) {
-        ++nb;
-        nl = clamp_len(P.seq_lens[nb], P.capacity);
-      }
-      s.b = nb;
-      s.len = nl;
-      s.g = 0;
-    }
-    s.off = seg_end;
+    if (s.off + s.hi >= p1) break;
+    seg_next(P, s, p1);
   }
 }
 
