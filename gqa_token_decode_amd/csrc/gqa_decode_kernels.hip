@@ -445,6 +445,13 @@ __device__ __forceinline__ void tile_step(const Params& P, _Float16* cur, _Float
   compute_tile(cur, qb, t, hi, P.scale_log2, acc);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its vector memory loads (the next tiles' loads stay in
+// flight across it). __syncthreads() would also wait for all vector memory.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 struct MergeLds {
   float m[kWaves][kGroup];
   float l[kWaves][kGroup];
@@ -460,7 +467,7 @@ __device__ __forceinline__ void merge_waves(const WaveAcc& acc, MergeLds& sm, fl
   const float kNegInf = -__builtin_inff();
   float l = acc.l + __shfl_xor(acc.l, 16);
   l += __shfl_xor(l, 32);
-  __syncthreads();   // earlier readers of sm are done
+  lds_barrier();     // earlier readers of sm are done
   if (lane < kGroup) {
     sm.m[wv][lane] = acc.m;
     sm.l[wv][lane] = l;
@@ -472,7 +479,7 @@ __device__ __forceinline__ void merge_waves(const WaveAcc& acc, MergeLds& sm, fl
       for (int r = 0; r < 4; ++r) sm.acc[wv][r][16 * db + j] = acc.O[db][r];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int hh = tid >> 6, d = (tid & 63) * 2;
   M = kNegInf;
 #pragma unroll

@@ -93,6 +93,19 @@ def test_ragged_lengths_odd_capacity_and_clamping(chunk_len):
     check(got, oracle_of(w), f"ragged chunk_len={chunk_len}")
 
 
+@pytest.mark.parametrize("batch,cap,lo,hi", [(100, 512, 0, 300), (300, 128, 1, 64), (1000, 64, 0, 40)])
+def test_large_batches_use_the_block_level_plan(batch, cap, lo, hi):
+    # Batches above 64 locate their rows with workgroup-wide scans (and
+    # above 256 with several passes over the lengths).
+    w = workloads.build(f"batch{batch}", 42 + batch, cap,
+                        lambda r: r.integers(lo, hi, batch, endpoint=True), fill="nan")
+    got = run(w)
+    for b in np.flatnonzero(w.valid_lengths == 0):
+        assert np.all(got[b] == 0)
+    check(got, oracle_of(w), f"batch {batch}")
+    check(run(w, chunk_len=37), oracle_of(w), f"batch {batch}, chunk_len 37")
+
+
 def test_long_sequence_with_one_row_tail():
     w = workloads.build("tail", 33, 65600, [65537, 65600, 1])
     check(run(w), oracle_of(w), "65537-row tail")
