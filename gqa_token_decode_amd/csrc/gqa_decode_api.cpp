@@ -178,11 +178,9 @@ int check_args(const void* q, const void* kv, const int32_t* seq_lens, const voi
                 batch, capacity);
   if (batch > (1 << 24))
     return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: batch %d exceeds the supported 2^24", batch);
-  // kv bytes = batch * capacity * 4096 must fit in int64 (it always does for
-  // int batch and capacity, but keep the guard explicit).
-  const double kv_bytes = (double)batch * (double)capacity * (double)kKvBytesPerPos;
-  if (kv_bytes >= 9.2e18)
-    return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: kv size overflows 64-bit offsets");
+  if (capacity > GQA_MAX_CAPACITY)
+    return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: capacity %d exceeds the supported %d", capacity,
+                GQA_MAX_CAPACITY);
   if (chunk_len < 0)
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: chunk_len must be >= 0, got %d", chunk_len);
   if (((uintptr_t)q | (uintptr_t)kv | (uintptr_t)out) & 15u)
@@ -282,7 +280,7 @@ int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, v
 }
 
 size_t gqa_decode_workspace_bytes(int batch, int capacity) {
-  if (batch <= 0 || capacity <= 0) return 0;
+  if (batch <= 0 || capacity <= 0 || batch > (1 << 24) || capacity > GQA_MAX_CAPACITY) return 0;
   int dev = 0, ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0 || hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();

@@ -44,11 +44,17 @@ extern "C" {
 #define GQA_NUM_KV_HEADS 8
 #define GQA_HEAD_DIM 128
 
+/* Largest supported capacity (rows per (sequence, KV head)). The kernels
+ * address one (sequence, KV head) block of K or V with 32-bit byte offsets,
+ * so a block stays below 2 GiB: 2^22 rows x 256 B = 1 GiB. */
+#define GQA_MAX_CAPACITY (1 << 22)
+
 /* Status codes returned by the entry points (0 = success). */
 typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_NULL = -1,             /* a required pointer is NULL                        */
-  GQA_ERR_BAD_SHAPE = -2,        /* batch <= 0, capacity <= 0, or sizes overflow       */
+  GQA_ERR_BAD_SHAPE = -2,        /* batch outside [1, 2^24] or capacity outside
+                                    [1, GQA_MAX_CAPACITY]                              */
   GQA_ERR_MISALIGNED = -3,       /* q, kv or out not 16-byte aligned; seq_lens not 4   */
   GQA_ERR_ALIAS = -4,            /* out overlaps q, kv or seq_lens                     */
   GQA_ERR_NO_DEVICE = -5,        /* no HIP device visible                              */
@@ -73,7 +79,8 @@ typedef enum gqa_status {
  * out      device, fp16 [batch, 32, 128], contiguous, 16-byte aligned,
  *          caller-allocated; must not overlap q, kv or seq_lens (written).
  * q_scale  extra score scale, applied together with 1/sqrt(128).
- * batch, capacity  positive sizes.
+ * batch     1 .. 2^24.
+ * capacity  1 .. GQA_MAX_CAPACITY.
  * stream   HIP stream to enqueue on (NULL = the device's null stream).
  *
  * All buffers must live on one device; the kernels run on that device and

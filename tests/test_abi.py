@@ -96,6 +96,11 @@ def test_argument_errors_are_reported_before_device_work(lib):
     assert _call(lib, B=0) == BAD_SHAPE
     assert _call(lib, C=0) == BAD_SHAPE
     assert _call(lib, B=-3) == BAD_SHAPE
+    assert _call(lib, B=(1 << 24) + 1) == BAD_SHAPE
+    # one (sequence, KV head) block of K must stay addressable with 32-bit offsets
+    assert _call(lib, B=1, C=(1 << 22) + 1) == BAD_SHAPE
+    assert "capacity" in lib.gqa_decode_last_error().decode()
+    assert lib.gqa_decode_workspace_bytes(1, (1 << 22) + 1) == 0
     assert _call(lib, q=0x10008) == MISALIGNED
     assert _call(lib, out=0x40004) == MISALIGNED
     assert _call(lib, lens=0x30002) == MISALIGNED
