@@ -14,13 +14,14 @@ partly cache-resident, reported as kv_copies_rotated).
 Timed region: K steps captured once in a HIP graph and replayed, bracketed
 by device synchronisation (a decode loop replays captured steps; this
 removes host launch cost, not GPU work). The same K steps issued as eager
-API calls are timed separately (api_us_per_step), with the library's HIP
-events around each kernel on the launch stream (kernel_us).
+API calls are timed separately (api_us_per_step), with the library's
+start/stop HIP events attached to each kernel dispatch on the launch stream
+(kernel_us: the kernels' execution time, without launch gaps).
 
 Prints ONE JSON line:
   value       KV-read throughput: sum(L_b) * 4096 B / step time (GB/s)
   roofline    the pieces kernel's algorithmic KV bytes per launch divided
-              by its average event-measured duration, against the 8 TB/s
+              by its average event-measured execution time, against the 8 TB/s
               HBM peak; `traffic` is the measured HBM bytes per launch
               from rocprofv3 counters when a committed summary matches the
               current kernel source, else null

@@ -63,7 +63,7 @@ struct Workspace {
 };
 
 struct ProfileRecord {
-  hipEvent_t ev[3];
+  hipEvent_t ev[4];   // pieces start, stop; combine start, stop
 };
 
 std::mutex g_mu;
@@ -244,11 +244,13 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
           // kernel can use the hardware base-2 exponential.
           const double scale = (double)q_scale / std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
           hipEvent_t* ev = nullptr;
-          if (g_profiling) {
+          hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+          if (g_profiling && hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+              cap == hipStreamCaptureStatusNone) {
             if (g_profile_used == g_profile.size()) {
               ProfileRecord rec;
               bool ok = true;
-              for (int i = 0; i < 3; ++i) ok = ok && hipEventCreate(&rec.ev[i]) == hipSuccess;
+              for (int i = 0; i < 4; ++i) ok = ok && hipEventCreate(&rec.ev[i]) == hipSuccess;
               if (ok) g_profile.push_back(rec);
             }
             if (g_profile_used < g_profile.size()) ev = g_profile[g_profile_used++].ev;
@@ -341,9 +343,9 @@ int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls) {
   for (size_t i = 0; i < g_profile_used; ++i) {
     const ProfileRecord& r = g_profile[i];
     float a = 0.f, c = 0.f;
-    if (hipEventSynchronize(r.ev[2]) != hipSuccess ||
+    if (hipEventSynchronize(r.ev[3]) != hipSuccess ||
         hipEventElapsedTime(&a, r.ev[0], r.ev[1]) != hipSuccess ||
-        hipEventElapsedTime(&c, r.ev[1], r.ev[2]) != hipSuccess) {
+        hipEventElapsedTime(&c, r.ev[2], r.ev[3]) != hipSuccess) {
       (void)hipGetLastError();
       st = fail(GQA_ERR_LAUNCH, "gqa_decode_profile_end: event query failed");
     } else {

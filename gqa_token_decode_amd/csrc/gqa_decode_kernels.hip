@@ -46,6 +46,7 @@
 //   next tile's loads, which are in flight by design.
 // Each K/V row crosses HBM once, for all 4 query heads of its group.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -149,7 +150,7 @@ __device__ long long block_scan(long long v, long long* red, long long* total) {
 // Batch entry b whose flat rows [8*P_b, 8*P_{b+1}) hold flat row p, and
 // 8*P_b. p must be below 8 * sum(L).
 __device__ void locate(long long p, const Params& P, long long* red, long long* found,
-                       int* found_b) {
+                       int* found_b, int* found_len) {
   if (threadIdx.x == 0) *found_b = -1;
   long long before = 0;
   for (int b0 = 0; b0 < P.batch; b0 += kThreads) {
@@ -161,6 +162,7 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
     if (len > 0 && p >= lo && p < lo + 8 * len) {
       *found_b = b;
       *found = lo;
+      *found_len = (int)len;
     }
     before += total;
     __syncthreads();
@@ -170,11 +172,14 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
 
 // Small batches (<= 64): every wave finds the total and the batch entry of
 // flat row p on its own (lane b holds sequence b), with no workgroup barrier.
-// Returns the total valid rows; *found_b = -1 if p is past them.
+// Returns the total valid rows; *found_b = -1 if p is past them. *lens_v
+// keeps the clamped lengths (lane b holds sequence b's), so later segment
+// steps read them with readlane instead of a dependent memory load.
 __device__ long long wave_plan(const Params& P, long long (*piece_start)(const Params&, long long),
-                               long long* p_out, long long* found, int* found_b) {
+                               long long* p_out, long long* found, int* found_b, int* lens_v) {
   const int lane = threadIdx.x & 63;
   const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
+  *lens_v = (int)len;
   long long incl = 8 * len;
   for (int o = 1; o < 64; o <<= 1) {
     const long long t = __shfl_up(incl, o);
@@ -217,18 +222,25 @@ __device__ __forceinline__ void seg_set_range(Seg& s, long long p_begin, long lo
   s.hi = (int)(e < s.len ? e : s.len);
 }
 
+// Clamped length of sequence b (b uniform): from the wave's length register
+// for batches <= 64 (lane b holds it), else through the scalar path.
+__device__ __forceinline__ int seq_len_of(const Params& P, int lens_v, int b) {
+  return P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, b)
+                       : seq_len_uniform(P.seq_lens, b, P.capacity);
+}
+
 // Advance to the next segment (next KV head of b, else the next non-empty
 // sequence). Only called while rows remain below p_end, so one exists.
-__device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end) {
+__device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end, int lens_v) {
   const long long end = s.off + s.len;
   if (s.g + 1 < kKvHeads) {
     s.g += 1;
   } else {
     int nb = s.b + 1;
-    int nl = seq_len_uniform(P.seq_lens, nb, P.capacity);
+    int nl = seq_len_of(P, lens_v, nb);
     while (nl == 0) {
       ++nb;
-      nl = seq_len_uniform(P.seq_lens, nb, P.capacity);
+      nl = seq_len_of(P, lens_v, nb);
     }
     s.b = nb;
     s.len = nl;
@@ -241,21 +253,23 @@ __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_en
 // Move (s, t) to this wave's next tile in the piece: the next 16-row tile of
 // the wave in s, else its first tile in a later segment. Returns false when
 // the piece has no more tiles for this wave.
-__device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long long p_end, int wv) {
+__device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long long p_end, int wv,
+                                          int lens_v) {
   t += kStepRows;
   while (t >= s.hi) {
     if (s.off + s.hi >= p_end) return false;
-    seg_next(P, s, p_end);
+    seg_next(P, s, p_end, lens_v);
     t = s.lo + kTileRows * wv;
   }
   return true;
 }
 
 // First tile of this wave at or after (s, t) (t = s.lo + 16 * wv).
-__device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long long p_end, int wv) {
+__device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long long p_end, int wv,
+                                           int lens_v) {
   while (t >= s.hi) {
     if (s.off + s.hi >= p_end) return false;
-    seg_next(P, s, p_end);
+    seg_next(P, s, p_end, lens_v);
     t = s.lo + kTileRows * wv;
   }
   return true;
@@ -520,7 +534,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void gqa_decode_pieces(Params P) {
   __shared__ long long red[kWaves];
   __shared__ long long sh_found;
-  __shared__ int sh_found_b;
+  __shared__ int sh_found_b, sh_found_len;
   __shared__ __attribute__((aligned(16))) _Float16 stages[kWaves][2][kStageHalves];
   __shared__ __attribute__((aligned(16))) _Float16 qslots[kWaves][kQHalves];
   __shared__ __attribute__((aligned(16))) MergeLds sm;
@@ -542,9 +556,10 @@ void gqa_decode_pieces(Params P) {
   }
 
   long long total, p0, found;
-  int found_b;
+  int found_b, found_len = 0;
+  int lens_v = 0;
   if (P.batch <= 64) {
-    total = wave_plan(P, this_piece_start, &p0, &found, &found_b);
+    total = wave_plan(P, this_piece_start, &p0, &found, &found_b, &lens_v);
   } else {
     long long part = 0;
     for (int b = tid; b < P.batch; b += kThreads) part += clamp_len(P.seq_lens[b], P.capacity);
@@ -552,10 +567,11 @@ void gqa_decode_pieces(Params P) {
     p0 = this_piece_start(P, total);
     found_b = -1;
     if (p0 < total) {
-      locate(p0, P, red, &sh_found, &sh_found_b);
+      locate(p0, P, red, &sh_found, &sh_found_b, &sh_found_len);
       __syncthreads();
       found_b = sh_found_b;
       found = sh_found;
+      found_len = sh_found_len;
     }
   }
   total = uniform64(total);
@@ -568,7 +584,8 @@ void gqa_decode_pieces(Params P) {
 
   Seg s;
   s.b = found_b;
-  s.len = seq_len_uniform(P.seq_lens, s.b, P.capacity);
+  s.len = P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, s.b)
+                        : __builtin_amdgcn_readfirstlane(found_len);
   s.g = (int)((p0 - found) / s.len);
   s.off = found + (long long)s.g * s.len;
   seg_set_range(s, p0, p1);
@@ -579,7 +596,7 @@ void gqa_decode_pieces(Params P) {
   _Float16* qslot = qslots[wv];
   Seg pf = s;
   int pt = s.lo + kTileRows * wv;
-  const bool pf_ok = tile_first(P, pf, pt, p1, wv);
+  const bool pf_ok = tile_first(P, pf, pt, p1, wv, lens_v);
   issue_tile(P, pf, pt, pf_ok, st0, qslot);
   int par = 0;
 
@@ -593,7 +610,7 @@ void gqa_decode_pieces(Params P) {
     for (int t = s.lo + kTileRows * wv; t < s.hi; t += kStepRows) {
       Seg nf = pf;
       int nt = pt;
-      const bool n_ok = tile_next(P, nf, nt, p1, wv);
+      const bool n_ok = tile_next(P, nf, nt, p1, wv, lens_v);
       tile_step(P, par ? st1 : st0, par ? st0 : st1, qslot, n_ok, nf, nt, t, s.hi, acc);
       pf = nf;
       pt = nt;
@@ -621,7 +638,7 @@ void gqa_decode_pieces(Params P) {
     }
 
     if (s.off + s.hi >= p1) break;
-    seg_next(P, s, p1);
+    seg_next(P, s, p1, lens_v);
   }
 }
 
@@ -741,13 +758,19 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.scale_log2 = score_scale_log2;
 
   hipError_t err = hipSuccess;
-  if (events && (err = hipEventRecord(events[0], stream)) != hipSuccess) return err;
-  gqa_decode_pieces<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(P);
+  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * kQHeads)), block(kThreads);
+  if (events) {
+    // Start/stop events attached to the dispatches: they time each kernel's
+    // execution without extra packets between the kernels.
+    hipExtLaunchKernelGGL(gqa_decode_pieces, pieces_grid, block, 0, stream, events[0], events[1], 0, P);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipExtLaunchKernelGGL(gqa_decode_combine, combine_grid, block, 0, stream, events[2], events[3], 0, P);
+    return hipGetLastError();
+  }
+  gqa_decode_pieces<<<pieces_grid, block, 0, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (events && (err = hipEventRecord(events[1], stream)) != hipSuccess) return err;
-  gqa_decode_combine<<<dim3((unsigned)(batch * kQHeads)), dim3(kThreads), 0, stream>>>(P);
+  gqa_decode_combine<<<combine_grid, block, 0, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (events && (err = hipEventRecord(events[2], stream)) != hipSuccess) return err;
   return hipSuccess;
 }
 

@@ -29,8 +29,9 @@ size_t partial_bytes_for_grid(long long grid);
 size_t segment_bytes_for_batch(int batch);
 
 // Enqueue the two decode kernels (pieces, then combine). `partials` must
-// hold segment_bytes_for_batch(batch) + partial_bytes_for_grid(grid) bytes. `events` (may be null) points at
-// three events recorded before, between and after the kernels.
+// hold segment_bytes_for_batch(batch) + partial_bytes_for_grid(grid) bytes.
+// `events` (may be null) points at four events: start and stop of the pieces
+// kernel, then start and stop of the combine kernel.
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                          float score_scale_log2, int batch, int capacity,
                          const SplitConfig& cfg, long long grid, void* partials,

@@ -139,12 +139,13 @@ const char* gqa_decode_last_error(void);
 
 /*
  * Kernel timing aid. gqa_decode_profile_begin() makes subsequent decode
- * calls (any thread) record HIP events before, between and after their two
- * kernels on the call's stream. gqa_decode_profile_end() waits for the
- * recorded events, returns the summed durations in milliseconds of the
- * pieces kernel and of the combine kernel (each including its launch gap)
- * and the number of calls recorded, then stops recording. Any output
- * pointer may be NULL.
+ * calls (any thread) attach start and stop HIP events to the dispatch of
+ * each of their two kernels on the call's stream, so the events time the
+ * kernels' execution. gqa_decode_profile_end() waits for the recorded
+ * events, returns the summed durations in milliseconds of the pieces kernel
+ * and of the combine kernel and the number of calls recorded, then stops
+ * recording. Any output pointer may be NULL. Calls made while their stream
+ * is being captured into a graph are not timed (nor counted).
  */
 int gqa_decode_profile_begin(void);
 int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls);
