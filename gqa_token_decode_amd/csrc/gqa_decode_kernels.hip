@@ -113,6 +113,35 @@ __device__ __forceinline__ long long uniform64(long long v) {
 }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Cross-lane steps on the VALU (no LDS round trip). The permlane swaps of
+// gfx950 exchange 16-lane rows: called with the same value twice, each
+// returns, per lane, the lane's own value and that of lane ^ 16 (resp.
+// lane ^ 32) as its two results, so a symmetric op of the two results
+// reduces over the pair.
+__device__ __forceinline__ unsigned fbits(float x) { return __builtin_bit_cast(unsigned, x); }
+__device__ __forceinline__ float bitsf(unsigned x) { return __builtin_bit_cast(float, x); }
+
+// Max over the lanes j, j + 16, j + 32, j + 48 (j = lane % 16).
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+  x = fmaxf(bitsf(a[0]), bitsf(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fmaxf(bitsf(b[0]), bitsf(b[1]));
+}
+
+// Sum over the lanes j, j + 16, j + 32, j + 48 (j = lane % 16).
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+  x = bitsf(a[0]) + bitsf(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return bitsf(b[0]) + bitsf(b[1]);
+}
+
+// Value of x in lane `src` (uniform), through a scalar register.
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return bitsf((unsigned)__builtin_amdgcn_readlane((int)fbits(x), src));
+}
+
 // ---------------------------------------------------------------- planning
 // Workgroup-wide helpers; every thread of the workgroup must call them.
 
@@ -404,8 +433,7 @@ __device__ __forceinline__ void compute_tile(const _Float16* stage, const half8_
     sv[r] = x;
     mx = fmaxf(mx, x);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_over_row_groups(mx);
   // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
   // tile, where acc.m is still -inf.
   const float m_new = fmaxf(acc.m, mx);
@@ -425,8 +453,8 @@ __device__ __forceinline__ void compute_tile(const _Float16* stage, const half8_
   acc.l = acc.l * alpha + psum;
 
   // Row r of every PV tile is head r; lane h holds head h's alpha.
-  const float a0 = __shfl(alpha, 0), a1 = __shfl(alpha, 1), a2 = __shfl(alpha, 2),
-              a3 = __shfl(alpha, 3);
+  const float a0 = lane_value(alpha, 0), a1 = lane_value(alpha, 1), a2 = lane_value(alpha, 2),
+              a3 = lane_value(alpha, 3);
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     acc.O[db][0] *= a0;
@@ -479,8 +507,7 @@ __device__ __forceinline__ void merge_waves(const WaveAcc& acc, MergeLds& sm, fl
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int G = lane >> 4, j = lane & 15;
   const float kNegInf = -__builtin_inff();
-  float l = acc.l + __shfl_xor(acc.l, 16);
-  l += __shfl_xor(l, 32);
+  const float l = sum_over_row_groups(acc.l);
   lds_barrier();     // earlier readers of sm are done
   if (lane < kGroup) {
     sm.m[wv][lane] = acc.m;
@@ -529,6 +556,21 @@ __device__ long long this_piece_start(const Params& P, long long total) {
   return (long long)blockIdx.x * piece_len(P, total);
 }
 
+// Empty sequences get zero rows and empty segment descriptors (workgroup w
+// takes b = w, w + grid, ...). Lengths come from the length register or
+// scalar loads, so nothing here waits for vector loads in flight.
+__device__ __forceinline__ void zero_empty_sequences(const Params& P, int lens_v, int w) {
+  const int tid = threadIdx.x;
+  for (int b = w; b < P.batch; b += gridDim.x) {
+    if (seq_len_of(P, lens_v, b) == 0) {
+      uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * kQHeads * kDim);
+      dst[tid] = (uint4_t){0u, 0u, 0u, 0u};
+      dst[tid + kThreads] = (uint4_t){0u, 0u, 0u, 0u};
+      if (tid < kKvHeads) P.seg_desc[b * kKvHeads + tid] = make_int2(0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- kernel 1
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(Params P) {
@@ -543,17 +585,6 @@ void gqa_decode_pieces(Params P) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
   const int G = lane >> 4, j = lane & 15;
   const int w = blockIdx.x;
-
-  // Empty sequences get zero rows and empty segment descriptors
-  // (workgroup w takes b = w, w + grid, ...).
-  for (int b = w; b < P.batch; b += gridDim.x) {
-    if (clamp_len(P.seq_lens[b], P.capacity) == 0) {
-      uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * kQHeads * kDim);
-      dst[tid] = (uint4_t){0u, 0u, 0u, 0u};
-      dst[tid + kThreads] = (uint4_t){0u, 0u, 0u, 0u};
-      if (tid < kKvHeads) P.seg_desc[b * kKvHeads + tid] = make_int2(0, 0);
-    }
-  }
 
   long long total, p0, found;
   int found_b, found_len = 0;
@@ -576,7 +607,10 @@ void gqa_decode_pieces(Params P) {
   }
   total = uniform64(total);
   p0 = uniform64(p0);
-  if (p0 >= total) return;                          // uniform: this piece is empty
+  if (p0 >= total) {                                // uniform: this piece is empty
+    zero_empty_sequences(P, lens_v, w);
+    return;
+  }
   found = uniform64(found);
   found_b = __builtin_amdgcn_readfirstlane(found_b);
   const long long Q = piece_len(P, total);
@@ -598,6 +632,7 @@ void gqa_decode_pieces(Params P) {
   int pt = s.lo + kTileRows * wv;
   const bool pf_ok = tile_first(P, pf, pt, p1, wv, lens_v);
   issue_tile(P, pf, pt, pf_ok, st0, qslot);
+  zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
 
   while (true) {
