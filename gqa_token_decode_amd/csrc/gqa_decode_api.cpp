@@ -30,7 +30,8 @@ namespace {
 constexpr size_t kQBytesPerSeq = (size_t)GQA_NUM_Q_HEADS * GQA_HEAD_DIM * 2;           // 8 KiB
 constexpr size_t kKvBytesPerPos = (size_t)2 * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * 2;    // 4 KiB
 constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
-constexpr int kMinPieceDefault = 128;      // rows; keeps tiny decodes from over-splitting
+constexpr int kMinPieceDefault = 128;      // cost units: two 64-row steps of a workgroup
+constexpr int kSegCostDefault = 128;       // fixed cost of a segment, in row units
 // Forced chunk lengths may not make the workspace exceed this.
 constexpr size_t kMaxForcedWorkspace = (size_t)4 << 30;
 
@@ -117,6 +118,7 @@ gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece) {
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
   cfg.pieces = (di.cus > 0 ? di.cus : 256) * (di.resident > 0 ? di.resident : 1) * per_slot;
   cfg.min_piece = env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30);
+  cfg.seg_cost = env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20);
   cfg.forced_piece = forced_piece;
   return cfg;
 }

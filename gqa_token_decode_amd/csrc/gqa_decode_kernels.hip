@@ -6,12 +6,14 @@
 //   out[b,h] = softmax_i(q_scale / sqrt(128) * q[b,h] . K[b,g,i]) . V[b,g,i],  i < L.
 //
 // Work split (decided on the device from seq_lens; the host never reads them)
-//   The valid rows of all (b, g) pairs are laid end to end, b-major then g:
-//   segment (b, g) covers flat rows [8*P_b + g*L_b, +L_b), P_b = L_0 + ... +
-//   L_{b-1}. That flat range of 8*sum(L) rows is cut into equal pieces of Q
-//   rows, one per workgroup, so every workgroup streams the same number of
-//   K/V bytes and all finish together. A piece covers the tail of one
-//   segment, any number of whole segments and the head of another.
+//   Every (b, g) pair with L_b > 0 is a segment of cost c0 + L_b: c0 units
+//   stand for its fixed cost (q, merge, output) and come first, then one unit
+//   per valid row. The segments are laid end to end, b-major then g, and that
+//   cost line is cut into equal pieces of Q units, one per workgroup, so
+//   workgroups get equal work and finish together, and tiny segments spread
+//   over workgroups instead of queueing in one. A piece covers the tail of
+//   one segment, any number of whole segments and the head of another; a
+//   piece that holds only fixed-cost units of a segment skips it.
 //   A segment inside one piece is finished by that workgroup (normalised
 //   fp16 output). A segment cut by piece boundaries gets one fp32 partial
 //   (running max, softmax denominator, unnormalised weighted V sum) per
@@ -93,10 +95,16 @@ struct Params {
   int pieces;          // automatic split: number of equal pieces
   int min_piece;       // automatic split: lower bound on the piece length
   int forced_piece;    // > 0: fixed piece length
+  int seg_cost;        // fixed cost units per segment (c0)
   float scale_log2;    // q_scale / sqrt(128) * log2(e)
 };
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
+
+// Cost of sequence b on the cost line: 8 segments of c0 + L units, or 0.
+__device__ __forceinline__ long long seq_cost(long long len, int c0) {
+  return len > 0 ? 8 * (len + c0) : 0;
+}
 
 // Length of sequence b read through the scalar path (b must be uniform), so
 // waiting for it does not wait for vector loads in flight.
@@ -176,8 +184,8 @@ __device__ long long block_scan(long long v, long long* red, long long* total) {
   return v + before;
 }
 
-// Batch entry b whose flat rows [8*P_b, 8*P_{b+1}) hold flat row p, and
-// 8*P_b. p must be below 8 * sum(L).
+// Batch entry b whose cost range holds position p, and the start of that
+// range. p must be below the total cost.
 __device__ void locate(long long p, const Params& P, long long* red, long long* found,
                        int* found_b, int* found_len) {
   if (threadIdx.x == 0) *found_b = -1;
@@ -186,9 +194,10 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
     const int b = b0 + threadIdx.x;
     const long long len = b < P.batch ? clamp_len(P.seq_lens[b], P.capacity) : 0;
     long long total;
-    const long long incl = block_scan(8 * len, red, &total);
-    const long long lo = before + incl - 8 * len;
-    if (len > 0 && p >= lo && p < lo + 8 * len) {
+    const long long cost = seq_cost(len, P.seg_cost);
+    const long long incl = block_scan(cost, red, &total);
+    const long long lo = before + incl - cost;
+    if (cost > 0 && p >= lo && p < lo + cost) {
       *found_b = b;
       *found = lo;
       *found_len = (int)len;
@@ -201,7 +210,7 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
 
 // Small batches (<= 64): every wave finds the total and the batch entry of
 // flat row p on its own (lane b holds sequence b), with no workgroup barrier.
-// Returns the total valid rows; *found_b = -1 if p is past them. *lens_v
+// Returns the total cost; *found_b = -1 if p is past it. *lens_v
 // keeps the clamped lengths (lane b holds sequence b's), so later segment
 // steps read them with readlane instead of a dependent memory load.
 __device__ long long wave_plan(const Params& P, long long (*piece_start)(const Params&, long long),
@@ -209,7 +218,8 @@ __device__ long long wave_plan(const Params& P, long long (*piece_start)(const P
   const int lane = threadIdx.x & 63;
   const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
   *lens_v = (int)len;
-  long long incl = 8 * len;
+  const long long cost = seq_cost(len, P.seg_cost);
+  long long incl = cost;
   for (int o = 1; o < 64; o <<= 1) {
     const long long t = __shfl_up(incl, o);
     if (lane >= o) incl += t;
@@ -217,8 +227,8 @@ __device__ long long wave_plan(const Params& P, long long (*piece_start)(const P
   const long long total = __shfl(incl, 63);
   const long long p = piece_start(P, total);
   *p_out = p;
-  const long long lo = incl - 8 * len;
-  const unsigned long long hit = __ballot(len > 0 && p >= lo && p < incl);
+  const long long lo = incl - cost;
+  const unsigned long long hit = __ballot(cost > 0 && p >= lo && p < incl);
   if (hit == 0) {
     *found_b = -1;
     return total;
@@ -238,17 +248,23 @@ struct Segment {
 // Position of 16-byte chunk c of row r inside an LDS V stage.
 __device__ __forceinline__ int vchunk(int r, int c) { return c ^ (2 * (r & 7)); }
 
-// Rows [lo, hi) of segment (b, g) that lie in this workgroup's piece; the
-// segment covers flat rows [off, off + len). Wave-uniform.
+// Rows [lo, hi) of segment (b, g) that lie in this workgroup's piece; row i
+// of the segment sits at cost position off + i (its fixed-cost units are
+// [off - c0, off)). Wave-uniform.
 struct Seg {
   int b, g, len, lo, hi;
   long long off;
 };
 
 __device__ __forceinline__ void seg_set_range(Seg& s, long long p_begin, long long p_end) {
-  s.lo = (int)(p_begin > s.off ? p_begin - s.off : 0);
-  const long long e = p_end - s.off;
-  s.hi = (int)(e < s.len ? e : s.len);
+  const long long b = p_begin - s.off, e = p_end - s.off;
+  s.lo = (int)(b <= 0 ? 0 : (b < s.len ? b : s.len));
+  s.hi = (int)(e <= 0 ? 0 : (e < s.len ? e : s.len));
+}
+
+// Whether the piece ending at p_end holds rows of a segment after s.
+__device__ __forceinline__ bool more_segments(const Params& P, const Seg& s, long long p_end) {
+  return s.off + s.len + P.seg_cost < p_end;
 }
 
 // Clamped length of sequence b (b uniform): from the wave's length register
@@ -261,7 +277,7 @@ __device__ __forceinline__ int seq_len_of(const Params& P, int lens_v, int b) {
 // Advance to the next segment (next KV head of b, else the next non-empty
 // sequence). Only called while rows remain below p_end, so one exists.
 __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end, int lens_v) {
-  const long long end = s.off + s.len;
+  const long long end = s.off + s.len + P.seg_cost;
   if (s.g + 1 < kKvHeads) {
     s.g += 1;
   } else {
@@ -286,7 +302,7 @@ __device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long 
                                           int lens_v) {
   t += kStepRows;
   while (t >= s.hi) {
-    if (s.off + s.hi >= p_end) return false;
+    if (!more_segments(P, s, p_end)) return false;
     seg_next(P, s, p_end, lens_v);
     t = s.lo + kTileRows * wv;
   }
@@ -297,7 +313,7 @@ __device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long 
 __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long long p_end, int wv,
                                            int lens_v) {
   while (t >= s.hi) {
-    if (s.off + s.hi >= p_end) return false;
+    if (!more_segments(P, s, p_end)) return false;
     seg_next(P, s, p_end, lens_v);
     t = s.lo + kTileRows * wv;
   }
@@ -308,16 +324,18 @@ __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long
 // (K, then V) and the segment's 4 query rows into the wave's q slot, in this
 // order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros. With live ==
 // false the buffers are empty: the same 9 loads return zeros without
-// touching memory, so every pipeline step has the same shape.
+// touching memory, so every pipeline step has the same shape. The q load is
+// live only for a wave's first tile of a segment (live_q); later tiles reuse
+// the q registers, and their empty q load leaves zeros in the slot.
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
-                                           _Float16* stage, _Float16* qslot) {
+                                           bool live_q, _Float16* stage, _Float16* qslot) {
   const int lane = threadIdx.x & 63;
   const size_t seg_elems = (size_t)P.capacity * kDim;
   const _Float16* kb = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_elems;
   const _Float16* vb = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_elems;
   const _Float16* qg = P.q + ((size_t)s.b * kQHeads + s.g * kGroup) * kDim;
   const int nbytes = live ? s.hi * (kDim * 2) : 0;
-  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, live ? kQHalves * 2 : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, live && live_q ? kQHalves * 2 : 0, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nbytes, kBufferFlags);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)qslot, 16, 16 * lane, 0, 0, 0);
@@ -375,49 +393,68 @@ __device__ __forceinline__ void read_q(const _Float16* qslot, half8_t (&qb)[4]) 
   qb[3] = __builtin_bit_cast(half8_t, j < kGroup ? x3 : zero);
 }
 
-// Fold tile rows [t, t + 16) held in an LDS stage into acc.
-__device__ __forceinline__ void compute_tile(const _Float16* stage, const half8_t (&qb)[4], int t,
-                                             int hi, float scale_log2, WaveAcc& acc) {
-  const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
-  const float kNegInf = -__builtin_inff();
+// LDS addresses of this lane's operand reads in stage 0 of its wave; stage 1
+// lies kStageHalves halves higher (an immediate offset of the reads).
+struct LdsReads {
+  unsigned k[4];     // K: lane (G, j) reads row j, logical chunk 4kk + G
+  unsigned v[8];     // V, transposed: row 4G + j/4, columns 16db + 4(j%4) .. +3
+};
 
-  // Per-lane LDS addresses, recomputed every step (a few VALU ops; the empty
-  // asm hides their loop invariance so they are not kept live).
-  int jj = j;
-  asm volatile("" : "+v"(jj));
-  const int rr = 4 * G + (jj >> 2);
-  const unsigned kbase = lds_addr(stage);
+__device__ __forceinline__ LdsReads lds_reads(const _Float16* stage0) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
+  const int rr = 4 * G + (j >> 2);
+  const unsigned kbase = lds_addr(stage0);
   const unsigned vbase = kbase + 2 * kTileHalves;
-  unsigned ka[4], va[8];
+  LdsReads r;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) ka[kk] = kbase + 2 * (jj * kDim + 8 * vchunk(jj, 4 * kk + G));
+  for (int kk = 0; kk < 4; ++kk) r.k[kk] = kbase + 2 * (j * kDim + 8 * vchunk(j, 4 * kk + G));
   // Transposed reads: lane (G, j) supplies the address of row 4G + j/4,
   // columns 16*db + 4*(j%4) .. +3 and receives column 16*db + j of rows
   // 4G .. 4G+3.
 #pragma unroll
   for (int db = 0; db < 8; ++db)
-    va[db] = vbase + 2 * (rr * kDim + 8 * vchunk(rr, 2 * db + ((jj & 3) >> 1)) + 4 * (jj & 1));
-  uint4_t k0, k1, k2, k3;
-  short4_t v0, v1, v2, v3, v4, v5, v6, v7;
+    r.v[db] = vbase + 2 * (rr * kDim + 8 * vchunk(rr, 2 * db + ((j & 3) >> 1)) + 4 * (j & 1));
+  return r;
+}
+
+// Read the K and V operands of one stage (byte offset OFF from stage 0).
+template <int OFF>
+__device__ __forceinline__ void read_stage(const LdsReads& a, uint4_t (&k)[4], short4_t (&v)[8]) {
   asm volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %13\n\t"
-      "ds_read_b128 %2, %14\n\t"
-      "ds_read_b128 %3, %15\n\t"
-      "ds_read_b64_tr_b16 %4, %16\n\t"
-      "ds_read_b64_tr_b16 %5, %17\n\t"
-      "ds_read_b64_tr_b16 %6, %18\n\t"
-      "ds_read_b64_tr_b16 %7, %19\n\t"
-      "ds_read_b64_tr_b16 %8, %20\n\t"
-      "ds_read_b64_tr_b16 %9, %21\n\t"
-      "ds_read_b64_tr_b16 %10, %22\n\t"
-      "ds_read_b64_tr_b16 %11, %23\n\t"
+      "ds_read_b128 %0, %12 offset:%24\n\t"
+      "ds_read_b128 %1, %13 offset:%24\n\t"
+      "ds_read_b128 %2, %14 offset:%24\n\t"
+      "ds_read_b128 %3, %15 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %10, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %11, %23 offset:%24\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k0), "=&v"(k1), "=&v"(k2), "=&v"(k3), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3),
-        "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
-      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
-        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
+        "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a.k[0]), "v"(a.k[1]), "v"(a.k[2]), "v"(a.k[3]), "v"(a.v[0]), "v"(a.v[1]),
+        "v"(a.v[2]), "v"(a.v[3]), "v"(a.v[4]), "v"(a.v[5]), "v"(a.v[6]), "v"(a.v[7]), "n"(OFF)
       : "memory");
+}
+
+// Fold tile rows [t, t + 16) held in LDS stage `par` into acc.
+__device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const half8_t (&qb)[4],
+                                             int t, int hi, float scale_log2, WaveAcc& acc) {
+  const int lane = threadIdx.x & 63, G = lane >> 4;
+  const float kNegInf = -__builtin_inff();
+  uint4_t kr[4];
+  short4_t vr[8];
+  if (par)
+    read_stage<kStageHalves * 2>(la, kr, vr);
+  else
+    read_stage<0>(la, kr, vr);
+  const uint4_t k0 = kr[0], k1 = kr[1], k2 = kr[2], k3 = kr[3];
+  const short4_t v0 = vr[0], v1 = vr[1], v2 = vr[2], v3 = vr[3], v4 = vr[4], v5 = vr[5],
+                 v6 = vr[6], v7 = vr[7];
 
   float4_t sc = {0.f, 0.f, 0.f, 0.f};
   sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k0), qb[0], sc, 0, 0, 0);
@@ -472,19 +509,23 @@ __device__ __forceinline__ void compute_tile(const _Float16* stage, const half8_
   }
 }
 
-// One pipeline step for the tile held in `cur`: take its q from the q slot,
-// issue the next tile (or an empty load group) into `nxt` and the q slot,
-// wait for the current tile, fold it in. Loads complete in issue order, so
-// "all but the newest N" waits are exact.
-__device__ __forceinline__ void tile_step(const Params& P, _Float16* cur, _Float16* nxt,
-                                          _Float16* qslot, bool has_next, const Seg& nseg, int nt,
-                                          int t, int hi, WaveAcc& acc) {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
-  half8_t qb[4];
-  read_q(qslot, qb);
-  issue_tile(P, nseg, nt, has_next, nxt, qslot);
+// One pipeline step for the tile held in `cur`: on the wave's first tile of
+// a segment, take q from the q slot; issue the next tile (or an empty load
+// group) into `nxt` and the q slot; wait for the current tile; fold it in.
+// Loads complete in issue order, so "all but the newest N" waits are exact
+// (vector stores issued in between only make them wait longer).
+__device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, int par,
+                                          _Float16* nxt, _Float16* qslot, bool first,
+                                          bool has_next, const Seg& nseg, int nt,
+                                          bool next_new_seg, int t, int hi, half8_t (&qb)[4],
+                                          WaveAcc& acc) {
+  if (first) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
+    read_q(qslot, qb);
+  }
+  issue_tile(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
-  compute_tile(cur, qb, t, hi, P.scale_log2, acc);
+  compute_tile(la, par, qb, t, hi, P.scale_log2, acc);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -593,8 +634,9 @@ void gqa_decode_pieces(Params P) {
     total = wave_plan(P, this_piece_start, &p0, &found, &found_b, &lens_v);
   } else {
     long long part = 0;
-    for (int b = tid; b < P.batch; b += kThreads) part += clamp_len(P.seq_lens[b], P.capacity);
-    total = 8 * block_sum(part, red);
+    for (int b = tid; b < P.batch; b += kThreads)
+      part += seq_cost(clamp_len(P.seq_lens[b], P.capacity), P.seg_cost);
+    total = block_sum(part, red);
     p0 = this_piece_start(P, total);
     found_b = -1;
     if (p0 < total) {
@@ -620,18 +662,24 @@ void gqa_decode_pieces(Params P) {
   s.b = found_b;
   s.len = P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, s.b)
                         : __builtin_amdgcn_readfirstlane(found_len);
-  s.g = (int)((p0 - found) / s.len);
-  s.off = found + (long long)s.g * s.len;
+  const long long stride = (long long)s.len + P.seg_cost;
+  s.g = (int)((p0 - found) / stride);
+  s.off = found + (long long)s.g * stride + P.seg_cost;
   seg_set_range(s, p0, p1);
+  if (s.hi <= s.lo) {                               // only fixed-cost units in this piece
+    zero_empty_sequences(P, lens_v, w);
+    return;
+  }
 
   // Prime the pipeline with this wave's first tile.
   _Float16* st0 = stages[wv][0];
   _Float16* st1 = stages[wv][1];
   _Float16* qslot = qslots[wv];
+  const LdsReads la = lds_reads(st0);
   Seg pf = s;
   int pt = s.lo + kTileRows * wv;
   const bool pf_ok = tile_first(P, pf, pt, p1, wv, lens_v);
-  issue_tile(P, pf, pt, pf_ok, st0, qslot);
+  issue_tile(P, pf, pt, pf_ok, true, st0, qslot);
   zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
 
@@ -642,11 +690,13 @@ void gqa_decode_pieces(Params P) {
     acc.m = -__builtin_inff();
     acc.l = 0.f;
     // This wave's tiles of s; the prefetch cursor (pf, pt) is on the first.
+    half8_t qb[4];
     for (int t = s.lo + kTileRows * wv; t < s.hi; t += kStepRows) {
       Seg nf = pf;
       int nt = pt;
       const bool n_ok = tile_next(P, nf, nt, p1, wv, lens_v);
-      tile_step(P, par ? st1 : st0, par ? st0 : st1, qslot, n_ok, nf, nt, t, s.hi, acc);
+      tile_step(P, la, par, par ? st0 : st1, qslot, t == s.lo + kTileRows * wv, n_ok, nf, nt,
+                nf.off != s.off, t, s.hi, qb, acc);
       pf = nf;
       pt = nt;
       par ^= 1;
@@ -672,7 +722,7 @@ void gqa_decode_pieces(Params P) {
       if (d == 0) P.ws_ml[slot * kGroup + hh] = make_float2(M, den);
     }
 
-    if (s.off + s.hi >= p1) break;
+    if (!more_segments(P, s, p1)) break;
     seg_next(P, s, p1, lens_v);
   }
 }
@@ -790,6 +840,7 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.pieces = (int)grid;
   P.min_piece = cfg.min_piece;
   P.forced_piece = cfg.forced_piece;
+  P.seg_cost = cfg.forced_piece > 0 ? 0 : cfg.seg_cost;
   P.scale_log2 = score_scale_log2;
 
   hipError_t err = hipSuccess;

@@ -14,6 +14,7 @@ struct SplitConfig {
   int pieces;         // automatic split: number of equal pieces (one workgroup each)
   int min_piece;      // automatic split: lower bound on the piece length (rows)
   int forced_piece;   // > 0: fixed piece length; the grid then covers batch*capacity rows
+  int seg_cost;       // automatic split: fixed cost units per (sequence, KV head) segment
 };
 
 // Workgroups of the pieces kernel that fit on one CU at once (0 on error).
