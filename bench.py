@@ -80,8 +80,15 @@ def traffic_from_profiles(workload: str):
 def cpu_baseline(w, min_seconds: float):
     import numpy as np
 
+    from oracle.formats import bf16_to_f64
     from oracle.reference import decode_ragged
 
+    if w.elem == "bf16":     # the oracle takes the element values widened exactly
+        q = bf16_to_f64(w.q)
+        kval = [bf16_to_f64(k) for k in w.k_valid]
+        vval = [bf16_to_f64(v) for v in w.v_valid]
+    else:
+        q, kval, vval = w.q, w.k_valid, w.v_valid
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -89,7 +96,7 @@ def cpu_baseline(w, min_seconds: float):
         threads = len(os.sched_getaffinity(0))
     reps, t0 = 0, time.perf_counter()
     while True:
-        decode_ragged(w.q, w.k_valid, w.v_valid, w.q_scale)
+        decode_ragged(q, kval, vval, w.q_scale)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -163,6 +170,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--elem", default="f16", choices=["f16", "bf16"],
+                    help="element type of q, kv and out (bf16 uses the typed entry point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -189,11 +198,11 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.get(args.workload)
+    w = workloads.get(args.workload, args.elem)
     kv_bytes = w.kv_bytes_read
     sum_len = int(w.valid_lengths.sum())
 
-    q = torch.from_numpy(w.q).to(dev)
+    q = w.q_to_device(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
     kv0 = w.kv_to_device(dev)
     rot = max(1, math.ceil(ROTATE_TARGET_BYTES / max(kv_bytes, 1)))
@@ -259,7 +268,7 @@ def main(argv=None):
     assert np.all(np.isfinite(res)), "non-finite decode output"
 
     achieved = kv_bytes / (pieces_us * 1e-6) / 1e9
-    traffic = traffic_from_profiles(args.workload)
+    traffic = traffic_from_profiles(args.workload) if args.elem == "f16" else None
     line = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 3),
@@ -273,7 +282,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.elem,
         "data": "synthetic",
         "config": {
             "workload": args.workload,

@@ -9,8 +9,10 @@ PyTorch supplies device memory and the current stream; the decode itself
 never goes through torch operators.
 
 Public API (names and keyword arguments follow the ``sm110_gqa_decode``
-entry point documented on the FlashInfer PR #5052 analysis page, section 1):
-    gqa_decode(q, kv, sequence_lengths, *, out=None, q_scale=1.0, chunk_len=0)
+entry point documented on the FlashInfer PR #5052 analysis page, section 1;
+bf16 tensors and the K/V scales are this library's extension):
+    gqa_decode(q, kv, sequence_lengths, *, out=None, q_scale=1.0, chunk_len=0,
+               k_scale=1.0, v_scale=1.0)
 """
 from __future__ import annotations
 
@@ -61,6 +63,8 @@ def load_library():
     lib.gqa_decode.restype = i32
     lib.gqa_decode_chunked.argtypes = [vp, vp, vp, vp, f32, i32, i32, i32, vp]
     lib.gqa_decode_chunked.restype = i32
+    lib.gqa_decode_typed.argtypes = [vp, vp, vp, vp, i32, f32, f32, f32, i32, i32, i32, vp]
+    lib.gqa_decode_typed.restype = i32
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32]
     lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_decode_release_workspace.argtypes = []
@@ -99,21 +103,29 @@ def _check_device(name, t):
         raise ValueError(f"{name} must be on a GPU device, got {t.device}")
 
 
+_DTYPES = {torch.float16: 0, torch.bfloat16: 1}   # gqa_dtype codes
+
+
 def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor, *,
                out: Optional[torch.Tensor] = None, q_scale: float = 1.0,
-               chunk_len: int = 0) -> torch.Tensor:
-    """Decode one token of FP16 GQA (32 query heads, 8 KV heads, dim 128).
+               chunk_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Decode one token of GQA (32 query heads, 8 KV heads, dim 128).
 
-    q: fp16 [batch, 32, 128]; kv: fp16 [batch, 2, 8, capacity, 128] with K at
-    index 0 and V at index 1 of axis 1; sequence_lengths: int32 [batch] on the
-    same device (values clamped to [0, capacity]). ``out`` (optional,
-    caller-owned, fp16, q's shape) receives the result and is returned;
-    otherwise a new tensor is allocated. Scores are scaled by
-    ``q_scale / sqrt(128)``. ``chunk_len`` > 0 fixes the split-KV piece
-    length (0 = automatic). Enqueued on the current stream of q's device.
+    q: fp16 or bf16 [batch, 32, 128]; kv: same dtype [batch, 2, 8, capacity,
+    128] with K at index 0 and V at index 1 of axis 1; sequence_lengths:
+    int32 [batch] on the same device (values clamped to [0, capacity]).
+    ``out`` (optional, caller-owned, q's dtype and shape) receives the result
+    and is returned; otherwise a new tensor is allocated. Scores are scaled by
+    ``q_scale * k_scale / sqrt(128)`` and the output by ``v_scale``.
+    ``chunk_len`` > 0 fixes the split-KV piece length (0 = automatic).
+    Enqueued on the current stream of q's device.
     """
-    _check_tensor("q", q, torch.float16, 3)
-    _check_tensor("kv", kv, torch.float16, 5)
+    if isinstance(q, torch.Tensor) and q.dtype in _DTYPES:
+        dtype = q.dtype
+    else:
+        dtype = torch.float16
+    _check_tensor("q", q, dtype, 3)
+    _check_tensor("kv", kv, dtype, 5)
     _check_tensor("sequence_lengths", sequence_lengths, torch.int32, 1)
     B = q.shape[0]
     kshape = kv.shape
@@ -133,7 +145,7 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensor("out", out, torch.float16, 3)
+        _check_tensor("out", out, dtype, 3)
         if out.shape != q.shape or out.device != dev:
             _check_device("out", out)
             raise ValueError("out must have q's shape and device")
@@ -142,7 +154,11 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
     lib = _lib if _lib is not None else load_library()
     index = dev.index if dev.index is not None else torch.cuda.current_device()
     stream = torch._C._cuda_getCurrentRawStream(index)
-    if chunk_len:
+    if dtype != torch.float16 or k_scale != 1.0 or v_scale != 1.0:
+        st = lib.gqa_decode_typed(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
+                                  out.data_ptr(), _DTYPES[dtype], float(q_scale), float(k_scale),
+                                  float(v_scale), B, kshape[3], chunk_len, stream)
+    elif chunk_len:
         st = lib.gqa_decode_chunked(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
                                     out.data_ptr(), float(q_scale), B, kshape[3], chunk_len,
                                     stream)

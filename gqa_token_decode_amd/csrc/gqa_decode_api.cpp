@@ -197,12 +197,15 @@ int check_args(const void* q, const void* kv, const int32_t* seq_lens, const voi
   return GQA_OK;
 }
 
-int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* out, float q_scale,
-                int batch, int capacity, int chunk_len, hipStream_t stream) {
+int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
+                float q_scale, float k_scale, float v_scale, int batch, int capacity,
+                int chunk_len, hipStream_t stream) {
   int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len);
   if (st != GQA_OK) return st;
-  if (!std::isfinite(q_scale))
-    return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_scale must be finite");
+  if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode: unknown dtype %d", dtype);
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_scale, k_scale and v_scale must be finite");
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
@@ -242,9 +245,10 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
       } else {
         void* ws = get_workspace(dev, stream, pbytes, &st);
         if (ws) {
-          // Scores are formed as dot * q_scale / sqrt(128) * log2(e), so the
-          // kernel can use the hardware base-2 exponential.
-          const double scale = (double)q_scale / std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
+          // Scores are formed as dot * q_scale * k_scale / sqrt(128) * log2(e),
+          // so the kernel can use the hardware base-2 exponential.
+          const double scale = (double)q_scale * (double)k_scale /
+                               std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
           hipEvent_t* ev = nullptr;
           hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
           if (g_profiling && hipStreamIsCapturing(stream, &cap) == hipSuccess &&
@@ -257,8 +261,11 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
             }
             if (g_profile_used < g_profile.size()) ev = g_profile[g_profile_used++].ev;
           }
-          const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, (float)scale, batch,
-                                                  capacity, cfg, grid, ws, stream, ev);
+          const gqa::ElemType elem =
+              dtype == GQA_DTYPE_BF16 ? gqa::ElemType::kBf16 : gqa::ElemType::kF16;
+          const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, elem, (float)scale,
+                                                  v_scale, batch, capacity, cfg, grid, ws, stream,
+                                                  ev);
           if (e != hipSuccess)
             st = fail(GQA_ERR_LAUNCH, "gqa_decode: kernel launch failed: %s", hipGetErrorString(e));
         }
@@ -275,12 +282,21 @@ extern "C" {
 
 int gqa_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out, float q_scale,
                int batch, int capacity, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, q_scale, batch, capacity, 0, stream);
+  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, q_scale, 1.0f, 1.0f, batch, capacity, 0,
+                     stream);
 }
 
 int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                        float q_scale, int batch, int capacity, int chunk_len, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, q_scale, batch, capacity, chunk_len, stream);
+  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, q_scale, 1.0f, 1.0f, batch, capacity,
+                     chunk_len, stream);
+}
+
+int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
+                     float q_scale, float k_scale, float v_scale, int batch, int capacity,
+                     int chunk_len, hipStream_t stream) {
+  return decode_impl(q, kv, seq_lens, out, dtype, q_scale, k_scale, v_scale, batch, capacity,
+                     chunk_len, stream);
 }
 
 size_t gqa_decode_workspace_bytes(int batch, int capacity) {

@@ -60,6 +60,10 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t e16_t;      // 16-bit element storage: fp16 or bf16 bit patterns
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -83,10 +87,10 @@ constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
 constexpr int kSlotFloats = kGroup * (2 + kDim);   // one partial: 4 x (max, den) + 4 x 128 sums
 
 struct Params {
-  const _Float16* q;
-  const _Float16* kv;
+  const e16_t* q;
+  const e16_t* kv;
   const int32_t* seq_lens;
-  _Float16* out;
+  e16_t* out;
   float2* ws_ml;       // [2 * grid][4] (max, denominator) per partial and head
   float* ws_acc;       // [2 * grid][4][128] unnormalised weighted V sums
   int2* seg_desc;      // [8 * batch] per segment: first piece, 2 * pieces + second-slot bit
@@ -96,7 +100,8 @@ struct Params {
   int min_piece;       // automatic split: lower bound on the piece length
   int forced_piece;    // > 0: fixed piece length
   int seg_cost;        // fixed cost units per segment (c0)
-  float scale_log2;    // q_scale / sqrt(128) * log2(e)
+  float scale_log2;    // q_scale * k_scale / sqrt(128) * log2(e)
+  float out_scale;     // v_scale: applied to the normalised output
 };
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
@@ -328,12 +333,12 @@ __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long
 // live only for a wave's first tile of a segment (live_q); later tiles reuse
 // the q registers, and their empty q load leaves zeros in the slot.
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
-                                           bool live_q, _Float16* stage, _Float16* qslot) {
+                                           bool live_q, e16_t* stage, e16_t* qslot) {
   const int lane = threadIdx.x & 63;
   const size_t seg_elems = (size_t)P.capacity * kDim;
-  const _Float16* kb = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_elems;
-  const _Float16* vb = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_elems;
-  const _Float16* qg = P.q + ((size_t)s.b * kQHeads + s.g * kGroup) * kDim;
+  const e16_t* kb = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_elems;
+  const e16_t* vb = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_elems;
+  const e16_t* qg = P.q + ((size_t)s.b * kQHeads + s.g * kGroup) * kDim;
   const int nbytes = live ? s.hi * (kDim * 2) : 0;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, live && live_q ? kQHalves * 2 : 0, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nbytes, kBufferFlags);
@@ -359,8 +364,8 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
   }
 }
 
-__device__ __forceinline__ unsigned lds_addr(const _Float16* p) {
-  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const _Float16*)p;
+__device__ __forceinline__ unsigned lds_addr(const e16_t* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const e16_t*)p;
 }
 
 struct WaveAcc {
@@ -371,7 +376,7 @@ struct WaveAcc {
 
 // q^T as the QK B operand, read from the wave's q slot: lane (G, j) takes
 // head j, depth 32kk + 8G .. +7; columns j >= 4 are zero.
-__device__ __forceinline__ void read_q(const _Float16* qslot, half8_t (&qb)[4]) {
+__device__ __forceinline__ void read_q(const e16_t* qslot, uint4_t (&qb)[4]) {
   const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
   int row = j & 3;
   asm volatile("" : "+v"(row));
@@ -387,10 +392,10 @@ __device__ __forceinline__ void read_q(const _Float16* qslot, half8_t (&qb)[4]) 
       : "v"(base)
       : "memory");
   const uint4_t zero = {0u, 0u, 0u, 0u};
-  qb[0] = __builtin_bit_cast(half8_t, j < kGroup ? x0 : zero);
-  qb[1] = __builtin_bit_cast(half8_t, j < kGroup ? x1 : zero);
-  qb[2] = __builtin_bit_cast(half8_t, j < kGroup ? x2 : zero);
-  qb[3] = __builtin_bit_cast(half8_t, j < kGroup ? x3 : zero);
+  qb[0] = j < kGroup ? x0 : zero;
+  qb[1] = j < kGroup ? x1 : zero;
+  qb[2] = j < kGroup ? x2 : zero;
+  qb[3] = j < kGroup ? x3 : zero;
 }
 
 // LDS addresses of this lane's operand reads in stage 0 of its wave; stage 1
@@ -400,7 +405,7 @@ struct LdsReads {
   unsigned v[8];     // V, transposed: row 4G + j/4, columns 16db + 4(j%4) .. +3
 };
 
-__device__ __forceinline__ LdsReads lds_reads(const _Float16* stage0) {
+__device__ __forceinline__ LdsReads lds_reads(const e16_t* stage0) {
   const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
   const int rr = 4 * G + (j >> 2);
   const unsigned kbase = lds_addr(stage0);
@@ -441,8 +446,54 @@ __device__ __forceinline__ void read_stage(const LdsReads& a, uint4_t (&k)[4], s
       : "memory");
 }
 
+// Element-type specific steps: MFMAs on fp16 or bf16 operands (raw 16-bit
+// patterns in registers), the two-part rounding of the softmax weights, and
+// the round-to-nearest-even output conversion.
+template <bool kBf16>
+__device__ __forceinline__ float4_t mfma_qk(uint4_t a, uint4_t b, float4_t c) {
+  if constexpr (kBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float4_t mfma_pv(short4_t a, short4_t b, float4_t c) {
+  if constexpr (kBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                 __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+}
+
+// p = hi + lo with hi = p rounded to the element type and lo = the rest,
+// rounded again: the pair carries 22 (fp16) or 16 (bf16) significant bits.
+template <bool kBf16>
+__device__ __forceinline__ void split_weight(float p, short& hi, short& lo) {
+  if constexpr (kBf16) {
+    const __bf16 h = (__bf16)p;
+    hi = __builtin_bit_cast(short, h);
+    lo = __builtin_bit_cast(short, (__bf16)(p - (float)h));
+  } else {
+    const _Float16 h = (_Float16)p;
+    hi = __builtin_bit_cast(short, h);
+    lo = __builtin_bit_cast(short, (_Float16)(p - (float)h));
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ e16_t to_elem(float x) {
+  if constexpr (kBf16)
+    return __builtin_bit_cast(e16_t, (__bf16)x);
+  else
+    return __builtin_bit_cast(e16_t, (_Float16)x);
+}
+
 // Fold tile rows [t, t + 16) held in LDS stage `par` into acc.
-__device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const half8_t (&qb)[4],
+template <bool kBf16>
+__device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const uint4_t (&qb)[4],
                                              int t, int hi, float scale_log2, WaveAcc& acc) {
   const int lane = threadIdx.x & 63, G = lane >> 4;
   const float kNegInf = -__builtin_inff();
@@ -457,10 +508,10 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
                  v6 = vr[6], v7 = vr[7];
 
   float4_t sc = {0.f, 0.f, 0.f, 0.f};
-  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k0), qb[0], sc, 0, 0, 0);
-  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k1), qb[1], sc, 0, 0, 0);
-  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k2), qb[2], sc, 0, 0, 0);
-  sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, k3), qb[3], sc, 0, 0, 0);
+  sc = mfma_qk<kBf16>(k0, qb[0], sc);
+  sc = mfma_qk<kBf16>(k1, qb[1], sc);
+  sc = mfma_qk<kBf16>(k2, qb[2], sc);
+  sc = mfma_qk<kBf16>(k3, qb[3], sc);
 
   float sv[4];
   float mx = kNegInf;
@@ -477,15 +528,16 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
-  half4_t ph, pl;
+  short4_t ph, pl;
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float p = (sv[r] == kNegInf) ? 0.f : exp2_hw(sv[r] - m_new);
     psum += p;
-    const _Float16 h = (_Float16)p;
+    short h, l;
+    split_weight<kBf16>(p, h, l);
     ph[r] = h;
-    pl[r] = (_Float16)(p - (float)h);
+    pl[r] = l;
   }
   acc.l = acc.l * alpha + psum;
 
@@ -503,9 +555,8 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   const short4_t vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const half4_t vb = __builtin_bit_cast(half4_t, vv[db]);
-    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, acc.O[db], 0, 0, 0);
-    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, acc.O[db], 0, 0, 0);
+    acc.O[db] = mfma_pv<kBf16>(ph, vv[db], acc.O[db]);
+    acc.O[db] = mfma_pv<kBf16>(pl, vv[db], acc.O[db]);
   }
 }
 
@@ -514,10 +565,11 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
 // group) into `nxt` and the q slot; wait for the current tile; fold it in.
 // Loads complete in issue order, so "all but the newest N" waits are exact
 // (vector stores issued in between only make them wait longer).
+template <bool kBf16>
 __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, int par,
-                                          _Float16* nxt, _Float16* qslot, bool first,
+                                          e16_t* nxt, e16_t* qslot, bool first,
                                           bool has_next, const Seg& nseg, int nt,
-                                          bool next_new_seg, int t, int hi, half8_t (&qb)[4],
+                                          bool next_new_seg, int t, int hi, uint4_t (&qb)[4],
                                           WaveAcc& acc) {
   if (first) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
@@ -525,7 +577,7 @@ __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, i
   }
   issue_tile(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
-  compute_tile(la, par, qb, t, hi, P.scale_log2, acc);
+  compute_tile<kBf16>(la, par, qb, t, hi, P.scale_log2, acc);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -613,13 +665,14 @@ __device__ __forceinline__ void zero_empty_sequences(const Params& P, int lens_v
 }
 
 // ---------------------------------------------------------------- kernel 1
+template <bool kBf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(Params P) {
   __shared__ long long red[kWaves];
   __shared__ long long sh_found;
   __shared__ int sh_found_b, sh_found_len;
-  __shared__ __attribute__((aligned(16))) _Float16 stages[kWaves][2][kStageHalves];
-  __shared__ __attribute__((aligned(16))) _Float16 qslots[kWaves][kQHalves];
+  __shared__ __attribute__((aligned(16))) e16_t stages[kWaves][2][kStageHalves];
+  __shared__ __attribute__((aligned(16))) e16_t qslots[kWaves][kQHalves];
   __shared__ __attribute__((aligned(16))) MergeLds sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -672,9 +725,9 @@ void gqa_decode_pieces(Params P) {
   }
 
   // Prime the pipeline with this wave's first tile.
-  _Float16* st0 = stages[wv][0];
-  _Float16* st1 = stages[wv][1];
-  _Float16* qslot = qslots[wv];
+  e16_t* st0 = stages[wv][0];
+  e16_t* st1 = stages[wv][1];
+  e16_t* qslot = qslots[wv];
   const LdsReads la = lds_reads(st0);
   Seg pf = s;
   int pt = s.lo + kTileRows * wv;
@@ -690,12 +743,12 @@ void gqa_decode_pieces(Params P) {
     acc.m = -__builtin_inff();
     acc.l = 0.f;
     // This wave's tiles of s; the prefetch cursor (pf, pt) is on the first.
-    half8_t qb[4];
+    uint4_t qb[4];
     for (int t = s.lo + kTileRows * wv; t < s.hi; t += kStepRows) {
       Seg nf = pf;
       int nt = pt;
       const bool n_ok = tile_next(P, nf, nt, p1, wv, lens_v);
-      tile_step(P, la, par, par ? st0 : st1, qslot, t == s.lo + kTileRows * wv, n_ok, nf, nt,
+      tile_step<kBf16>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kTileRows * wv, n_ok, nf, nt,
                 nf.off != s.off, t, s.hi, qb, acc);
       pf = nf;
       pt = nt;
@@ -712,10 +765,10 @@ void gqa_decode_pieces(Params P) {
       P.seg_desc[s.b * kKvHeads + s.g] =
           make_int2(w, (int)(2 * (last_w - first_w + 1)) + (s.off > p0 ? 1 : 0));
     if (first_w == last_w) {                         // the segment lies in this piece
-      half2_t o;
-      o.x = (_Float16)(n0 / den);
-      o.y = (_Float16)(n1 / den);
-      *reinterpret_cast<half2_t*>(P.out + ((size_t)s.b * kQHeads + s.g * kGroup + hh) * kDim + d) = o;
+      const float vs = P.out_scale;
+      const unsigned o = (unsigned)to_elem<kBf16>(n0 / den * vs) |
+                         ((unsigned)to_elem<kBf16>(n1 / den * vs) << 16);
+      *reinterpret_cast<unsigned*>(P.out + ((size_t)s.b * kQHeads + s.g * kGroup + hh) * kDim + d) = o;
     } else {
       const long long slot = slot_of(s.off, p0, w);
       *reinterpret_cast<float2*>(P.ws_acc + (slot * kGroup + hh) * kDim + d) = make_float2(n0, n1);
@@ -735,6 +788,7 @@ constexpr int kCombineSubsets = kThreads / 32;   // 8 subsets x 32 four-column g
 // row; otherwise exit. Each of 8 thread subsets merges every 8th partial
 // with a running max (its loads do not depend on each other), then the
 // subsets are merged through LDS.
+template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
   __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][32][6];
 
@@ -787,25 +841,26 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
       o2 += wt * y[4];
       o3 += wt * y[5];
     }
-    half4_t o;
-    o[0] = (_Float16)(o0 / d);
-    o[1] = (_Float16)(o1 / d);
-    o[2] = (_Float16)(o2 / d);
-    o[3] = (_Float16)(o3 / d);
-    *reinterpret_cast<half4_t*>(P.out + ((size_t)b * kQHeads + head) * kDim + 4 * tid) = o;
+    const float vs = P.out_scale;
+    uint2 o;
+    o.x = (unsigned)to_elem<kBf16>(o0 / d * vs) | ((unsigned)to_elem<kBf16>(o1 / d * vs) << 16);
+    o.y = (unsigned)to_elem<kBf16>(o2 / d * vs) | ((unsigned)to_elem<kBf16>(o3 / d * vs) << 16);
+    *reinterpret_cast<uint2*>(P.out + ((size_t)b * kQHeads + head) * kDim + 4 * tid) = o;
   }
 }
 
 }  // namespace
 
 int resident_workgroups_per_cu() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_decode_pieces, kThreads, 0) !=
-      hipSuccess) {
+  int n16 = 0, nb16 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n16, gqa_decode_pieces<false>, kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb16, gqa_decode_pieces<true>, kThreads, 0) !=
+          hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  return n;
+  return n16 < nb16 ? n16 : nb16;
 }
 
 long long grid_for(int batch, int capacity, const SplitConfig& cfg) {
@@ -824,14 +879,36 @@ size_t segment_bytes_for_batch(int batch) {
   return ((size_t)batch * kKvHeads * sizeof(int2) + 255) & ~(size_t)255;
 }
 
+template <bool kBf16>
+hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
+                          hipEvent_t* events) {
+  hipError_t err = hipSuccess;
+  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * kQHeads)), block(kThreads);
+  if (events) {
+    // Start/stop events attached to the dispatches: they time each kernel's
+    // execution without extra packets between the kernels.
+    hipExtLaunchKernelGGL(gqa_decode_pieces<kBf16>, pieces_grid, block, 0, stream, events[0],
+                          events[1], 0, P);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipExtLaunchKernelGGL(gqa_decode_combine<kBf16>, combine_grid, block, 0, stream, events[2],
+                          events[3], 0, P);
+    return hipGetLastError();
+  }
+  gqa_decode_pieces<kBf16><<<pieces_grid, block, 0, stream>>>(P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  gqa_decode_combine<kBf16><<<combine_grid, block, 0, stream>>>(P);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
-                         float score_scale_log2, int batch, int capacity, const SplitConfig& cfg,
-                         long long grid, void* partials, hipStream_t stream, hipEvent_t* events) {
+                         ElemType elem, float score_scale_log2, float out_scale, int batch,
+                         int capacity, const SplitConfig& cfg, long long grid, void* partials,
+                         hipStream_t stream, hipEvent_t* events) {
   Params P;
-  P.q = static_cast<const _Float16*>(q);
-  P.kv = static_cast<const _Float16*>(kv);
+  P.q = static_cast<const e16_t*>(q);
+  P.kv = static_cast<const e16_t*>(kv);
   P.seq_lens = seq_lens;
-  P.out = static_cast<_Float16*>(out);
+  P.out = static_cast<e16_t*>(out);
   P.seg_desc = reinterpret_cast<int2*>(partials);
   P.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) + segment_bytes_for_batch(batch));
   P.ws_acc = reinterpret_cast<float*>(P.ws_ml + (size_t)(2 * grid) * kGroup);
@@ -842,22 +919,10 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.forced_piece = cfg.forced_piece;
   P.seg_cost = cfg.forced_piece > 0 ? 0 : cfg.seg_cost;
   P.scale_log2 = score_scale_log2;
+  P.out_scale = out_scale;
 
-  hipError_t err = hipSuccess;
-  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * kQHeads)), block(kThreads);
-  if (events) {
-    // Start/stop events attached to the dispatches: they time each kernel's
-    // execution without extra packets between the kernels.
-    hipExtLaunchKernelGGL(gqa_decode_pieces, pieces_grid, block, 0, stream, events[0], events[1], 0, P);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipExtLaunchKernelGGL(gqa_decode_combine, combine_grid, block, 0, stream, events[2], events[3], 0, P);
-    return hipGetLastError();
-  }
-  gqa_decode_pieces<<<pieces_grid, block, 0, stream>>>(P);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  gqa_decode_combine<<<combine_grid, block, 0, stream>>>(P);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  return hipSuccess;
+  return elem == ElemType::kBf16 ? launch_kernels<true>(P, grid, batch, stream, events)
+                                 : launch_kernels<false>(P, grid, batch, stream, events);
 }
 
 }  // namespace gqa

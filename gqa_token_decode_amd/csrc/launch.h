@@ -9,6 +9,9 @@
 
 namespace gqa {
 
+// Element type of q, kv and out.
+enum class ElemType { kF16, kBf16 };
+
 // How the device-side planner cuts the valid rows into pieces.
 struct SplitConfig {
   int pieces;         // automatic split: number of equal pieces (one workgroup each)
@@ -34,7 +37,8 @@ size_t segment_bytes_for_batch(int batch);
 // `events` (may be null) points at four events: start and stop of the pieces
 // kernel, then start and stop of the combine kernel.
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
-                         float score_scale_log2, int batch, int capacity,
+                         ElemType elem, float score_scale_log2, float out_scale, int batch,
+                         int capacity,
                          const SplitConfig& cfg, long long grid, void* partials,
                          hipStream_t stream, hipEvent_t* events);
 

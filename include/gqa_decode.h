@@ -115,6 +115,33 @@ int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, v
                        float q_scale, int batch, int capacity, int chunk_len,
                        hipStream_t stream);
 
+/* Element types accepted by gqa_decode_typed. */
+typedef enum gqa_dtype {
+  GQA_DTYPE_F16 = 0,   /* q, kv and out are IEEE binary16 (the page-4 operation)       */
+  GQA_DTYPE_BF16 = 1   /* q, kv and out are bfloat16 (8-bit exponent, 7-bit fraction)   */
+} gqa_dtype;
+
+/*
+ * gqa_decode_typed -- gqa_decode_chunked for other element types, with
+ * per-tensor K and V scales.
+ *
+ * Same layouts, alignment, ownership and error behaviour as gqa_decode, with
+ * q, kv and out of element type `dtype` (a gqa_dtype; 2 bytes per element
+ * for both). The stored K and V values stand for k_scale * K and
+ * v_scale * V:
+ *   s_i = (q_scale * k_scale / sqrt(128)) * dot(q[b,h,:], kv[b,0,g,i,:])
+ *   out[b,h,:] = v_scale * sum_i softmax(s)_i * kv[b,1,g,i,:]
+ * in fp32, rounded once to the output type (round to nearest even). With
+ * dtype GQA_DTYPE_F16 and k_scale = v_scale = 1 this is gqa_decode_chunked.
+ * The page-4 API is FP16 only (FlashInfer PR #5052 analysis page, section
+ * 1); BF16 and the scales are this library's extension.
+ * chunk_len  as for gqa_decode_chunked (0 = automatic split).
+ * Returns GQA_ERR_BAD_ARG for an unknown dtype or a non-finite scale.
+ */
+int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
+                     float q_scale, float k_scale, float v_scale, int batch, int capacity,
+                     int chunk_len, hipStream_t stream);
+
 /*
  * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace
  * the automatic split needs for (batch, capacity) on the current device

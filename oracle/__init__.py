@@ -14,10 +14,12 @@ section 2, and the benchmark's PyTorch SDPA comparator in section 3
 
 Modules:
   reference -- numpy float64 definition, one (batch, kv head) at a time.
+  formats   -- exact widening of bfloat16 and float64 -> bfloat16 rounding.
   brute     -- scalar pure-Python loops (math.fsum) and an mpmath variant,
                used only to pin ``reference`` on tiny inputs.
 """
+from .formats import bf16_to_f64, round_bf16  # noqa: F401
 from .reference import (  # noqa: F401
     GROUP, HEAD_DIM, NUM_KV_HEADS, NUM_Q_HEADS,
-    decode, decode_head, effective_scale, round_fp16,
+    decode, decode_head, decode_ragged, effective_scale, round_fp16,
 )

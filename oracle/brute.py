@@ -23,17 +23,23 @@ def _head_float(qv, Krows, Vrows, scale):
     return [math.fsum(w[i] * Vrows[i][d] for i in range(L)) / den for d in range(D)]
 
 
-def decode_brute(q, kv, seq_lens, q_scale, n_kv_heads=8):
+def decode_brute(q, kv, seq_lens, q_scale, n_kv_heads=8, k_scale=1.0, v_scale=1.0):
     """q: nested lists [B][H][D]; kv: nested [B][2][G][C][D]; floats.
 
     Returns nested lists [B][H][D]. Query head h reads KV head h // (H/G).
+    k_scale and v_scale (float32 values) multiply every stored K and V
+    element before anything else, as their definition says.
     """
-    import numpy as np  # only to turn q_scale into its float32 value
+    import numpy as np  # only to turn the scales into their float32 values
 
     B = len(q)
     H = len(q[0])
     group = H // n_kv_heads
     scale = float(np.float32(q_scale)) / math.sqrt(len(q[0][0]))
+    ks, vs = float(np.float32(k_scale)), float(np.float32(v_scale))
+    if ks != 1.0 or vs != 1.0:
+        kv = [[[[[x * (ks if kind == 0 else vs) for x in row] for row in head]
+                for head in part] for kind, part in enumerate(seq)] for seq in kv]
     out = []
     for b in range(B):
         C = len(kv[b][0][0])

@@ -1,0 +1,42 @@
+"""Element formats used by the decode's extended entry points (test
+infrastructure; see the package docstring).
+
+bfloat16: the upper 16 bits of an IEEE binary32 value (1 sign bit, 8
+exponent bits with bias 127, 7 fraction bits). Widening is exact; narrowing
+rounds to nearest, ties to even, directly from float64 (no float32 step, so
+there is no double rounding). Subnormals are kept (spacing 2^-133); values
+beyond the largest finite bfloat16 become infinities.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_BF16_MIN_NORMAL_EXP = -126      # smallest normal exponent (as for binary32)
+_BF16_FRACTION_BITS = 7
+_BF16_MAX = float.fromhex("0x1.fep127")
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16 array) as float64."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
+    finite = np.isfinite(x)
+    xf = np.where(finite, x, 0.0)
+    # spacing of bfloat16 numbers around |x|: 2^(e - 7) for |x| in [2^e, 2^(e+1)),
+    # and the subnormal spacing 2^(-126 - 7) below 2^-126
+    _, e = np.frexp(np.abs(xf))              # |x| = f * 2^e, f in [0.5, 1)
+    e = np.maximum(e - 1, _BF16_MIN_NORMAL_EXP)
+    quantum = np.ldexp(1.0, e - _BF16_FRACTION_BITS)
+    r = np.rint(xf / quantum) * quantum      # exact: division by a power of two, rint is RNE
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
+    out[finite] = r[finite]
+    out[~finite] = x[~finite]
+    bits = out.astype(np.float32).view(np.uint32) >> np.uint32(16)   # exact: out is a bfloat16 value
+    return bits.astype(np.uint16)

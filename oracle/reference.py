@@ -21,6 +21,12 @@ design notes):
 
 Rows at or beyond L are sliced away, never read, so their contents (NaN or
 garbage) cannot influence the result.
+
+Extension beyond the page (the library's typed entry point): stored K and V
+values may stand for k_scale * K and v_scale * V (per-tensor scales, float32
+at the ABI). The definition is unchanged with K and V replaced by those
+products; here k_scale joins the score scale and v_scale multiplies the
+normalised output, which is the same real number.
 """
 from __future__ import annotations
 
@@ -34,9 +40,9 @@ HEAD_DIM = 128
 GROUP = NUM_Q_HEADS // NUM_KV_HEADS  # 4 query heads share one KV head
 
 
-def effective_scale(q_scale: float) -> float:
-    """Score scale: float32(q_scale) times the standard 1/sqrt(128)."""
-    return float(np.float32(q_scale)) / math.sqrt(HEAD_DIM)
+def effective_scale(q_scale: float, k_scale: float = 1.0) -> float:
+    """Score scale: float32(q_scale) * float32(k_scale) / sqrt(128)."""
+    return float(np.float32(q_scale)) * float(np.float32(k_scale)) / math.sqrt(HEAD_DIM)
 
 
 def decode_head(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
@@ -55,13 +61,14 @@ def decode_head(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -
 
 
 def decode(q: np.ndarray, kv: np.ndarray, seq_lens, q_scale: float = 1.0,
-           rows=None) -> np.ndarray:
+           rows=None, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Decode one token for every (batch, query head); float64 result.
 
-    q: fp16 [B, 32, 128]; kv: fp16 [B, 2, 8, C, 128]; seq_lens: int [B].
-    ``rows`` optionally restricts the work to a list of (b, h) pairs; the
-    other output rows are left as NaN (used for sampled checks on large
-    inputs).
+    q: [B, 32, 128]; kv: [B, 2, 8, C, 128], any float dtype holding the
+    element values exactly (fp16, or bf16 widened with formats.bf16_to_f64);
+    seq_lens: int [B]. ``rows`` optionally restricts the work to a list of
+    (b, h) pairs; the other output rows are left as NaN (used for sampled
+    checks on large inputs).
     """
     q = np.asarray(q)
     B = q.shape[0]
@@ -69,7 +76,8 @@ def decode(q: np.ndarray, kv: np.ndarray, seq_lens, q_scale: float = 1.0,
     assert q.shape == (B, NUM_Q_HEADS, HEAD_DIM)
     assert kv.shape == (B, 2, NUM_KV_HEADS, C, HEAD_DIM)
     lens = np.asarray(seq_lens).astype(np.int64)
-    scale = effective_scale(q_scale)
+    scale = effective_scale(q_scale, k_scale)
+    vs = float(np.float32(v_scale))
     out = np.full((B, NUM_Q_HEADS, HEAD_DIM), np.nan if rows is not None else 0.0)
     wanted = None
     if rows is not None:
@@ -88,24 +96,26 @@ def decode(q: np.ndarray, kv: np.ndarray, seq_lens, q_scale: float = 1.0,
             K = kv[b, 0, g, :L, :].astype(np.float64)
             V = kv[b, 1, g, :L, :].astype(np.float64)
             for h in heads:
-                out[b, h] = decode_head(q[b, h].astype(np.float64), K, V, scale)
+                out[b, h] = vs * decode_head(q[b, h].astype(np.float64), K, V, scale)
     return out
 
 
-def decode_ragged(q: np.ndarray, k_valid, v_valid, q_scale: float = 1.0) -> np.ndarray:
+def decode_ragged(q: np.ndarray, k_valid, v_valid, q_scale: float = 1.0,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Same definition, taking each sequence's valid K/V rows directly.
 
     k_valid[b], v_valid[b]: [8, L_b, 128]. Avoids building a dense cache.
     """
     B = q.shape[0]
-    scale = effective_scale(q_scale)
+    scale = effective_scale(q_scale, k_scale)
+    vs = float(np.float32(v_scale))
     out = np.zeros((B, NUM_Q_HEADS, HEAD_DIM))
     for b in range(B):
         for g in range(NUM_KV_HEADS):
             K = np.asarray(k_valid[b][g], dtype=np.float64)
             V = np.asarray(v_valid[b][g], dtype=np.float64)
             for h in range(g * GROUP, (g + 1) * GROUP):
-                out[b, h] = decode_head(q[b, h].astype(np.float64), K, V, scale)
+                out[b, h] = vs * decode_head(q[b, h].astype(np.float64), K, V, scale)
     return out
 
 

@@ -51,7 +51,7 @@ def _gpu_visible():
 def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     assert names == sorted([
-        "gqa_decode", "gqa_decode_chunked", "gqa_decode_workspace_bytes",
+        "gqa_decode", "gqa_decode_chunked", "gqa_decode_typed", "gqa_decode_workspace_bytes",
         "gqa_decode_release_workspace", "gqa_decode_status_string", "gqa_decode_last_error",
         "gqa_decode_profile_begin", "gqa_decode_profile_end"])
 
@@ -111,6 +111,29 @@ def test_argument_errors_are_reported_before_device_work(lib):
     assert _call(lib, chunk=-1) == BAD_ARG
     assert _call(lib, scale=float("nan")) == BAD_ARG
     assert _call(lib, scale=float("inf")) == BAD_ARG
+
+
+def _call_typed(lib, dtype=1, ks=1.0, vs=1.0, **kw):
+    a = dict(q=0x10000, kv=0x20000000, lens=0x30000, out=0x40000, scale=1.0, B=2, C=64, chunk=0)
+    a.update(kw)
+    return lib.gqa_decode_typed(a["q"], a["kv"], a["lens"], a["out"], dtype, a["scale"], ks, vs,
+                                a["B"], a["C"], a["chunk"], None)
+
+
+def test_typed_entry_point_argument_errors(lib):
+    assert _call_typed(lib, q=None) == NULL
+    assert _call_typed(lib, B=0) == BAD_SHAPE
+    assert _call_typed(lib, out=0x40004) == MISALIGNED
+    assert _call_typed(lib, out=0x10000 + 0x2000) == ALIAS
+    assert _call_typed(lib, dtype=7) == BAD_ARG
+    assert "dtype" in lib.gqa_decode_last_error().decode()
+    assert _call_typed(lib, dtype=-1) == BAD_ARG
+    assert _call_typed(lib, ks=float("nan")) == BAD_ARG
+    assert _call_typed(lib, vs=float("inf")) == BAD_ARG
+    assert _call_typed(lib, chunk=-2) == BAD_ARG
+    expected = MISMATCH if _gpu_visible() else NO_DEVICE
+    for dt in (0, 1):
+        assert _call_typed(lib, dtype=dt, ks=0.5, vs=2.0) == expected
 
 
 def test_valid_looking_call_without_device_memory(lib):

@@ -1,0 +1,204 @@
+"""GPU parity of the typed entry point (bfloat16 tensors, K/V scales) against
+the CPU oracle, through the C ABI.
+
+bf16 bar (no tolerance is fixed for it; derived from the arithmetic): the
+kernel accumulates in fp32 and splits each softmax weight p into two bf16
+parts, whose sum is within 2^-17 * p of p. The weighted V sum over the
+normalised weights is therefore off by at most 2^-17 * max|V| in absolute
+terms (under 5e-5 for N(0,1) values, whose largest draws stay below 6), plus
+fp32 rounding far below that. One final rounding to bf16 can then differ
+from the correctly rounded oracle by one unit in the last place when the
+exact value lies that close to a rounding boundary. So every element must
+satisfy |gpu - bf16(oracle)| <= ulp(bf16(oracle)) + 2^-13 (twice the bound
+above), and at most 2% of the elements may differ at all (expected: under
+1%).
+
+fp16 with scales keeps the page bar: max |gpu - fp16(oracle)| <= 2e-3 and
+mean <= 2e-4 (the scales used keep |out| below 4, where one fp16 unit is
+still within 2e-3).
+"""
+import numpy as np
+import pytest
+
+from oracle.formats import bf16_to_f64, round_bf16
+from oracle.reference import decode_ragged, round_fp16
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MAX_TOL, MEAN_TOL = 2e-3, 2e-4
+BF16_MAX_DIFFER = 0.02
+BF16_ABS_SLACK = 2.0 ** -13
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _g():
+    import gqa_token_decode_amd as g
+    return g
+
+
+class _Widened:
+    """k_valid / v_valid of a bf16 workload, widened per (b, g) on access."""
+
+    def __init__(self, arrays):
+        self.arrays = arrays
+
+    def __getitem__(self, b):
+        arr = self.arrays[b]
+
+        class _Seq:
+            def __getitem__(self, g):
+                return bf16_to_f64(arr[g])
+
+        return _Seq()
+
+
+def oracle_of(w, q_scale=None, k_scale=1.0, v_scale=1.0):
+    qs = w.q_scale if q_scale is None else q_scale
+    if w.elem == "bf16":
+        return decode_ragged(bf16_to_f64(w.q), _Widened(w.k_valid), _Widened(w.v_valid), qs,
+                             k_scale=k_scale, v_scale=v_scale)
+    return decode_ragged(w.q, w.k_valid, w.v_valid, qs, k_scale=k_scale, v_scale=v_scale)
+
+
+def run(w, chunk_len=0, q_scale=None, k_scale=1.0, v_scale=1.0, kv=None):
+    torch = _torch()
+    q = w.q_to_device(DEV)
+    lens = torch.from_numpy(w.seq_lens).to(DEV)
+    if kv is None:
+        kv = w.kv_to_device(DEV)
+    out = _g().gqa_decode(q, kv, lens, q_scale=w.q_scale if q_scale is None else q_scale,
+                          chunk_len=chunk_len, k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def bits_of(out):
+    torch = _torch()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _bf16_ulp(vals):
+    a = np.abs(vals)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    return np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+
+
+def check_bf16(out, ref64, label):
+    got = bf16_to_f64(bits_of(out))
+    ref = bf16_to_f64(round_bf16(ref64))
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    d = np.abs(got - ref)
+    excess = d - _bf16_ulp(ref)
+    frac = float(np.mean(d > 0))
+    print(f"{label}: max excess over 1 ulp {excess.max():.3e}, {100 * frac:.3f}% differ, "
+          f"max|gpu-oracle64|={np.abs(got - ref64).max():.3e}", flush=True)
+    assert excess.max() <= BF16_ABS_SLACK, \
+        f"{label}: |d| exceeds 1 ulp by {excess.max():.3e} at {np.unravel_index(excess.argmax(), d.shape)}"
+    assert frac <= BF16_MAX_DIFFER, f"{label}: {100 * frac:.2f}% of elements differ"
+
+
+def check_f16(out, ref64, label):
+    got = out.cpu().numpy().astype(np.float64)
+    ref16 = round_fp16(ref64).astype(np.float64)
+    d = np.abs(got - ref16)
+    print(f"{label}: max|d|={d.max():.3e} mean|d|={d.mean():.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert d.max() <= MAX_TOL and d.mean() <= MEAN_TOL, label
+
+
+# ---------------------------------------------------------------- bf16 workloads
+@pytest.mark.parametrize("name", workloads.SYNTHETIC + workloads.PAGE_SHAPES)
+def test_bf16_parity_workloads(name):
+    print(f"case bf16 {name}", flush=True)
+    w = workloads.get(name, "bf16")
+    check_bf16(run(w), oracle_of(w), f"bf16 {name}")
+
+
+@pytest.mark.parametrize("chunk_len", [0, 7, 143])
+def test_bf16_ragged_lengths_odd_capacity(chunk_len):
+    lens = [0, 1, 2, 3, 15, 16, 17, 63, 64, 65, 255, 256, 257, -5, 1000]
+    w = workloads.build("bf16 ragged", 52, 257, lens, fill="nan", elem="bf16")
+    out = run(w, chunk_len=chunk_len)
+    got = bits_of(out)
+    for b in np.flatnonzero(w.valid_lengths == 0):
+        assert np.all(got[b] == 0)
+    check_bf16(out, oracle_of(w), f"bf16 ragged chunk_len={chunk_len}")
+
+
+@pytest.mark.parametrize("batch,cap,lo,hi", [(100, 512, 0, 300), (1000, 64, 0, 40)])
+def test_bf16_large_batches(batch, cap, lo, hi):
+    w = workloads.build(f"bf16 batch{batch}", 60 + batch, cap,
+                        lambda r: r.integers(lo, hi, batch, endpoint=True), elem="bf16")
+    check_bf16(run(w), oracle_of(w), f"bf16 batch {batch}")
+
+
+def test_bf16_length_one_returns_v_row_bitwise():
+    w = workloads.build("bf16 len1", 53, 96, [1, 1, 1], fill="nan", elem="bf16")
+    got = bits_of(run(w))
+    for b in range(3):
+        for h in range(32):
+            assert np.array_equal(got[b, h], w.v_valid[b][h // 4, 0])
+
+
+def test_bf16_contents_beyond_length_have_no_effect_bitwise():
+    torch = _torch()
+    w = workloads.build("bf16 beyond", 54, 512, [100, 512, 3, 0], elem="bf16")
+    base = bits_of(run(w))
+    kv = w.kv_to_device(DEV)
+    raw = kv.view(torch.int16)
+    for b, L in enumerate(w.valid_lengths):
+        raw[b, :, :, int(L):, :] = torch.randint(-32768, 32767, raw[b, :, :, int(L):, :].shape,
+                                                 dtype=torch.int16, device=DEV)
+    assert np.array_equal(bits_of(run(w, kv=kv)), base)
+
+
+# ---------------------------------------------------------------- scales
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("k_scale,v_scale", [(0.37, 1.0), (1.0, 0.5), (2.5, 1.75), (-1.0, 0.25)])
+def test_scales_match_oracle(elem, k_scale, v_scale):
+    w = workloads.build(f"scales {elem}", 55, 3000, [3000, 1700, 1, 257], sigma_k=2.0, elem=elem)
+    out = run(w, k_scale=k_scale, v_scale=v_scale)
+    ref = oracle_of(w, k_scale=k_scale, v_scale=v_scale)
+    label = f"{elem} k_scale={k_scale} v_scale={v_scale}"
+    if elem == "bf16":
+        check_bf16(out, ref, label)
+    else:
+        check_f16(out, ref, label)
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_power_of_two_scales_are_exact(elem):
+    # v_scale = 2 doubles every output; k_scale = 2 with q_scale = 1/2 is the
+    # same score scale: both bitwise.
+    w = workloads.build(f"pow2 {elem}", 56, 600, [600, 77], elem=elem)
+    base = run(w)
+    doubled = run(w, v_scale=2.0)
+    same = run(w, q_scale=0.5, k_scale=2.0)
+    if elem == "bf16":
+        b0 = bf16_to_f64(bits_of(base))
+        b2 = bf16_to_f64(bits_of(doubled))
+    else:
+        b0 = base.cpu().numpy().astype(np.float64)
+        b2 = doubled.cpu().numpy().astype(np.float64)
+    normal = np.abs(b0) >= 2.0 ** -13
+    assert np.array_equal(b2[normal], 2 * b0[normal])
+    assert np.array_equal(bits_of(same), bits_of(base))
+
+
+def test_binding_rejects_mixed_dtypes():
+    torch = _torch()
+    g = _g()
+    q = torch.zeros(1, 32, 128, dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros(1, 2, 8, 16, 128, dtype=torch.float16, device=DEV)
+    lens = torch.ones(1, dtype=torch.int32, device=DEV)
+    with pytest.raises(TypeError):
+        g.gqa_decode(q, kv, lens)
+    with pytest.raises(TypeError):
+        g.gqa_decode(q, kv.to(torch.bfloat16), lens, out=torch.empty(1, 32, 128, dtype=torch.float16,
+                                                                     device=DEV))

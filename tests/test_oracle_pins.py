@@ -321,3 +321,105 @@ def test_page_shapes_match_golden_fixture():
         w = workloads.get(s["name"])
         assert w.batch == s["batch"] and w.capacity == s["capacity"]
         assert w.seq_lens.tolist() == s["lengths"]
+
+
+# ---------------------------------------------------------------- extension: bf16, K/V scales
+def test_bf16_widening_matches_torch_for_every_pattern():
+    import torch
+
+    from oracle.formats import bf16_to_f64
+
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    got = bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    import torch
+
+    from oracle.formats import round_bf16
+
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormal range
+        (rng.standard_normal(2000) * 1e38).astype(np.float32),      # near overflow
+        np.float32([0.0, -0.0, 1e-45, -1e-45, 3.3895e38]),
+    ])
+    # exact ties: midpoints between neighbouring bfloat16 numbers
+    lo = rng.integers(0x0080, 0x7F00, 5000).astype(np.uint32)
+    ties = ((lo << 16) | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    got = round_bf16(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (got == ref).all()
+
+
+def test_bf16_rounding_is_direct_from_float64():
+    from oracle.formats import bf16_to_f64, round_bf16
+
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7; 2^-40 above it must round
+    # up, while a float32 step would first drop the 2^-40 and then tie to 1.
+    x = np.array([1 + 2.0 ** -8 + 2.0 ** -40, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8 + 2.0 ** -40)])
+    assert bf16_to_f64(round_bf16(x)).tolist() == [1 + 2.0 ** -7, 1.0, 1 + 2 * 2.0 ** -7,
+                                                    -(1 + 2.0 ** -7)]
+    assert np.isinf(bf16_to_f64(round_bf16(np.array([3.5e38, -3.5e38])))).all()
+    assert bf16_to_f64(round_bf16(np.array([2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -134]))).tolist() \
+        == [2.0 ** -133, 0.0, 2.0 ** -132]
+
+
+@pytest.mark.parametrize("C", [1, 3, 6])
+def test_scales_match_brute_force_with_scaled_rows(C):
+    # brute force multiplies every stored K and V element by its scale first;
+    # the oracle folds k_scale into the score scale and v_scale into the output
+    rng = np.random.default_rng(200 + C)
+    lens = list(range(C + 1))
+    q, kv = _rand_inputs(rng, len(lens), C)
+    qf, kvf = q.astype(np.float64).tolist(), kv.astype(np.float64).tolist()
+    for q_scale, k_scale, v_scale in ((1.0, 0.37, 1.0), (0.5, 1.0, -2.5), (1.3, 3.1, 0.011)):
+        got = decode(q, kv, np.array(lens, np.int32), q_scale, k_scale=k_scale, v_scale=v_scale)
+        ref = np.array(brute.decode_brute(qf, kvf, lens, q_scale, k_scale=k_scale,
+                                          v_scale=v_scale))
+        assert np.abs(got - ref).max() <= 1e-12 * max(1.0, float(np.abs(ref).max()))
+
+
+def test_scales_match_torch_sdpa_on_scaled_tensors():
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(12)
+    B, C = 3, 70
+    q, kv = _rand_inputs(rng, B, C)
+    lens = np.array([70, 5, 33], np.int32)
+    ks, vs = 0.8125, 1.75
+    tq = torch.from_numpy(q.astype(np.float64)).unsqueeze(2)
+    tk = torch.from_numpy(kv[:, 0].astype(np.float64)) * float(np.float32(ks))
+    tv = torch.from_numpy(kv[:, 1].astype(np.float64)) * float(np.float32(vs))
+    mask = (torch.arange(C)[None, :] < torch.from_numpy(lens.astype(np.int64))[:, None])[:, None, None, :]
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=effective_scale(0.9),
+                                         enable_gqa=True).squeeze(2).numpy()
+    got = decode(q, kv, lens, 0.9, k_scale=ks, v_scale=vs)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
+def test_bf16_inputs_match_sdpa_on_widened_values():
+    import torch
+    import torch.nn.functional as F
+
+    from oracle.formats import bf16_to_f64
+
+    rng = np.random.default_rng(13)
+    B, C = 2, 40
+    qb = torch.from_numpy(rng.standard_normal((B, H, D)).astype(np.float32)).to(torch.bfloat16)
+    kvb = torch.from_numpy(rng.standard_normal((B, 2, G, C, D)).astype(np.float32)).to(torch.bfloat16)
+    q64 = bf16_to_f64(qb.view(torch.int16).numpy().view(np.uint16))
+    kv64 = bf16_to_f64(kvb.view(torch.int16).numpy().view(np.uint16))
+    lens = np.array([40, 17], np.int32)
+    got = decode(q64, kv64, lens, 1.0)
+    mask = (torch.arange(C)[None, :] < torch.from_numpy(lens.astype(np.int64))[:, None])[:, None, None, :]
+    ref = F.scaled_dot_product_attention(qb.double().unsqueeze(2), kvb[:, 0].double(),
+                                         kvb[:, 1].double(), attn_mask=mask,
+                                         scale=effective_scale(1.0), enable_gqa=True)
+    assert np.abs(got - ref.squeeze(2).numpy()).max() <= 1e-12

@@ -18,8 +18,12 @@ Draw order (fixed, so a seed reproduces the same bytes):
   3. for b in 0..B-1: K_b = standard_normal((8, L_b, 128)) * sigma_k -> fp16,
      then V_b the same way with sigma_v.
 Only the valid prefix [0, L_b) of each sequence is drawn. Slots beyond L_b
-are filled with zeros, or with fp16 quiet NaN (0x7E00) when the workload says
-so; a correct decode never reads them.
+are filled with zeros, or with a quiet NaN when the workload says so; a
+correct decode never reads them.
+
+Element types: "f16" (default), or "bf16" for the library's bfloat16 entry
+point: the same float32 draws rounded to bfloat16 (nearest even) instead of
+fp16, kept as uint16 bit patterns on the host (numpy has no bfloat16).
 """
 from __future__ import annotations
 
@@ -33,6 +37,7 @@ NUM_KV_HEADS = 8
 HEAD_DIM = 128
 
 FP16_QNAN_BITS = 0x7E00
+BF16_QNAN_BITS = 0x7FC0
 
 
 @dataclasses.dataclass
@@ -46,13 +51,14 @@ class Workload:
     """
 
     name: str
-    q: np.ndarray                 # fp16 [B, 32, 128]
+    q: np.ndarray                 # fp16 [B, 32, 128] (uint16 bit patterns for bf16)
     seq_lens: np.ndarray          # int32 [B]
     capacity: int
     q_scale: float
     k_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
     v_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
     fill: str = "zero"            # "zero" or "nan": contents beyond L_b
+    elem: str = "f16"             # "f16" or "bf16"
 
     @property
     def batch(self) -> int:
@@ -68,13 +74,37 @@ class Workload:
         """K+V bytes of the valid prefixes: sum(L_b) * 2 * 8 * 128 * 2 B."""
         return int(self.valid_lengths.sum()) * 2 * NUM_KV_HEADS * HEAD_DIM * 2
 
+    @property
+    def elem_bytes(self) -> int:
+        return 2
+
     def fill_value_bits(self) -> int:
-        return FP16_QNAN_BITS if self.fill == "nan" else 0
+        if self.fill != "nan":
+            return 0
+        return BF16_QNAN_BITS if self.elem == "bf16" else FP16_QNAN_BITS
+
+    def _host_dtype(self):
+        return np.uint16 if self.elem == "bf16" else np.float16
+
+    def _torch_dtype(self):
+        import torch
+
+        return torch.bfloat16 if self.elem == "bf16" else torch.float16
+
+    def q_to_device(self, device):
+        """q as a device tensor of the workload's element type."""
+        import torch
+
+        t = torch.from_numpy(self.q)
+        if self.elem == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(device)
 
     def dense_kv(self) -> np.ndarray:
-        """Host fp16 ``[B, 2, 8, C, 128]`` cache with the fill beyond L_b."""
+        """Host ``[B, 2, 8, C, 128]`` cache (fp16, or bf16 bit patterns)
+        with the fill beyond L_b."""
         B, C = self.batch, self.capacity
-        kv = np.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=np.float16)
+        kv = np.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=self._host_dtype())
         kv.view(np.uint16)[...] = self.fill_value_bits()
         for b in range(B):
             L = self.k_valid[b].shape[1]
@@ -87,20 +117,26 @@ class Workload:
         import torch
 
         B, C = self.batch, self.capacity
-        kv = torch.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=torch.float16, device=device)
-        kv.view(torch.int16).fill_(np.int16(np.uint16(self.fill_value_bits())).item())
+        kv = torch.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=self._torch_dtype(),
+                         device=device)
+        raw = kv.view(torch.int16)
+        raw.fill_(np.int16(np.uint16(self.fill_value_bits())).item())
         for b in range(B):
             L = self.k_valid[b].shape[1]
             if L:
-                kv[b, 0, :, :L, :].copy_(torch.from_numpy(self.k_valid[b]))
-                kv[b, 1, :, :L, :].copy_(torch.from_numpy(self.v_valid[b]))
+                raw[b, 0, :, :L, :].copy_(torch.from_numpy(self.k_valid[b].view(np.int16)))
+                raw[b, 1, :, :L, :].copy_(torch.from_numpy(self.v_valid[b].view(np.int16)))
         return kv
 
 
-def _normal_fp16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+def _normal(rng: np.random.Generator, shape, sigma: float, elem: str) -> np.ndarray:
     x = rng.standard_normal(shape, dtype=np.float32)
     if sigma != 1.0:
         x = x * np.float32(sigma)
+    if elem == "bf16":
+        import torch
+
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     return x.astype(np.float16)
 
 
@@ -115,6 +151,7 @@ def build(
     sigma_k: float = 1.0,
     sigma_v: float = 1.0,
     fill: str = "zero",
+    elem: str = "f16",
 ) -> Workload:
     """Draw a workload. ``lengths`` is a list or a callable taking the rng.
 
@@ -127,14 +164,15 @@ def build(
     else:
         lens = np.asarray(lengths, dtype=np.int64)
     B = int(lens.shape[0])
-    q = _normal_fp16(rng, (B, NUM_Q_HEADS, HEAD_DIM), sigma_q)
+    assert elem in ("f16", "bf16"), elem
+    q = _normal(rng, (B, NUM_Q_HEADS, HEAD_DIM), sigma_q, elem)
     k_valid, v_valid = [], []
     for b in range(B):
         L = int(min(max(lens[b], 0), capacity))
-        k_valid.append(_normal_fp16(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_k))
-        v_valid.append(_normal_fp16(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_v))
+        k_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_k, elem))
+        v_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_v, elem))
     return Workload(name, q, lens.astype(np.int32), int(capacity), float(q_scale),
-                    k_valid, v_valid, fill)
+                    k_valid, v_valid, fill, elem)
 
 
 def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
@@ -144,48 +182,49 @@ def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
     return rng.permutation(np.concatenate([short, long_]))
 
 
-# Name -> (description, factory). The five synthetic decode workloads, then
-# the four benchmark shapes printed in the PR #5052 page's timing tables
-# (batch/capacity/valid lengths exactly as printed there).
+# Name -> (description, factory of the element type). The five synthetic
+# decode workloads, then the four benchmark shapes printed in the PR #5052
+# page's timing tables (batch/capacity/valid lengths exactly as printed there).
 WORKLOADS: Dict[str, tuple] = {
     "b1_c256_len200": (
         "batch 1, capacity 256, length 200, N(0,1), q_scale 1.0",
-        lambda: build("b1_c256_len200", 1, 256, [200]),
+        lambda e: build("b1_c256_len200", 1, 256, [200], elem=e),
     ),
     "b8_c4096_nanfill": (
         "batch 8, capacity 4096, lengths U[1,4096], N(0,1), NaN beyond each length, q_scale 1.0",
-        lambda: build("b8_c4096_nanfill", 2, 4096,
-                      lambda r: r.integers(1, 4096, 8, endpoint=True), fill="nan"),
+        lambda e: build("b8_c4096_nanfill", 2, 4096,
+                        lambda r: r.integers(1, 4096, 8, endpoint=True), fill="nan", elem=e),
     ),
     "b32_c8192_qs05": (
         "batch 32, capacity 8192, lengths U[1024,8192], N(0,1), q_scale 0.5",
-        lambda: build("b32_c8192_qs05", 3, 8192,
-                      lambda r: r.integers(1024, 8192, 32, endpoint=True), q_scale=0.5),
+        lambda e: build("b32_c8192_qs05", 3, 8192,
+                        lambda r: r.integers(1024, 8192, 32, endpoint=True), q_scale=0.5,
+                        elem=e),
     ),
     "b64_c16384_skewed": (
         "batch 64, capacity 16384, 58 lengths U[16,512] + 6 lengths U[8192,16384] shuffled, "
         "q,V ~ N(0,1), K ~ N(0, std 2), q_scale 1.0",
-        lambda: build("b64_c16384_skewed", 4, 16384, _cfg4_lengths, sigma_k=2.0),
+        lambda e: build("b64_c16384_skewed", 4, 16384, _cfg4_lengths, sigma_k=2.0, elem=e),
     ),
     "b2_c131072_long": (
         "batch 2, capacity 131072, lengths [131072, 65537], N(0,1), q_scale 1.0",
-        lambda: build("b2_c131072_long", 5, 131072, [131072, 65537]),
+        lambda e: build("b2_c131072_long", 5, 131072, [131072, 65537], elem=e),
     ),
     "page_b1_c64": (
         "page shape: batch 1, capacity 64, lengths [1]",
-        lambda: build("page_b1_c64", 11, 64, [1]),
+        lambda e: build("page_b1_c64", 11, 64, [1], elem=e),
     ),
     "page_b4_c256": (
         "page shape: batch 4, capacity 256, lengths [64, 127, 191, 256]",
-        lambda: build("page_b4_c256", 12, 256, [64, 127, 191, 256]),
+        lambda e: build("page_b4_c256", 12, 256, [64, 127, 191, 256], elem=e),
     ),
     "page_b1_c1024": (
         "page shape: batch 1, capacity 1024, lengths [1024]",
-        lambda: build("page_b1_c1024", 13, 1024, [1024]),
+        lambda e: build("page_b1_c1024", 13, 1024, [1024], elem=e),
     ),
     "page_b1_c4096": (
         "page shape: batch 1, capacity 4096, lengths [3968]",
-        lambda: build("page_b1_c4096", 14, 4096, [3968]),
+        lambda e: build("page_b1_c4096", 14, 4096, [3968], elem=e),
     ),
 }
 
@@ -195,8 +234,9 @@ SYNTHETIC = ["b1_c256_len200", "b8_c4096_nanfill", "b32_c8192_qs05",
 PAGE_SHAPES = ["page_b1_c64", "page_b4_c256", "page_b1_c1024", "page_b1_c4096"]
 
 
-def get(name: str) -> Workload:
-    return WORKLOADS[name][1]()
+def get(name: str, elem: str = "f16") -> Workload:
+    """Named workload; elem="bf16" draws it (same seed and recipe) in bfloat16."""
+    return WORKLOADS[name][1](elem)
 
 
 def describe(name: str) -> str:
