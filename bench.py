@@ -80,13 +80,18 @@ def traffic_from_profiles(workload: str):
 def cpu_baseline(w, min_seconds: float):
     import numpy as np
 
-    from oracle.formats import bf16_to_f64
+    from oracle.formats import bf16_to_f64, e4m3_to_f64
     from oracle.reference import decode_ragged
 
-    if w.elem == "bf16":     # the oracle takes the element values widened exactly
+    # the oracle takes the element values widened exactly
+    if w.elem == "bf16":
         q = bf16_to_f64(w.q)
         kval = [bf16_to_f64(k) for k in w.k_valid]
         vval = [bf16_to_f64(v) for v in w.v_valid]
+    elif w.elem == "e4m3":
+        q = w.q
+        kval = [e4m3_to_f64(k) for k in w.k_valid]
+        vval = [e4m3_to_f64(v) for v in w.v_valid]
     else:
         q, kval, vval = w.q, w.k_valid, w.v_valid
     try:
@@ -96,7 +101,7 @@ def cpu_baseline(w, min_seconds: float):
         threads = len(os.sched_getaffinity(0))
     reps, t0 = 0, time.perf_counter()
     while True:
-        decode_ragged(q, kval, vval, w.q_scale)
+        decode_ragged(q, kval, vval, w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -170,8 +175,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--elem", default="f16", choices=["f16", "bf16"],
-                    help="element type of q, kv and out (bf16 uses the typed entry point)")
+    ap.add_argument("--elem", default="f16", choices=["f16", "bf16", "e4m3"],
+                    help="element type: f16 (default), bf16 (q, kv, out), or e4m3 (fp16 q and "
+                         "out, FP8 E4M3 kv with per-tensor scales); non-f16 types use the typed "
+                         "entry point")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -206,13 +213,14 @@ def main(argv=None):
     lens = torch.from_numpy(w.seq_lens).to(dev)
     kv0 = w.kv_to_device(dev)
     rot = max(1, math.ceil(ROTATE_TARGET_BYTES / max(kv_bytes, 1)))
-    rot = min(rot, ROTATE_MAX_COPIES, max(1, int(40e9 // (kv0.numel() * 2))))
+    rot = min(rot, ROTATE_MAX_COPIES, max(1, int(40e9 // (kv0.numel() * kv0.element_size()))))
     kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
     out = torch.empty_like(q)
     torch.cuda.synchronize()
 
     def step(i):
-        g.gqa_decode(q, kvs[i % rot], lens, out=out, q_scale=w.q_scale)
+        g.gqa_decode(q, kvs[i % rot], lens, out=out, q_scale=w.q_scale, k_scale=w.k_scale,
+                     v_scale=w.v_scale)
 
     for i in range(args.warmup):
         step(i)

@@ -104,6 +104,8 @@ def _check_device(name, t):
 
 
 _DTYPES = {torch.float16: 0, torch.bfloat16: 1}   # gqa_dtype codes
+_E4M3_KV = 2
+_FP8_KV_DTYPES = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
 
 
 def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor, *,
@@ -112,7 +114,9 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
     """Decode one token of GQA (32 query heads, 8 KV heads, dim 128).
 
     q: fp16 or bf16 [batch, 32, 128]; kv: same dtype [batch, 2, 8, capacity,
-    128] with K at index 0 and V at index 1 of axis 1; sequence_lengths:
+    128] with K at index 0 and V at index 1 of axis 1, or, with fp16 q, an
+    OCP FP8 E4M3 cache (torch.float8_e4m3fn, or uint8 holding E4M3 bytes)
+    dequantised by k_scale and v_scale; sequence_lengths:
     int32 [batch] on the same device (values clamped to [0, capacity]).
     ``out`` (optional, caller-owned, q's dtype and shape) receives the result
     and is returned; otherwise a new tensor is allocated. Scores are scaled by
@@ -124,8 +128,10 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
         dtype = q.dtype
     else:
         dtype = torch.float16
+    fp8_kv = (dtype == torch.float16 and isinstance(kv, torch.Tensor)
+              and kv.dtype in _FP8_KV_DTYPES)
     _check_tensor("q", q, dtype, 3)
-    _check_tensor("kv", kv, dtype, 5)
+    _check_tensor("kv", kv, kv.dtype if fp8_kv else dtype, 5)
     _check_tensor("sequence_lengths", sequence_lengths, torch.int32, 1)
     B = q.shape[0]
     kshape = kv.shape
@@ -154,9 +160,10 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
     lib = _lib if _lib is not None else load_library()
     index = dev.index if dev.index is not None else torch.cuda.current_device()
     stream = torch._C._cuda_getCurrentRawStream(index)
-    if dtype != torch.float16 or k_scale != 1.0 or v_scale != 1.0:
+    if fp8_kv or dtype != torch.float16 or k_scale != 1.0 or v_scale != 1.0:
+        code = _E4M3_KV if fp8_kv else _DTYPES[dtype]
         st = lib.gqa_decode_typed(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
-                                  out.data_ptr(), _DTYPES[dtype], float(q_scale), float(k_scale),
+                                  out.data_ptr(), code, float(q_scale), float(k_scale),
                                   float(v_scale), B, kshape[3], chunk_len, stream)
     elif chunk_len:
         st = lib.gqa_decode_chunked(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),

@@ -172,7 +172,7 @@ void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
 }
 
 int check_args(const void* q, const void* kv, const int32_t* seq_lens, const void* out, int batch,
-               int capacity, int chunk_len) {
+               int capacity, int chunk_len, size_t kv_elem_bytes) {
   if (!q || !kv || !seq_lens || !out)
     return fail(GQA_ERR_NULL, "gqa_decode: q, kv, seq_lens and out must be non-NULL");
   if (batch <= 0 || capacity <= 0)
@@ -190,7 +190,7 @@ int check_args(const void* q, const void* kv, const int32_t* seq_lens, const voi
   if ((uintptr_t)seq_lens & 3u)
     return fail(GQA_ERR_MISALIGNED, "gqa_decode: seq_lens must be 4-byte aligned");
   const size_t qb = (size_t)batch * kQBytesPerSeq;
-  const size_t kvb = (size_t)batch * (size_t)capacity * kKvBytesPerPos;
+  const size_t kvb = (size_t)batch * (size_t)capacity * (kKvBytesPerPos / 2) * kv_elem_bytes;
   if (overlaps(out, qb, q, qb) || overlaps(out, qb, kv, kvb) ||
       overlaps(out, qb, seq_lens, (size_t)batch * 4))
     return fail(GQA_ERR_ALIAS, "gqa_decode: out must not overlap q, kv or seq_lens");
@@ -200,10 +200,11 @@ int check_args(const void* q, const void* kv, const int32_t* seq_lens, const voi
 int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
                 float q_scale, float k_scale, float v_scale, int batch, int capacity,
                 int chunk_len, hipStream_t stream) {
-  int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len);
-  if (st != GQA_OK) return st;
-  if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16)
+  if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16 && dtype != GQA_DTYPE_E4M3_KV)
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: unknown dtype %d", dtype);
+  int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len,
+                      dtype == GQA_DTYPE_E4M3_KV ? 1 : 2);
+  if (st != GQA_OK) return st;
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_scale, k_scale and v_scale must be finite");
 
@@ -261,8 +262,9 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
             }
             if (g_profile_used < g_profile.size()) ev = g_profile[g_profile_used++].ev;
           }
-          const gqa::ElemType elem =
-              dtype == GQA_DTYPE_BF16 ? gqa::ElemType::kBf16 : gqa::ElemType::kF16;
+          const gqa::ElemType elem = dtype == GQA_DTYPE_BF16      ? gqa::ElemType::kBf16
+                                     : dtype == GQA_DTYPE_E4M3_KV ? gqa::ElemType::kE4m3Kv
+                                                                  : gqa::ElemType::kF16;
           const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, elem, (float)scale,
                                                   v_scale, batch, capacity, cfg, grid, ws, stream,
                                                   ev);

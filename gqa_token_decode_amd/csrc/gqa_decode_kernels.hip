@@ -82,6 +82,13 @@ constexpr int kTileHalves = kTileRows * kDim;     // one K or V tile in LDS (4 K
 constexpr int kStageHalves = 2 * kTileHalves;     // one pipeline stage: K then V
 constexpr int kQHalves = kGroup * kDim;           // the group's 4 query rows (1 KiB)
 constexpr int kLoadsPerTile = 9;             // per lane: q, 4 x K, 4 x V
+
+// Element formats: q, K, V and out in fp16 or bf16 (16-row tiles of 256-byte
+// rows), or fp16 q and out with OCP FP8 E4M3 K and V (32-row tiles of
+// 128-byte rows; one stage holds the same 8 KiB).
+constexpr int kFmtF16 = 0, kFmtBf16 = 1, kFmtE4m3 = 2;
+template <int F> constexpr int tile_rows() { return F == kFmtE4m3 ? 32 : 16; }
+template <int F> constexpr int row_bytes() { return F == kFmtE4m3 ? kDim : 2 * kDim; }
 constexpr unsigned kBufferFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
 constexpr int kSlotFloats = kGroup * (2 + kDim);   // one partial: 4 x (max, den) + 4 x 128 sums
@@ -303,64 +310,81 @@ __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_en
 // Move (s, t) to this wave's next tile in the piece: the next 16-row tile of
 // the wave in s, else its first tile in a later segment. Returns false when
 // the piece has no more tiles for this wave.
+template <int kRows>
 __device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long long p_end, int wv,
                                           int lens_v) {
-  t += kStepRows;
+  t += kWaves * kRows;
   while (t >= s.hi) {
     if (!more_segments(P, s, p_end)) return false;
     seg_next(P, s, p_end, lens_v);
-    t = s.lo + kTileRows * wv;
+    t = s.lo + kRows * wv;
   }
   return true;
 }
 
-// First tile of this wave at or after (s, t) (t = s.lo + 16 * wv).
+// First tile of this wave at or after (s, t) (t = s.lo + kRows * wv).
+template <int kRows>
 __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long long p_end, int wv,
                                            int lens_v) {
   while (t >= s.hi) {
     if (!more_segments(P, s, p_end)) return false;
     seg_next(P, s, p_end, lens_v);
-    t = s.lo + kTileRows * wv;
+    t = s.lo + kRows * wv;
   }
   return true;
 }
 
-// Issue the loads of tile rows [t, t + 16) of segment s into an LDS stage
-// (K, then V) and the segment's 4 query rows into the wave's q slot, in this
-// order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros. With live ==
-// false the buffers are empty: the same 9 loads return zeros without
-// touching memory, so every pipeline step has the same shape. The q load is
-// live only for a wave's first tile of a segment (live_q); later tiles reuse
-// the q registers, and their empty q load leaves zeros in the slot.
+// 16-byte chunk c of row r of an E4M3 tile sits at chunk c ^ swz8(r) of the
+// row in LDS, so the K reads (16 rows apart by 128 B) and the transposed V
+// reads (rows r and r + 16 together) spread over the banks.
+__device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (((r >> 4) & 1) << 2); }
+
+// Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
+// an LDS stage (K, then V) and the segment's 4 query rows into the wave's q
+// slot, in this order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros.
+// With live == false the buffers are empty: the same 9 loads return zeros
+// without touching memory, so every pipeline step has the same shape. The q
+// load is live only for a wave's first tile of a segment (live_q); later
+// tiles reuse the q registers, and their empty q load leaves zeros in the
+// slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
+// rows of 128 B (E4M3).
+template <int F>
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
                                            bool live_q, e16_t* stage, e16_t* qslot) {
+  constexpr int kRowBytes = row_bytes<F>();
   const int lane = threadIdx.x & 63;
-  const size_t seg_elems = (size_t)P.capacity * kDim;
-  const e16_t* kb = P.kv + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_elems;
-  const e16_t* vb = P.kv + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_elems;
+  const char* kvb = reinterpret_cast<const char*>(P.kv);
+  const size_t seg_bytes = (size_t)P.capacity * kRowBytes;
+  const char* kb = kvb + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_bytes;
+  const char* vb = kvb + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_bytes;
   const e16_t* qg = P.q + ((size_t)s.b * kQHeads + s.g * kGroup) * kDim;
-  const int nbytes = live ? s.hi * (kDim * 2) : 0;
+  const int nbytes = live ? s.hi * kRowBytes : 0;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, live && live_q ? kQHalves * 2 : 0, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nbytes, kBufferFlags);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)qslot, 16, 16 * lane, 0, 0, 0);
-  // DMA lane l writes 16 B at LDS offset 16*l: row 4u + l/16, physical chunk
-  // l%16, which holds logical chunk vchunk(row, l%16) (the swizzle is its own
-  // inverse).
-  const int rsub = lane >> 4;
+  // DMA lane l writes 16 B at LDS offset 16*l of the 1 KiB block u: for
+  // 16-bit formats row 4u + l/16, physical chunk l%16, which holds logical
+  // chunk vchunk(row, l%16); for E4M3 row 8u + l/8, physical chunk l%8,
+  // holding logical chunk (l%8) ^ swz8(row). Both swizzles are their own
+  // inverse.
+  char* st = reinterpret_cast<char*>(stage);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 4 * u + rsub;
-    const int off = (t + r) * (kDim * 2) + 16 * vchunk(r, lane & 15);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(stage + u * 512), 16, off, 0, 0,
-                                             kNonTemporal);
-  }
+  for (int kind = 0; kind < 2; ++kind) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 4 * u + rsub;
-    const int off = (t + r) * (kDim * 2) + 16 * vchunk(r, lane & 15);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(stage + kTileHalves + u * 512), 16,
-                                             off, 0, 0, kNonTemporal);
+    for (int u = 0; u < 4; ++u) {
+      int off;
+      if constexpr (F == kFmtE4m3) {
+        const int r = 8 * u + (lane >> 3);
+        off = (t + r) * kRowBytes + 16 * ((lane & 7) ^ swz8(r));
+      } else {
+        const int r = 4 * u + (lane >> 4);
+        off = (t + r) * kRowBytes + 16 * vchunk(r, lane & 15);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kind ? rv : rk,
+                                               (lds_void_t*)(st + kind * 4096 + u * 1024), 16,
+                                               off, 0, 0, kNonTemporal);
+    }
   }
 }
 
@@ -400,25 +424,52 @@ __device__ __forceinline__ void read_q(const e16_t* qslot, uint4_t (&qb)[4]) {
 
 // LDS addresses of this lane's operand reads in stage 0 of its wave; stage 1
 // lies kStageHalves halves higher (an immediate offset of the reads).
+//   16-bit formats: k[kk] = row j, logical chunk 4kk + G (16 B); v[db] =
+//   transposed read of row 4G + j/4, columns 16db + 4(j%4) .. +3.
+//   E4M3: k[4h + kk] = row 16h + j, bytes 32kk + 8G .. +7; v[db] =
+//   transposed read of row rowE(G, j/2), bytes 16db + 8(j%2) .. +7, where
+//   rowE(G, e) = 4G + e for e < 4 and 16 + 4G + e - 4 for e >= 4.
 struct LdsReads {
-  unsigned k[4];     // K: lane (G, j) reads row j, logical chunk 4kk + G
-  unsigned v[8];     // V, transposed: row 4G + j/4, columns 16db + 4(j%4) .. +3
+  unsigned k[8];
+  unsigned v[8];
 };
 
+template <int F>
 __device__ __forceinline__ LdsReads lds_reads(const e16_t* stage0) {
   const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
-  const int rr = 4 * G + (j >> 2);
   const unsigned kbase = lds_addr(stage0);
-  const unsigned vbase = kbase + 2 * kTileHalves;
+  const unsigned vbase = kbase + 4096;
   LdsReads r;
+  if constexpr (F == kFmtE4m3) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) r.k[kk] = kbase + 2 * (j * kDim + 8 * vchunk(j, 4 * kk + G));
-  // Transposed reads: lane (G, j) supplies the address of row 4G + j/4,
-  // columns 16*db + 4*(j%4) .. +3 and receives column 16*db + j of rows
-  // 4G .. 4G+3.
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
-    r.v[db] = vbase + 2 * (rr * kDim + 8 * vchunk(rr, 2 * db + ((j & 3) >> 1)) + 4 * (j & 1));
+      for (int kk = 0; kk < 4; ++kk) {
+        const int row = 16 * h + j;
+        r.k[4 * h + kk] = kbase + row * kDim + 16 * ((2 * kk + (G >> 1)) ^ swz8(row)) + 8 * (G & 1);
+      }
+    }
+    // Transposed 8-bit reads (lane mapping measured on the hardware): within
+    // each 16-lane group, output lane i receives byte i % 8 of the 8-byte
+    // chunks addressed by lanes i/8 + 2e, e = 0..7. Lane (G, j) addresses
+    // row rowE(G, j/2), columns 16db + 8(j%2) .. +7, so it receives column
+    // 16db + j of rows rowE(G, 0..7): the B operand of a K = 32 MFMA.
+    const int e = j >> 1;
+    const int row = e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      r.v[db] = vbase + row * kDim + 16 * (db ^ swz8(row)) + 8 * (j & 1);
+  } else {
+    const int rr = 4 * G + (j >> 2);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) r.k[kk] = kbase + 2 * (j * kDim + 8 * vchunk(j, 4 * kk + G));
+    // Transposed reads: lane (G, j) supplies the address of row 4G + j/4,
+    // columns 16*db + 4*(j%4) .. +3 and receives column 16*db + j of rows
+    // 4G .. 4G+3.
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      r.v[db] = vbase + 2 * (rr * kDim + 8 * vchunk(rr, 2 * db + ((j & 3) >> 1)) + 4 * (j & 1));
+  }
   return r;
 }
 
@@ -444,6 +495,47 @@ __device__ __forceinline__ void read_stage(const LdsReads& a, uint4_t (&k)[4], s
       : "v"(a.k[0]), "v"(a.k[1]), "v"(a.k[2]), "v"(a.k[3]), "v"(a.v[0]), "v"(a.v[1]),
         "v"(a.v[2]), "v"(a.v[3]), "v"(a.v[4]), "v"(a.v[5]), "v"(a.v[6]), "v"(a.v[7]), "n"(OFF)
       : "memory");
+}
+
+// Read the E4M3 K and V operands of one stage (byte offset OFF from stage 0).
+template <int OFF>
+__device__ __forceinline__ void read_stage8(const LdsReads& a, uint2 (&k)[8], uint2 (&v)[8]) {
+  asm volatile(
+      "ds_read_b64 %0, %16 offset:%32\n\t"
+      "ds_read_b64 %1, %17 offset:%32\n\t"
+      "ds_read_b64 %2, %18 offset:%32\n\t"
+      "ds_read_b64 %3, %19 offset:%32\n\t"
+      "ds_read_b64 %4, %20 offset:%32\n\t"
+      "ds_read_b64 %5, %21 offset:%32\n\t"
+      "ds_read_b64 %6, %22 offset:%32\n\t"
+      "ds_read_b64 %7, %23 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %8, %24 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %9, %25 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %10, %26 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %11, %27 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %12, %28 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %13, %29 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %14, %30 offset:%32\n\t"
+      "ds_read_b64_tr_b8 %15, %31 offset:%32\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+        "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+        "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a.k[0]), "v"(a.k[1]), "v"(a.k[2]), "v"(a.k[3]), "v"(a.k[4]), "v"(a.k[5]),
+        "v"(a.k[6]), "v"(a.k[7]), "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]),
+        "v"(a.v[4]), "v"(a.v[5]), "v"(a.v[6]), "v"(a.v[7]), "n"(OFF)
+      : "memory");
+}
+
+// Eight E4M3 bytes (two dwords, byte 0 first) as eight fp16 values. Every
+// E4M3 value is an fp16 value, so the conversion is exact; its results were
+// checked on the hardware against the format's definition for all 256 codes.
+__device__ __forceinline__ half8_t e4m3x8_to_f16(uint2 x) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, false);
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.x, 1.0f, true);
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, false);
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x.y, 1.0f, true);
+  return (half8_t){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // Element-type specific steps: MFMAs on fp16 or bf16 operands (raw 16-bit
@@ -491,7 +583,79 @@ __device__ __forceinline__ e16_t to_elem(float x) {
     return __builtin_bit_cast(e16_t, (_Float16)x);
 }
 
-// Fold tile rows [t, t + 16) held in LDS stage `par` into acc.
+// Fold tile rows [t, t + 32) of an E4M3 tile held in LDS stage `par` into
+// acc. QK runs as two 16-row halves on the fp16 MFMA (K converted exactly);
+// lane (G, j) then holds the scores of rows 4G .. 4G+3 and 16 + 4G .. +3
+// for head j: in the order rowE(G, 0..7), which is the A layout of a K = 32
+// PV MFMA, matching the V operand read above.
+__device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const uint4_t (&qb)[4],
+                                              int t, int hi, float scale_log2, WaveAcc& acc) {
+  const int lane = threadIdx.x & 63, G = lane >> 4;
+  const float kNegInf = -__builtin_inff();
+  uint2 kr[8], vr[8];
+  if (par)
+    read_stage8<kStageHalves * 2>(la, kr, vr);
+  else
+    read_stage8<0>(la, kr, vr);
+
+  float4_t sc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    sc[h] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(kr[4 * h + kk]),
+                                                     __builtin_bit_cast(half8_t, qb[kk]), sc[h],
+                                                     0, 0, 0);
+  }
+
+  float sv[8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = (e < 4 ? 0 : 16) + 4 * G + (e & 3);
+    const float x = (t + row) < hi ? sc[e >> 2][e & 3] * scale_log2 : kNegInf;
+    sv[e] = x;
+    mx = fmaxf(mx, x);
+  }
+  mx = max_over_row_groups(mx);
+  // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
+  // tile, where acc.m is still -inf.
+  const float m_new = fmaxf(acc.m, mx);
+  const float alpha = exp2_hw(acc.m - m_new);
+  acc.m = m_new;
+
+  half8_t ph, pl;
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = (sv[e] == kNegInf) ? 0.f : exp2_hw(sv[e] - m_new);
+    psum += p;
+    short hs, ls;
+    split_weight<false>(p, hs, ls);
+    ph[e] = __builtin_bit_cast(_Float16, hs);
+    pl[e] = __builtin_bit_cast(_Float16, ls);
+  }
+  acc.l = acc.l * alpha + psum;
+
+  const float a0 = lane_value(alpha, 0), a1 = lane_value(alpha, 1), a2 = lane_value(alpha, 2),
+              a3 = lane_value(alpha, 3);
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    acc.O[db][0] *= a0;
+    acc.O[db][1] *= a1;
+    acc.O[db][2] *= a2;
+    acc.O[db][3] *= a3;
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const half8_t vb = e4m3x8_to_f16(vr[db]);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vb, acc.O[db], 0, 0, 0);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, acc.O[db], 0, 0, 0);
+  }
+}
+
+// Fold tile rows [t, t + 16) held in LDS stage `par` into acc (fp16 or bf16).
 template <bool kBf16>
 __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const uint4_t (&qb)[4],
                                              int t, int hi, float scale_log2, WaveAcc& acc) {
@@ -565,7 +729,7 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
 // group) into `nxt` and the q slot; wait for the current tile; fold it in.
 // Loads complete in issue order, so "all but the newest N" waits are exact
 // (vector stores issued in between only make them wait longer).
-template <bool kBf16>
+template <int F>
 __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, int par,
                                           e16_t* nxt, e16_t* qslot, bool first,
                                           bool has_next, const Seg& nseg, int nt,
@@ -575,9 +739,12 @@ __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, i
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
     read_q(qslot, qb);
   }
-  issue_tile(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
+  issue_tile<F>(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
-  compute_tile<kBf16>(la, par, qb, t, hi, P.scale_log2, acc);
+  if constexpr (F == kFmtE4m3)
+    compute_tile8(la, par, qb, t, hi, P.scale_log2, acc);
+  else
+    compute_tile<F == kFmtBf16>(la, par, qb, t, hi, P.scale_log2, acc);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -665,9 +832,11 @@ __device__ __forceinline__ void zero_empty_sequences(const Params& P, int lens_v
 }
 
 // ---------------------------------------------------------------- kernel 1
-template <bool kBf16>
+template <int F>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(Params P) {
+  constexpr bool kBf16 = F == kFmtBf16;
+  constexpr int kRows = tile_rows<F>();
   __shared__ long long red[kWaves];
   __shared__ long long sh_found;
   __shared__ int sh_found_b, sh_found_len;
@@ -728,11 +897,11 @@ void gqa_decode_pieces(Params P) {
   e16_t* st0 = stages[wv][0];
   e16_t* st1 = stages[wv][1];
   e16_t* qslot = qslots[wv];
-  const LdsReads la = lds_reads(st0);
+  const LdsReads la = lds_reads<F>(st0);
   Seg pf = s;
-  int pt = s.lo + kTileRows * wv;
-  const bool pf_ok = tile_first(P, pf, pt, p1, wv, lens_v);
-  issue_tile(P, pf, pt, pf_ok, true, st0, qslot);
+  int pt = s.lo + kRows * wv;
+  const bool pf_ok = tile_first<kRows>(P, pf, pt, p1, wv, lens_v);
+  issue_tile<F>(P, pf, pt, pf_ok, true, st0, qslot);
   zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
 
@@ -744,11 +913,11 @@ void gqa_decode_pieces(Params P) {
     acc.l = 0.f;
     // This wave's tiles of s; the prefetch cursor (pf, pt) is on the first.
     uint4_t qb[4];
-    for (int t = s.lo + kTileRows * wv; t < s.hi; t += kStepRows) {
+    for (int t = s.lo + kRows * wv; t < s.hi; t += kWaves * kRows) {
       Seg nf = pf;
       int nt = pt;
-      const bool n_ok = tile_next(P, nf, nt, p1, wv, lens_v);
-      tile_step<kBf16>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kTileRows * wv, n_ok, nf, nt,
+      const bool n_ok = tile_next<kRows>(P, nf, nt, p1, wv, lens_v);
+      tile_step<F>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
                 nf.off != s.off, t, s.hi, qb, acc);
       pf = nf;
       pt = nt;
@@ -788,8 +957,9 @@ constexpr int kCombineSubsets = kThreads / 32;   // 8 subsets x 32 four-column g
 // row; otherwise exit. Each of 8 thread subsets merges every 8th partial
 // with a running max (its loads do not depend on each other), then the
 // subsets are merged through LDS.
-template <bool kBf16>
+template <int F>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
+  constexpr bool kBf16 = F == kFmtBf16;
   __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][32][6];
 
   const int tid = threadIdx.x;
@@ -852,15 +1022,19 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
 }  // namespace
 
 int resident_workgroups_per_cu() {
-  int n16 = 0, nb16 = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n16, gqa_decode_pieces<false>, kThreads, 0) !=
+  int n[3] = {0, 0, 0};
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], gqa_decode_pieces<kFmtF16>, kThreads, 0) !=
           hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb16, gqa_decode_pieces<true>, kThreads, 0) !=
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], gqa_decode_pieces<kFmtBf16>, kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], gqa_decode_pieces<kFmtE4m3>, kThreads, 0) !=
           hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  return n16 < nb16 ? n16 : nb16;
+  int m = n[0];
+  for (int i = 1; i < 3; ++i) m = n[i] < m ? n[i] : m;
+  return m;
 }
 
 long long grid_for(int batch, int capacity, const SplitConfig& cfg) {
@@ -879,7 +1053,7 @@ size_t segment_bytes_for_batch(int batch) {
   return ((size_t)batch * kKvHeads * sizeof(int2) + 255) & ~(size_t)255;
 }
 
-template <bool kBf16>
+template <int F>
 hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
                           hipEvent_t* events) {
   hipError_t err = hipSuccess;
@@ -887,16 +1061,16 @@ hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_
   if (events) {
     // Start/stop events attached to the dispatches: they time each kernel's
     // execution without extra packets between the kernels.
-    hipExtLaunchKernelGGL(gqa_decode_pieces<kBf16>, pieces_grid, block, 0, stream, events[0],
+    hipExtLaunchKernelGGL(gqa_decode_pieces<F>, pieces_grid, block, 0, stream, events[0],
                           events[1], 0, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipExtLaunchKernelGGL(gqa_decode_combine<kBf16>, combine_grid, block, 0, stream, events[2],
+    hipExtLaunchKernelGGL(gqa_decode_combine<F>, combine_grid, block, 0, stream, events[2],
                           events[3], 0, P);
     return hipGetLastError();
   }
-  gqa_decode_pieces<kBf16><<<pieces_grid, block, 0, stream>>>(P);
+  gqa_decode_pieces<F><<<pieces_grid, block, 0, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  gqa_decode_combine<kBf16><<<combine_grid, block, 0, stream>>>(P);
+  gqa_decode_combine<F><<<combine_grid, block, 0, stream>>>(P);
   return hipGetLastError();
 }
 
@@ -921,8 +1095,11 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.scale_log2 = score_scale_log2;
   P.out_scale = out_scale;
 
-  return elem == ElemType::kBf16 ? launch_kernels<true>(P, grid, batch, stream, events)
-                                 : launch_kernels<false>(P, grid, batch, stream, events);
+  switch (elem) {
+    case ElemType::kBf16: return launch_kernels<kFmtBf16>(P, grid, batch, stream, events);
+    case ElemType::kE4m3Kv: return launch_kernels<kFmtE4m3>(P, grid, batch, stream, events);
+    default: return launch_kernels<kFmtF16>(P, grid, batch, stream, events);
+  }
 }
 
 }  // namespace gqa

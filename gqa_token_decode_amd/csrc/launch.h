@@ -9,8 +9,9 @@
 
 namespace gqa {
 
-// Element type of q, kv and out.
-enum class ElemType { kF16, kBf16 };
+// Element types: q, kv and out all fp16 or all bf16; or fp16 q and out with
+// OCP FP8 E4M3 kv.
+enum class ElemType { kF16, kBf16, kE4m3Kv };
 
 // How the device-side planner cuts the valid rows into pieces.
 struct SplitConfig {

@@ -117,8 +117,11 @@ int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, v
 
 /* Element types accepted by gqa_decode_typed. */
 typedef enum gqa_dtype {
-  GQA_DTYPE_F16 = 0,   /* q, kv and out are IEEE binary16 (the page-4 operation)       */
-  GQA_DTYPE_BF16 = 1   /* q, kv and out are bfloat16 (8-bit exponent, 7-bit fraction)   */
+  GQA_DTYPE_F16 = 0,     /* q, kv and out are IEEE binary16 (the page-4 operation)      */
+  GQA_DTYPE_BF16 = 1,    /* q, kv and out are bfloat16 (8-bit exponent, 7-bit fraction)  */
+  GQA_DTYPE_E4M3_KV = 2  /* q and out binary16; kv holds OCP FP8 E4M3 bytes (1 sign,
+                            4 exponent bits with bias 7, 3 fraction bits; no
+                            infinities; S.1111.111 is NaN), one byte per element  */
 } gqa_dtype;
 
 /*
@@ -126,15 +129,20 @@ typedef enum gqa_dtype {
  * per-tensor K and V scales.
  *
  * Same layouts, alignment, ownership and error behaviour as gqa_decode, with
- * q, kv and out of element type `dtype` (a gqa_dtype; 2 bytes per element
- * for both). The stored K and V values stand for k_scale * K and
- * v_scale * V:
+ * q, kv and out of element type `dtype` (a gqa_dtype: 2 bytes per element,
+ * except E4M3 kv at 1 byte, so its kv is [batch, 2, 8, capacity, 128]
+ * bytes). The stored K and V values stand for k_scale * K and v_scale * V
+ * (for E4M3 this is the usual per-tensor dequantisation scale):
  *   s_i = (q_scale * k_scale / sqrt(128)) * dot(q[b,h,:], kv[b,0,g,i,:])
  *   out[b,h,:] = v_scale * sum_i softmax(s)_i * kv[b,1,g,i,:]
  * in fp32, rounded once to the output type (round to nearest even). With
  * dtype GQA_DTYPE_F16 and k_scale = v_scale = 1 this is gqa_decode_chunked.
  * The page-4 API is FP16 only (FlashInfer PR #5052 analysis page, section
- * 1); BF16 and the scales are this library's extension.
+ * 1); BF16, the scales and the E4M3 cache are this library's extension (the
+ * E4M3 format and dequantisation in on-chip memory follow the FlashInfer
+ * NVFP4 paged-context attention page, whose K/V pages are dequantised to
+ * E4M3 in shared memory). E4M3 values inside [0, L) that are NaN are outside
+ * the contract, as non-finite fp16 inputs are.
  * chunk_len  as for gqa_decode_chunked (0 = automatic split).
  * Returns GQA_ERR_BAD_ARG for an unknown dtype or a non-finite scale.
  */

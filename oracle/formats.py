@@ -40,3 +40,20 @@ def round_bf16(x) -> np.ndarray:
     out[~finite] = x[~finite]
     bits = out.astype(np.float32).view(np.uint32) >> np.uint32(16)   # exact: out is a bfloat16 value
     return bits.astype(np.uint16)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 codes (uint8 array) as float64.
+
+    Bit fields s eeee mmm: exponent bias 7; e = 0 encodes subnormals
+    m * 2^-9; e = 15 with m = 7 is NaN (the format has no infinities), so
+    the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)

@@ -15,12 +15,15 @@ above), and at most 2% of the elements may differ at all (expected: under
 
 fp16 with scales keeps the page bar: max |gpu - fp16(oracle)| <= 2e-3 and
 mean <= 2e-4 (the scales used keep |out| below 4, where one fp16 unit is
-still within 2e-3).
+still within 2e-3). So does the E4M3 cache (fp16 q and output): every E4M3
+code is converted to fp16 exactly, so the arithmetic after the conversion is
+that of the fp16 path, and the oracle takes the same exact code values times
+the scales.
 """
 import numpy as np
 import pytest
 
-from oracle.formats import bf16_to_f64, round_bf16
+from oracle.formats import bf16_to_f64, e4m3_to_f64, round_bf16
 from oracle.reference import decode_ragged, round_fp16
 import workloads
 
@@ -43,27 +46,35 @@ def _g():
 
 
 class _Widened:
-    """k_valid / v_valid of a bf16 workload, widened per (b, g) on access."""
+    """k_valid / v_valid of a bf16 or e4m3 workload, widened per (b, g) on
+    access."""
 
-    def __init__(self, arrays):
+    def __init__(self, arrays, widen):
         self.arrays = arrays
+        self.widen = widen
 
     def __getitem__(self, b):
-        arr = self.arrays[b]
+        arr, widen = self.arrays[b], self.widen
 
         class _Seq:
             def __getitem__(self, g):
-                return bf16_to_f64(arr[g])
+                return widen(arr[g])
 
         return _Seq()
 
 
 def oracle_of(w, q_scale=None, k_scale=1.0, v_scale=1.0):
+    """k_scale / v_scale multiply the workload's own scales (1, or the E4M3
+    cache's dequantisation scales)."""
     qs = w.q_scale if q_scale is None else q_scale
+    ks, vs = k_scale * w.k_scale, v_scale * w.v_scale
     if w.elem == "bf16":
-        return decode_ragged(bf16_to_f64(w.q), _Widened(w.k_valid), _Widened(w.v_valid), qs,
-                             k_scale=k_scale, v_scale=v_scale)
-    return decode_ragged(w.q, w.k_valid, w.v_valid, qs, k_scale=k_scale, v_scale=v_scale)
+        return decode_ragged(bf16_to_f64(w.q), _Widened(w.k_valid, bf16_to_f64),
+                             _Widened(w.v_valid, bf16_to_f64), qs, k_scale=ks, v_scale=vs)
+    if w.elem == "e4m3":
+        return decode_ragged(w.q, _Widened(w.k_valid, e4m3_to_f64),
+                             _Widened(w.v_valid, e4m3_to_f64), qs, k_scale=ks, v_scale=vs)
+    return decode_ragged(w.q, w.k_valid, w.v_valid, qs, k_scale=ks, v_scale=vs)
 
 
 def run(w, chunk_len=0, q_scale=None, k_scale=1.0, v_scale=1.0, kv=None):
@@ -73,7 +84,8 @@ def run(w, chunk_len=0, q_scale=None, k_scale=1.0, v_scale=1.0, kv=None):
     if kv is None:
         kv = w.kv_to_device(DEV)
     out = _g().gqa_decode(q, kv, lens, q_scale=w.q_scale if q_scale is None else q_scale,
-                          chunk_len=chunk_len, k_scale=k_scale, v_scale=v_scale)
+                          chunk_len=chunk_len, k_scale=k_scale * w.k_scale,
+                          v_scale=v_scale * w.v_scale)
     torch.cuda.synchronize()
     return out
 
@@ -202,3 +214,70 @@ def test_binding_rejects_mixed_dtypes():
     with pytest.raises(TypeError):
         g.gqa_decode(q, kv.to(torch.bfloat16), lens, out=torch.empty(1, 32, 128, dtype=torch.float16,
                                                                      device=DEV))
+
+
+# ---------------------------------------------------------------- E4M3 cache
+@pytest.mark.parametrize("name", workloads.SYNTHETIC + workloads.PAGE_SHAPES)
+def test_e4m3_parity_workloads(name):
+    print(f"case e4m3 {name}", flush=True)
+    w = workloads.get(name, "e4m3")
+    check_f16(run(w), oracle_of(w), f"e4m3 {name}")
+
+
+@pytest.mark.parametrize("chunk_len", [0, 7, 100])
+def test_e4m3_ragged_lengths_around_the_32_row_tile(chunk_len):
+    lens = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, -5, 1000]
+    w = workloads.build("e4m3 ragged", 58, 257, lens, fill="nan", elem="e4m3")
+    out = run(w, chunk_len=chunk_len)
+    got = out.cpu().numpy()
+    for b in np.flatnonzero(w.valid_lengths == 0):
+        assert np.all(got[b] == 0)
+    check_f16(out, oracle_of(w), f"e4m3 ragged chunk_len={chunk_len}")
+
+
+@pytest.mark.parametrize("batch,cap,lo,hi", [(100, 512, 0, 300), (1000, 64, 0, 40)])
+def test_e4m3_large_batches(batch, cap, lo, hi):
+    w = workloads.build(f"e4m3 batch{batch}", 70 + batch, cap,
+                        lambda r: r.integers(lo, hi, batch, endpoint=True), elem="e4m3")
+    check_f16(run(w), oracle_of(w), f"e4m3 batch {batch}")
+
+
+def test_e4m3_length_one_returns_dequantised_v_row_exactly():
+    # out = v_scale * V[0]: the code's value times 2^-4, exactly an fp16
+    # value. Compared as numbers: the E4M3 code for -0 (a draw that underflows)
+    # comes out as +0, since the weighted sum starts from +0.
+    w = workloads.build("e4m3 len1", 59, 96, [1, 1, 1], fill="nan", elem="e4m3")
+    got = run(w).cpu().numpy()
+    for b in range(3):
+        for h in range(32):
+            want = (e4m3_to_f64(w.v_valid[b][h // 4, 0]) * w.v_scale).astype(np.float16)
+            assert np.array_equal(got[b, h], want)
+
+
+def test_e4m3_contents_beyond_length_have_no_effect_bitwise():
+    torch = _torch()
+    w = workloads.build("e4m3 beyond", 60, 512, [100, 512, 3, 0], elem="e4m3")
+    base = run(w).cpu().numpy()
+    kv = w.kv_to_device(DEV)
+    raw = kv.view(torch.uint8)
+    for b, L in enumerate(w.valid_lengths):
+        raw[b, :, :, int(L):, :] = torch.randint(0, 256, raw[b, :, :, int(L):, :].shape,
+                                                 dtype=torch.uint8, device=DEV)
+    assert np.array_equal(run(w, kv=kv).cpu().numpy().view(np.uint16), base.view(np.uint16))
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(0.37, 1.0), (1.0, 0.5), (2.5, 1.75)])
+def test_e4m3_extra_scales(k_scale, v_scale):
+    w = workloads.build("e4m3 scales", 61, 3000, [3000, 1700, 1, 257], sigma_k=2.0, elem="e4m3")
+    check_f16(run(w, k_scale=k_scale, v_scale=v_scale),
+              oracle_of(w, k_scale=k_scale, v_scale=v_scale),
+              f"e4m3 k_scale x{k_scale} v_scale x{v_scale}")
+
+
+def test_e4m3_cache_as_uint8_or_float8_tensor():
+    torch = _torch()
+    w = workloads.build("e4m3 views", 62, 300, [300, 41], elem="e4m3")
+    kv = w.kv_to_device(DEV)
+    a = run(w, kv=kv).cpu().numpy()
+    b = run(w, kv=kv.view(torch.uint8)).cpu().numpy()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))

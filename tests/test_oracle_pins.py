@@ -423,3 +423,40 @@ def test_bf16_inputs_match_sdpa_on_widened_values():
                                          kvb[:, 1].double(), attn_mask=mask,
                                          scale=effective_scale(1.0), enable_gqa=True)
     assert np.abs(got - ref.squeeze(2).numpy()).max() <= 1e-12
+
+
+def test_e4m3_decoding_matches_torch_for_every_code():
+    import torch
+
+    from oracle.formats import e4m3_to_f64
+
+    codes = np.arange(256, dtype=np.uint8)
+    got = e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert ((got == ref) | (np.isnan(got) & np.isnan(ref))).all()
+    # fixed points of the format: largest finite, smallest subnormal and
+    # normal, one, signed zero, NaN codes
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0
+    assert got[0x80] == 0.0 and np.signbit(got[0x80])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.isfinite(np.delete(got, [0x7F, 0xFF])).all()
+
+
+def test_e4m3_cache_matches_sdpa_on_dequantised_tensors():
+    import torch
+    import torch.nn.functional as F
+
+    from oracle.formats import e4m3_to_f64
+
+    w = workloads.build("e4m3 pin", 57, 90, [90, 33, 1], elem="e4m3")
+    kv = w.dense_kv()
+    kv64 = e4m3_to_f64(kv)
+    got = decode(w.q, kv64, w.seq_lens, 1.0, k_scale=w.k_scale, v_scale=w.v_scale)
+    tkv = torch.from_numpy(kv).view(torch.float8_e4m3fn).to(torch.float64)
+    tk, tv = tkv[:, 0] * w.k_scale, tkv[:, 1] * w.v_scale
+    C = kv.shape[3]
+    mask = (torch.arange(C)[None, :] < torch.from_numpy(w.seq_lens.astype(np.int64))[:, None])[:, None, None, :]
+    ref = F.scaled_dot_product_attention(torch.from_numpy(w.q.astype(np.float64)).unsqueeze(2),
+                                         tk, tv, attn_mask=mask, scale=effective_scale(1.0),
+                                         enable_gqa=True).squeeze(2).numpy()
+    assert np.abs(got - ref).max() <= 1e-12

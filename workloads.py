@@ -23,7 +23,12 @@ correct decode never reads them.
 
 Element types: "f16" (default), or "bf16" for the library's bfloat16 entry
 point: the same float32 draws rounded to bfloat16 (nearest even) instead of
-fp16, kept as uint16 bit patterns on the host (numpy has no bfloat16).
+fp16, kept as uint16 bit patterns on the host (numpy has no bfloat16). Or
+"e4m3": q as fp16, and each K (V) draw divided by the per-tensor scale
+k_scale (v_scale), a power of two, and rounded to OCP FP8 E4M3 (nearest
+even, by torch's float8_e4m3fn conversion), kept as uint8 codes. With
+k_scale = v_scale = 2^-4 a unit-variance draw is coded at variance 256:
+well inside the format's range (largest finite 448) and above its subnormals.
 """
 from __future__ import annotations
 
@@ -38,6 +43,8 @@ HEAD_DIM = 128
 
 FP16_QNAN_BITS = 0x7E00
 BF16_QNAN_BITS = 0x7FC0
+E4M3_NAN_CODE = 0x7F
+E4M3_SCALE = 2.0 ** -4
 
 
 @dataclasses.dataclass
@@ -58,7 +65,9 @@ class Workload:
     k_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
     v_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
     fill: str = "zero"            # "zero" or "nan": contents beyond L_b
-    elem: str = "f16"             # "f16" or "bf16"
+    elem: str = "f16"             # "f16", "bf16" or "e4m3" (kv only)
+    k_scale: float = 1.0          # e4m3: the stored codes stand for K / k_scale
+    v_scale: float = 1.0
 
     @property
     def batch(self) -> int:
@@ -71,25 +80,26 @@ class Workload:
 
     @property
     def kv_bytes_read(self) -> int:
-        """K+V bytes of the valid prefixes: sum(L_b) * 2 * 8 * 128 * 2 B."""
-        return int(self.valid_lengths.sum()) * 2 * NUM_KV_HEADS * HEAD_DIM * 2
+        """K+V bytes of the valid prefixes: sum(L_b) * 2 * 8 * 128 * (2 B, or
+        1 B for e4m3)."""
+        return int(self.valid_lengths.sum()) * 2 * NUM_KV_HEADS * HEAD_DIM * self.kv_elem_bytes
 
     @property
-    def elem_bytes(self) -> int:
-        return 2
+    def kv_elem_bytes(self) -> int:
+        return 1 if self.elem == "e4m3" else 2
 
     def fill_value_bits(self) -> int:
         if self.fill != "nan":
             return 0
-        return BF16_QNAN_BITS if self.elem == "bf16" else FP16_QNAN_BITS
+        return {"bf16": BF16_QNAN_BITS, "e4m3": E4M3_NAN_CODE}.get(self.elem, FP16_QNAN_BITS)
 
     def _host_dtype(self):
-        return np.uint16 if self.elem == "bf16" else np.float16
+        return {"bf16": np.uint16, "e4m3": np.uint8}.get(self.elem, np.float16)
 
     def _torch_dtype(self):
         import torch
 
-        return torch.bfloat16 if self.elem == "bf16" else torch.float16
+        return {"bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}.get(self.elem, torch.float16)
 
     def q_to_device(self, device):
         """q as a device tensor of the workload's element type."""
@@ -119,20 +129,30 @@ class Workload:
         B, C = self.batch, self.capacity
         kv = torch.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=self._torch_dtype(),
                          device=device)
-        raw = kv.view(torch.int16)
-        raw.fill_(np.int16(np.uint16(self.fill_value_bits())).item())
+        if self.elem == "e4m3":
+            raw, host_raw = kv.view(torch.uint8), np.uint8
+            raw.fill_(self.fill_value_bits())
+        else:
+            raw, host_raw = kv.view(torch.int16), np.int16
+            raw.fill_(np.int16(np.uint16(self.fill_value_bits())).item())
         for b in range(B):
             L = self.k_valid[b].shape[1]
             if L:
-                raw[b, 0, :, :L, :].copy_(torch.from_numpy(self.k_valid[b].view(np.int16)))
-                raw[b, 1, :, :L, :].copy_(torch.from_numpy(self.v_valid[b].view(np.int16)))
+                raw[b, 0, :, :L, :].copy_(torch.from_numpy(self.k_valid[b].view(host_raw)))
+                raw[b, 1, :, :L, :].copy_(torch.from_numpy(self.v_valid[b].view(host_raw)))
         return kv
 
 
-def _normal(rng: np.random.Generator, shape, sigma: float, elem: str) -> np.ndarray:
+def _normal(rng: np.random.Generator, shape, sigma: float, elem: str,
+            code_scale: float = 1.0) -> np.ndarray:
     x = rng.standard_normal(shape, dtype=np.float32)
     if sigma != 1.0:
         x = x * np.float32(sigma)
+    if elem == "e4m3":
+        import torch
+
+        y = x / np.float32(code_scale)           # exact: a power-of-two scale
+        return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     if elem == "bf16":
         import torch
 
@@ -164,15 +184,16 @@ def build(
     else:
         lens = np.asarray(lengths, dtype=np.int64)
     B = int(lens.shape[0])
-    assert elem in ("f16", "bf16"), elem
-    q = _normal(rng, (B, NUM_Q_HEADS, HEAD_DIM), sigma_q, elem)
+    assert elem in ("f16", "bf16", "e4m3"), elem
+    kv_scale = E4M3_SCALE if elem == "e4m3" else 1.0
+    q = _normal(rng, (B, NUM_Q_HEADS, HEAD_DIM), sigma_q, "f16" if elem == "e4m3" else elem)
     k_valid, v_valid = [], []
     for b in range(B):
         L = int(min(max(lens[b], 0), capacity))
-        k_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_k, elem))
-        v_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_v, elem))
+        k_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_k, elem, kv_scale))
+        v_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_v, elem, kv_scale))
     return Workload(name, q, lens.astype(np.int32), int(capacity), float(q_scale),
-                    k_valid, v_valid, fill, elem)
+                    k_valid, v_valid, fill, elem, kv_scale, kv_scale)
 
 
 def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
@@ -235,7 +256,8 @@ PAGE_SHAPES = ["page_b1_c64", "page_b4_c256", "page_b1_c1024", "page_b1_c4096"]
 
 
 def get(name: str, elem: str = "f16") -> Workload:
-    """Named workload; elem="bf16" draws it (same seed and recipe) in bfloat16."""
+    """Named workload; elem="bf16" or "e4m3" draws it (same seed and recipe)
+    in that element type."""
     return WORKLOADS[name][1](elem)
 
 
