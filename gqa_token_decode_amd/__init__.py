@@ -13,6 +13,7 @@ entry point documented on the FlashInfer PR #5052 analysis page, section 1;
 bf16 tensors and the K/V scales are this library's extension):
     gqa_decode(q, kv, sequence_lengths, *, out=None, q_scale=1.0, chunk_len=0,
                k_scale=1.0, v_scale=1.0)
+    gqa_decode_paged(q, kv_pages, block_table, sequence_lengths, *, ...)
 """
 from __future__ import annotations
 
@@ -22,7 +23,7 @@ from typing import Optional
 
 import torch  # must load before the library so both share one HIP runtime
 
-__all__ = ["gqa_decode", "workspace_bytes", "release_workspace", "library_path",
+__all__ = ["gqa_decode", "gqa_decode_paged", "workspace_bytes", "release_workspace", "library_path",
            "load_library", "KernelTimer", "GqaDecodeError",
            "NUM_Q_HEADS", "NUM_KV_HEADS", "HEAD_DIM"]
 
@@ -65,6 +66,9 @@ def load_library():
     lib.gqa_decode_chunked.restype = i32
     lib.gqa_decode_typed.argtypes = [vp, vp, vp, vp, i32, f32, f32, f32, i32, i32, i32, vp]
     lib.gqa_decode_typed.restype = i32
+    lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(_Layout), f32, f32, f32,
+                                  i32, i32, i32, vp]
+    lib.gqa_decode_ex.restype = i32
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32]
     lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_decode_release_workspace.argtypes = []
@@ -108,37 +112,45 @@ _E4M3_KV = 2
 _FP8_KV_DTYPES = tuple(t for t in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if t is not None)
 
 
-def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor, *,
-               out: Optional[torch.Tensor] = None, q_scale: float = 1.0,
-               chunk_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
-    """Decode one token of GQA (32 query heads, 8 KV heads, dim 128).
+class _Layout(ctypes.Structure):
+    """struct gqa_layout of the C ABI (strides in elements)."""
 
-    q: fp16 or bf16 [batch, 32, 128]; kv: same dtype [batch, 2, 8, capacity,
-    128] with K at index 0 and V at index 1 of axis 1, or, with fp16 q, an
-    OCP FP8 E4M3 cache (torch.float8_e4m3fn, or uint8 holding E4M3 bytes)
-    dequantised by k_scale and v_scale; sequence_lengths:
-    int32 [batch] on the same device (values clamped to [0, capacity]).
-    ``out`` (optional, caller-owned, q's dtype and shape) receives the result
-    and is returned; otherwise a new tensor is allocated. Scores are scaled by
-    ``q_scale * k_scale / sqrt(128)`` and the output by ``v_scale``.
-    ``chunk_len`` > 0 fixes the split-KV piece length (0 = automatic).
-    Enqueued on the current stream of q's device.
-    """
+    _fields_ = [("q_stride_batch", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+                ("kv_stride_batch", ctypes.c_int64), ("kv_stride_kind", ctypes.c_int64),
+                ("kv_stride_head", ctypes.c_int64), ("kv_stride_row", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int),
+                ("page_size", ctypes.c_int), ("num_pages", ctypes.c_int)]
+
+
+def _check_view(name, t, dtype, shape_len):
+    """A tensor whose innermost (head-dim) axis is contiguous; other axes may
+    be strided (views into larger buffers)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if t.dim() != shape_len:
+        raise ValueError(f"{name} must have {shape_len} dimensions, got shape {tuple(t.shape)}")
+    if t.stride(-1) != 1 or any(st < 0 for st in t.stride()):
+        raise ValueError(f"{name} must have a contiguous last axis and non-negative strides")
+
+
+def _prepare(q, kv, sequence_lengths, out, kv_shape_check):
+    """Type/shape/device checks shared by the entry points. Returns
+    (dtype code, fp8 cache flag, out)."""
     if isinstance(q, torch.Tensor) and q.dtype in _DTYPES:
         dtype = q.dtype
     else:
         dtype = torch.float16
     fp8_kv = (dtype == torch.float16 and isinstance(kv, torch.Tensor)
               and kv.dtype in _FP8_KV_DTYPES)
-    _check_tensor("q", q, dtype, 3)
-    _check_tensor("kv", kv, kv.dtype if fp8_kv else dtype, 5)
+    _check_view("q", q, dtype, 3)
+    _check_view("kv", kv, kv.dtype if fp8_kv else dtype, 5)
     _check_tensor("sequence_lengths", sequence_lengths, torch.int32, 1)
     B = q.shape[0]
-    kshape = kv.shape
     if q.shape[1] != NUM_Q_HEADS or q.shape[2] != HEAD_DIM:
         raise ValueError(f"q must have shape [batch, 32, 128], got {tuple(q.shape)}")
-    if kshape[0] != B or kshape[1] != 2 or kshape[2] != NUM_KV_HEADS or kshape[4] != HEAD_DIM:
-        raise ValueError(f"kv must have shape [{B}, 2, 8, capacity, 128], got {tuple(kshape)}")
+    kv_shape_check(B)
     if sequence_lengths.shape[0] != B:
         raise ValueError(f"sequence_lengths must have shape [{B}], got {tuple(sequence_lengths.shape)}")
     dev = q.device
@@ -149,29 +161,111 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
             _check_device(name, t)
         raise ValueError("q, kv and sequence_lengths must be on the same device")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=dtype, device=dev)
     else:
         _check_tensor("out", out, dtype, 3)
         if out.shape != q.shape or out.device != dev:
             _check_device("out", out)
             raise ValueError("out must have q's shape and device")
+    return (_E4M3_KV if fp8_kv else _DTYPES[dtype]), fp8_kv, out
+
+
+def _stream_of(dev):
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(index)
+
+
+def _check_chunk(chunk_len):
     if chunk_len.__class__ is not int or chunk_len < 0:
         raise ValueError("chunk_len must be a non-negative int")
+
+
+def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor, *,
+               out: Optional[torch.Tensor] = None, q_scale: float = 1.0,
+               chunk_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Decode one token of GQA (32 query heads, 8 KV heads, dim 128).
+
+    q: fp16 or bf16 [batch, 32, 128]; kv: same dtype [batch, 2, 8, capacity,
+    128] with K at index 0 and V at index 1 of axis 1, or, with fp16 q, an
+    OCP FP8 E4M3 cache (torch.float8_e4m3fn, or uint8 holding E4M3 bytes)
+    dequantised by k_scale and v_scale; sequence_lengths:
+    int32 [batch] on the same device (values clamped to [0, capacity]).
+    q and kv may be strided views whose last axis is contiguous (e.g. q
+    sliced from a packed projection, or an NHD cache [batch, capacity, 2, 8,
+    128] permuted to this shape); no copy is made.
+    ``out`` (optional, caller-owned, contiguous, q's dtype and shape)
+    receives the result and is returned; otherwise a new tensor is allocated.
+    Scores are scaled by ``q_scale * k_scale / sqrt(128)`` and the output by
+    ``v_scale``. ``chunk_len`` > 0 fixes the split-KV piece length (0 =
+    automatic). Enqueued on the current stream of q's device.
+    """
+    def kv_shape(B):
+        ks = kv.shape
+        if ks[0] != B or ks[1] != 2 or ks[2] != NUM_KV_HEADS or ks[4] != HEAD_DIM:
+            raise ValueError(f"kv must have shape [{B}, 2, 8, capacity, 128], got {tuple(ks)}")
+
+    code, fp8_kv, out = _prepare(q, kv, sequence_lengths, out, kv_shape)
+    _check_chunk(chunk_len)
+    B, C = q.shape[0], kv.shape[3]
     lib = _lib if _lib is not None else load_library()
-    index = dev.index if dev.index is not None else torch.cuda.current_device()
-    stream = torch._C._cuda_getCurrentRawStream(index)
-    if fp8_kv or dtype != torch.float16 or k_scale != 1.0 or v_scale != 1.0:
-        code = _E4M3_KV if fp8_kv else _DTYPES[dtype]
-        st = lib.gqa_decode_typed(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
-                                  out.data_ptr(), code, float(q_scale), float(k_scale),
-                                  float(v_scale), B, kshape[3], chunk_len, stream)
+    stream = _stream_of(q.device)
+    args = (q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(), out.data_ptr())
+    if not (q.is_contiguous() and kv.is_contiguous()):
+        lay = _Layout(q.stride(0), q.stride(1), kv.stride(0), kv.stride(1), kv.stride(2),
+                      kv.stride(3), None, 0, 0, 0)
+        st = lib.gqa_decode_ex(*args, code, ctypes.byref(lay), float(q_scale), float(k_scale),
+                               float(v_scale), B, C, chunk_len, stream)
+    elif code != 0 or k_scale != 1.0 or v_scale != 1.0:
+        st = lib.gqa_decode_typed(*args, code, float(q_scale), float(k_scale), float(v_scale),
+                                  B, C, chunk_len, stream)
     elif chunk_len:
-        st = lib.gqa_decode_chunked(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
-                                    out.data_ptr(), float(q_scale), B, kshape[3], chunk_len,
-                                    stream)
+        st = lib.gqa_decode_chunked(*args, float(q_scale), B, C, chunk_len, stream)
     else:
-        st = lib.gqa_decode(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
-                            out.data_ptr(), float(q_scale), B, kshape[3], stream)
+        st = lib.gqa_decode(*args, float(q_scale), B, C, stream)
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
+                     sequence_lengths: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                     q_scale: float = 1.0, chunk_len: int = 0, k_scale: float = 1.0,
+                     v_scale: float = 1.0) -> torch.Tensor:
+    """Decode one token of GQA from a paged KV cache.
+
+    kv_pages: [num_pages, 2, 8, page_size, 128] (HND pages; fp16, bf16 or an
+    E4M3 cache as for gqa_decode; strided views with a contiguous last axis
+    allowed), page_size a power of two >= 16. block_table: int32 [batch,
+    max_pages] on the same device; position i of sequence b lives in page
+    block_table[b, i // page_size]. Entries for positions at or beyond a
+    sequence's length are never read. Lengths are clamped to
+    max_pages * page_size. Other arguments as for gqa_decode.
+    """
+    def kv_shape(B):
+        ks = kv_pages.shape
+        if ks[1] != 2 or ks[2] != NUM_KV_HEADS or ks[4] != HEAD_DIM:
+            raise ValueError(f"kv_pages must have shape [num_pages, 2, 8, page_size, 128], "
+                             f"got {tuple(ks)}")
+        _check_tensor("block_table", block_table, torch.int32, 2)
+        if block_table.shape[0] != B:
+            raise ValueError(f"block_table must have {B} rows, got {tuple(block_table.shape)}")
+
+    code, _, out = _prepare(q, kv_pages, sequence_lengths, out, kv_shape)
+    if block_table.device != q.device:
+        _check_device("block_table", block_table)
+        raise ValueError("block_table must be on q's device")
+    _check_chunk(chunk_len)
+    B = q.shape[0]
+    num_pages, page_size = kv_pages.shape[0], kv_pages.shape[3]
+    max_pages = block_table.shape[1]
+    lay = _Layout(q.stride(0), q.stride(1), kv_pages.stride(0), kv_pages.stride(1),
+                  kv_pages.stride(2), kv_pages.stride(3), block_table.data_ptr(), max_pages,
+                  page_size, num_pages)
+    lib = _lib if _lib is not None else load_library()
+    st = lib.gqa_decode_ex(q.data_ptr(), kv_pages.data_ptr(), sequence_lengths.data_ptr(),
+                           out.data_ptr(), code, ctypes.byref(lay), float(q_scale),
+                           float(k_scale), float(v_scale), B, max_pages * page_size, chunk_len,
+                           _stream_of(q.device))
     if st != 0:
         _raise(lib, st)
     return out

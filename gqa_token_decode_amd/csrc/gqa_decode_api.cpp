@@ -28,7 +28,6 @@
 namespace {
 
 constexpr size_t kQBytesPerSeq = (size_t)GQA_NUM_Q_HEADS * GQA_HEAD_DIM * 2;           // 8 KiB
-constexpr size_t kKvBytesPerPos = (size_t)2 * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * 2;    // 4 KiB
 constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
 constexpr int kMinPieceDefault = 128;      // cost units: two 64-row steps of a workgroup
 constexpr int kSegCostDefault = 128;       // fixed cost of a segment, in row units
@@ -113,13 +112,16 @@ const DeviceInfo& device_info(int dev) {
 
 // One equal piece per workgroup that can be resident at once (times an
 // optional factor), so the whole decode runs in a single round.
-gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece) {
+// row_align (1, or 16 for paged caches) rounds the piece and cost sizes up.
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align = 1) {
   gqa::SplitConfig cfg;
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
+  auto up = [row_align](int v) { return (v + row_align - 1) / row_align * row_align; };
   cfg.pieces = (di.cus > 0 ? di.cus : 256) * (di.resident > 0 ? di.resident : 1) * per_slot;
-  cfg.min_piece = env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30);
-  cfg.seg_cost = env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20);
-  cfg.forced_piece = forced_piece;
+  cfg.min_piece = up(env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30));
+  cfg.seg_cost = up(env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20));
+  cfg.forced_piece = forced_piece > 0 ? up(forced_piece) : 0;
+  cfg.row_align = row_align;
   return cfg;
 }
 
@@ -171,8 +173,85 @@ void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
   return ws->ptr;
 }
 
+// Strides resolved to bytes, with the address range each of q and kv spans.
+struct Resolved {
+  gqa::Layout lay;
+  size_t q_extent = 0, kv_extent = 0, table_bytes = 0;
+  int row_align = 1;
+};
+
+int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, Resolved* r) {
+  const long long C = capacity;
+  gqa_layout L;
+  if (in) {
+    L = *in;
+  } else {
+    L = gqa_layout{};
+    L.q_stride_batch = (long long)GQA_NUM_Q_HEADS * GQA_HEAD_DIM;
+    L.q_stride_head = GQA_HEAD_DIM;
+    L.kv_stride_row = GQA_HEAD_DIM;
+    L.kv_stride_head = C * GQA_HEAD_DIM;
+    L.kv_stride_kind = GQA_NUM_KV_HEADS * C * GQA_HEAD_DIM;
+    L.kv_stride_batch = 2 * L.kv_stride_kind;
+  }
+  const long long qs[2] = {L.q_stride_batch, L.q_stride_head};
+  const long long ks[4] = {L.kv_stride_batch, L.kv_stride_kind, L.kv_stride_head, L.kv_stride_row};
+  const long long kLimit = 1LL << 40;   // elements; keeps every product below 2^62
+  for (long long v : qs)
+    if (v < 0 || v > kLimit || (v * 2) % 16 != 0)
+      return fail(GQA_ERR_BAD_ARG, "gqa_decode: q strides must be >= 0 and keep rows 16-byte aligned");
+  for (long long v : ks)
+    if (v < 0 || v > kLimit || (v * (long long)kv_eb) % 16 != 0)
+      return fail(GQA_ERR_BAD_ARG, "gqa_decode: kv strides must be >= 0 and keep rows 16-byte aligned");
+  const long long row_bytes = GQA_HEAD_DIM * (long long)kv_eb;
+  const long long sr = L.kv_stride_row * (long long)kv_eb;
+  if (sr < row_bytes)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode: kv_stride_row must cover a %lld-byte row", row_bytes);
+  if (3 * L.q_stride_head * 2 + 2 * GQA_HEAD_DIM >= (1LL << 31))
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_stride_head is too large for 32-bit offsets");
+  const bool paged = L.block_table != nullptr;
+  long long rows_per_block = C;
+  if (paged) {
+    const int P = L.page_size;
+    if (P < 16 || (P & (P - 1)) != 0)
+      return fail(GQA_ERR_BAD_ARG, "gqa_decode: page_size must be a power of two >= 16, got %d", P);
+    if (L.max_pages <= 0 || L.num_pages <= 0)
+      return fail(GQA_ERR_BAD_ARG, "gqa_decode: max_pages and num_pages must be positive");
+    if ((long long)L.max_pages * P < C)
+      return fail(GQA_ERR_BAD_ARG, "gqa_decode: capacity %d exceeds max_pages * page_size", capacity);
+    if ((uintptr_t)L.block_table & 3u)
+      return fail(GQA_ERR_MISALIGNED, "gqa_decode: block_table must be 4-byte aligned");
+    rows_per_block = P;
+  }
+  if (sr * rows_per_block >= (1LL << 31))
+    return fail(GQA_ERR_BAD_ARG,
+                "gqa_decode: kv_stride_row times %s is too large for 32-bit offsets",
+                paged ? "page_size" : "capacity");
+  const long long blocks = paged ? L.num_pages : batch;
+  r->q_extent = (size_t)(((long long)(batch - 1) * L.q_stride_batch +
+                          (GQA_NUM_Q_HEADS - 1) * L.q_stride_head + GQA_HEAD_DIM) * 2);
+  r->kv_extent = (size_t)(((blocks - 1) * L.kv_stride_batch + L.kv_stride_kind +
+                           (GQA_NUM_KV_HEADS - 1) * L.kv_stride_head +
+                           (rows_per_block - 1) * L.kv_stride_row + GQA_HEAD_DIM) * (long long)kv_eb);
+  r->table_bytes = paged ? (size_t)batch * (size_t)L.max_pages * 4 : 0;
+  r->lay.q_sb = L.q_stride_batch * 2;
+  r->lay.q_sh = L.q_stride_head * 2;
+  r->lay.kv_sb = L.kv_stride_batch * (long long)kv_eb;
+  r->lay.kv_sk = L.kv_stride_kind * (long long)kv_eb;
+  r->lay.kv_sh = L.kv_stride_head * (long long)kv_eb;
+  r->lay.kv_sr = sr;
+  r->lay.block_table = L.block_table;
+  r->lay.max_pages = paged ? L.max_pages : 0;
+  r->lay.num_pages = paged ? L.num_pages : 0;
+  int shift = 0;
+  while (paged && (1 << shift) < L.page_size) ++shift;
+  r->lay.page_shift = shift;
+  r->row_align = paged ? 16 : 1;
+  return GQA_OK;
+}
+
 int check_args(const void* q, const void* kv, const int32_t* seq_lens, const void* out, int batch,
-               int capacity, int chunk_len, size_t kv_elem_bytes) {
+               int capacity, int chunk_len) {
   if (!q || !kv || !seq_lens || !out)
     return fail(GQA_ERR_NULL, "gqa_decode: q, kv, seq_lens and out must be non-NULL");
   if (batch <= 0 || capacity <= 0)
@@ -189,21 +268,30 @@ int check_args(const void* q, const void* kv, const int32_t* seq_lens, const voi
     return fail(GQA_ERR_MISALIGNED, "gqa_decode: q, kv and out must be 16-byte aligned");
   if ((uintptr_t)seq_lens & 3u)
     return fail(GQA_ERR_MISALIGNED, "gqa_decode: seq_lens must be 4-byte aligned");
-  const size_t qb = (size_t)batch * kQBytesPerSeq;
-  const size_t kvb = (size_t)batch * (size_t)capacity * (kKvBytesPerPos / 2) * kv_elem_bytes;
-  if (overlaps(out, qb, q, qb) || overlaps(out, qb, kv, kvb) ||
-      overlaps(out, qb, seq_lens, (size_t)batch * 4))
-    return fail(GQA_ERR_ALIAS, "gqa_decode: out must not overlap q, kv or seq_lens");
+  return GQA_OK;
+}
+
+int check_alias(const void* q, const void* kv, const int32_t* seq_lens, const void* out,
+                int batch, const Resolved& r) {
+  const size_t ob = (size_t)batch * kQBytesPerSeq;
+  if (overlaps(out, ob, q, r.q_extent) || overlaps(out, ob, kv, r.kv_extent) ||
+      overlaps(out, ob, seq_lens, (size_t)batch * 4) ||
+      (r.table_bytes && overlaps(out, ob, r.lay.block_table, r.table_bytes)))
+    return fail(GQA_ERR_ALIAS, "gqa_decode: out must not overlap q, kv, seq_lens or block_table");
   return GQA_OK;
 }
 
 int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
-                float q_scale, float k_scale, float v_scale, int batch, int capacity,
-                int chunk_len, hipStream_t stream) {
+                const gqa_layout* layout, float q_scale, float k_scale, float v_scale, int batch,
+                int capacity, int chunk_len, hipStream_t stream) {
+  int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len);
+  if (st != GQA_OK) return st;
   if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16 && dtype != GQA_DTYPE_E4M3_KV)
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: unknown dtype %d", dtype);
-  int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len,
-                      dtype == GQA_DTYPE_E4M3_KV ? 1 : 2);
+  Resolved res;
+  st = resolve_layout(layout, batch, capacity, dtype == GQA_DTYPE_E4M3_KV ? 1 : 2, &res);
+  if (st != GQA_OK) return st;
+  st = check_alias(q, kv, seq_lens, out, batch, res);
   if (st != GQA_OK) return st;
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_scale, k_scale and v_scale must be finite");
@@ -215,9 +303,11 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
   }
   const int dev = pointer_device(q);
   if (dev < 0) return fail(GQA_ERR_DEVICE_MISMATCH, "gqa_decode: q is not device memory");
-  if (pointer_device(kv) != dev || pointer_device(out) != dev || pointer_device(seq_lens) != dev)
+  if (pointer_device(kv) != dev || pointer_device(out) != dev || pointer_device(seq_lens) != dev ||
+      (res.lay.block_table && pointer_device(res.lay.block_table) != dev))
     return fail(GQA_ERR_DEVICE_MISMATCH,
-                "gqa_decode: q, kv, seq_lens and out must be device memory on one device");
+                "gqa_decode: q, kv, seq_lens, out (and block_table) must be device memory on one "
+                "device");
 
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) prev = -1;
@@ -232,7 +322,7 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
       st = fail(di.status, "gqa_decode: device %d is %s; this library is built for gfx950", dev,
                 di.arch.c_str());
     } else {
-      const gqa::SplitConfig cfg = split_config(di, chunk_len);
+      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align);
       const long long grid = gqa::grid_for(batch, capacity, cfg);
       const size_t pbytes =
           grid > 0 ? gqa::segment_bytes_for_batch(batch) + gqa::partial_bytes_for_grid(grid) : 0;
@@ -265,9 +355,9 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
           const gqa::ElemType elem = dtype == GQA_DTYPE_BF16      ? gqa::ElemType::kBf16
                                      : dtype == GQA_DTYPE_E4M3_KV ? gqa::ElemType::kE4m3Kv
                                                                   : gqa::ElemType::kF16;
-          const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, elem, (float)scale,
-                                                  v_scale, batch, capacity, cfg, grid, ws, stream,
-                                                  ev);
+          const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, elem, res.lay,
+                                                  (float)scale, v_scale, batch, capacity, cfg,
+                                                  grid, ws, stream, ev);
           if (e != hipSuccess)
             st = fail(GQA_ERR_LAUNCH, "gqa_decode: kernel launch failed: %s", hipGetErrorString(e));
         }
@@ -284,21 +374,28 @@ extern "C" {
 
 int gqa_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out, float q_scale,
                int batch, int capacity, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, q_scale, 1.0f, 1.0f, batch, capacity, 0,
-                     stream);
+  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, nullptr, q_scale, 1.0f, 1.0f, batch,
+                     capacity, 0, stream);
 }
 
 int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                        float q_scale, int batch, int capacity, int chunk_len, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, q_scale, 1.0f, 1.0f, batch, capacity,
-                     chunk_len, stream);
+  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, nullptr, q_scale, 1.0f, 1.0f, batch,
+                     capacity, chunk_len, stream);
 }
 
 int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
                      float q_scale, float k_scale, float v_scale, int batch, int capacity,
                      int chunk_len, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, dtype, q_scale, k_scale, v_scale, batch, capacity,
-                     chunk_len, stream);
+  return decode_impl(q, kv, seq_lens, out, dtype, nullptr, q_scale, k_scale, v_scale, batch,
+                     capacity, chunk_len, stream);
+}
+
+int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
+                  const gqa_layout* layout, float q_scale, float k_scale, float v_scale,
+                  int batch, int capacity, int chunk_len, hipStream_t stream) {
+  return decode_impl(q, kv, seq_lens, out, dtype, layout, q_scale, k_scale, v_scale, batch,
+                     capacity, chunk_len, stream);
 }
 
 size_t gqa_decode_workspace_bytes(int batch, int capacity) {

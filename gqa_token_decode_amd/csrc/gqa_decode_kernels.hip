@@ -109,13 +109,29 @@ struct Params {
   int seg_cost;        // fixed cost units per segment (c0)
   float scale_log2;    // q_scale * k_scale / sqrt(128) * log2(e)
   float out_scale;     // v_scale: applied to the normalised output
+  // Addressing, in bytes. q row (b, h) starts at q + b*q_sb + h*q_sh; K (kind
+  // 0) or V (kind 1) row i of (b, g) at kv + b*kv_sb + kind*kv_sk + g*kv_sh +
+  // i*kv_sr. Paged caches replace b*kv_sb by page*kv_sb, page =
+  // block_table[b*max_pages + i/page_size], and i by i % page_size.
+  long long q_sb, q_sh, kv_sb, kv_sk, kv_sh, kv_sr;
+  const int32_t* block_table;   // paged: [batch][max_pages] page ids
+  int max_pages, page_shift, num_pages;
+  int row_align;                // 1, or 16 for paged caches: segments and pieces
+                                // start at multiples of 16 rows
 };
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
+// Rows a segment of length len occupies on the cost line: len rounded up to
+// the row alignment (so that with alignment 16 every segment's rows, and
+// every piece, start at a multiple of 16).
+__device__ __forceinline__ long long cost_len(const Params& P, long long len) {
+  return (len + P.row_align - 1) & ~(long long)(P.row_align - 1);
+}
+
 // Cost of sequence b on the cost line: 8 segments of c0 + L units, or 0.
-__device__ __forceinline__ long long seq_cost(long long len, int c0) {
-  return len > 0 ? 8 * (len + c0) : 0;
+__device__ __forceinline__ long long seq_cost(const Params& P, long long len) {
+  return len > 0 ? 8 * (cost_len(P, len) + P.seg_cost) : 0;
 }
 
 // Length of sequence b read through the scalar path (b must be uniform), so
@@ -206,7 +222,7 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
     const int b = b0 + threadIdx.x;
     const long long len = b < P.batch ? clamp_len(P.seq_lens[b], P.capacity) : 0;
     long long total;
-    const long long cost = seq_cost(len, P.seg_cost);
+    const long long cost = seq_cost(P, len);
     const long long incl = block_scan(cost, red, &total);
     const long long lo = before + incl - cost;
     if (cost > 0 && p >= lo && p < lo + cost) {
@@ -230,7 +246,7 @@ __device__ long long wave_plan(const Params& P, long long (*piece_start)(const P
   const int lane = threadIdx.x & 63;
   const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
   *lens_v = (int)len;
-  const long long cost = seq_cost(len, P.seg_cost);
+  const long long cost = seq_cost(P, len);
   long long incl = cost;
   for (int o = 1; o < 64; o <<= 1) {
     const long long t = __shfl_up(incl, o);
@@ -276,7 +292,7 @@ __device__ __forceinline__ void seg_set_range(Seg& s, long long p_begin, long lo
 
 // Whether the piece ending at p_end holds rows of a segment after s.
 __device__ __forceinline__ bool more_segments(const Params& P, const Seg& s, long long p_end) {
-  return s.off + s.len + P.seg_cost < p_end;
+  return s.off + cost_len(P, s.len) + P.seg_cost < p_end;
 }
 
 // Clamped length of sequence b (b uniform): from the wave's length register
@@ -289,7 +305,7 @@ __device__ __forceinline__ int seq_len_of(const Params& P, int lens_v, int b) {
 // Advance to the next segment (next KV head of b, else the next non-empty
 // sequence). Only called while rows remain below p_end, so one exists.
 __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end, int lens_v) {
-  const long long end = s.off + s.len + P.seg_cost;
+  const long long end = s.off + cost_len(P, s.len) + P.seg_cost;
   if (s.g + 1 < kKvHeads) {
     s.g += 1;
   } else {
@@ -348,40 +364,92 @@ __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (
 // tiles reuse the q registers, and their empty q load leaves zeros in the
 // slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
 // rows of 128 B (E4M3).
-template <int F>
+// Buffer resource over rows [row0, row0 + nrows) of one K or V block that
+// starts at `base` (row stride kv_sr bytes); rows past nrows read as zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, long long row0,
+                                                            int nrows, long long sr) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * sr), 0,
+                                           nrows > 0 ? (int)(nrows * sr) : 0, kBufferFlags);
+}
+
+// Page holding row i of sequence b (paged caches): the page's byte offset,
+// or -1 if the page id is outside [0, num_pages) (its rows then read as
+// zeros instead of faulting). Uniform: one scalar load.
+__device__ __forceinline__ long long page_base(const Params& P, int b, int i) {
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)P.block_table;
+  const int page = bt[(size_t)b * P.max_pages + (i >> P.page_shift)];
+  return (page >= 0 && page < P.num_pages) ? (long long)page * P.kv_sb : -1;
+}
+
+// Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
+// an LDS stage (K, then V) and the segment's 4 query rows into the wave's q
+// slot, in this order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros.
+// With live == false the buffers are empty: the same 9 loads return zeros
+// without touching memory, so every pipeline step has the same shape. The q
+// load is live only for a wave's first tile of a segment (live_q); later
+// tiles reuse the q registers, and their empty q load leaves zeros in the
+// slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
+// rows of 128 B (E4M3). In LDS the rows are dense whatever the strides.
+// Paged caches (page size a multiple of 16): each 16-row half of a tile
+// lies in one page.
+template <int F, bool kPaged>
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
                                            bool live_q, e16_t* stage, e16_t* qslot) {
   constexpr int kRowBytes = row_bytes<F>();
+  constexpr int kRows = tile_rows<F>();
   const int lane = threadIdx.x & 63;
-  const char* kvb = reinterpret_cast<const char*>(P.kv);
-  const size_t seg_bytes = (size_t)P.capacity * kRowBytes;
-  const char* kb = kvb + ((size_t)(s.b * 2 + 0) * kKvHeads + s.g) * seg_bytes;
-  const char* vb = kvb + ((size_t)(s.b * 2 + 1) * kKvHeads + s.g) * seg_bytes;
-  const e16_t* qg = P.q + ((size_t)s.b * kQHeads + s.g * kGroup) * kDim;
-  const int nbytes = live ? s.hi * kRowBytes : 0;
-  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, live && live_q ? kQHalves * 2 : 0, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nbytes, kBufferFlags);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)qslot, 16, 16 * lane, 0, 0, 0);
+  const char* qg = reinterpret_cast<const char*>(P.q) + s.b * P.q_sb + (s.g * kGroup) * P.q_sh;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)qg, 0, live && live_q ? (int)(3 * P.q_sh + 2 * kDim) : 0, kBufferFlags);
+  // q: lane l loads 16 B of query row l/16 (of the group's 4), chunk l%16.
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)qslot, 16,
+                                           (int)((lane >> 4) * P.q_sh) + 16 * (lane & 15), 0, 0, 0);
+  const int nrows = live ? s.hi - t : 0;          // rows of this tile below s.hi
   // DMA lane l writes 16 B at LDS offset 16*l of the 1 KiB block u: for
   // 16-bit formats row 4u + l/16, physical chunk l%16, which holds logical
   // chunk vchunk(row, l%16); for E4M3 row 8u + l/8, physical chunk l%8,
   // holding logical chunk (l%8) ^ swz8(row). Both swizzles are their own
   // inverse.
   char* st = reinterpret_cast<char*>(stage);
+  // Paged: byte offsets of the pages holding rows t and t + 16 (-1: none).
+  long long pb0 = -1, pb1 = -1;
+  if constexpr (kPaged) {
+    pb0 = nrows > 0 ? page_base(P, s.b, t) : -1;
+    if constexpr (kRows == 32) pb1 = nrows > 16 ? page_base(P, s.b, t + 16) : -1;
+  }
 #pragma unroll
   for (int kind = 0; kind < 2; ++kind) {
+    __amdgpu_buffer_rsrc_t r0, r1;   // rows [0, 16) and [16, 32) of the tile
+    if constexpr (kPaged) {
+      const char* blk = reinterpret_cast<const char*>(P.kv) + kind * P.kv_sk + s.g * P.kv_sh;
+      const int psz_mask = (1 << P.page_shift) - 1;
+      r0 = rows_rsrc(blk + (pb0 < 0 ? 0 : pb0), t & psz_mask, pb0 < 0 ? 0 : (nrows < 16 ? nrows : 16),
+                     P.kv_sr);
+      r1 = r0;
+      if constexpr (kRows == 32)
+        r1 = rows_rsrc(blk + (pb1 < 0 ? 0 : pb1), (t + 16) & psz_mask,
+                       pb1 < 0 ? 0 : (nrows - 16 < 16 ? nrows - 16 : 16), P.kv_sr);
+    } else {
+      const char* blk = reinterpret_cast<const char*>(P.kv) + s.b * P.kv_sb + kind * P.kv_sk +
+                        s.g * P.kv_sh;
+      r0 = rows_rsrc(blk, t, nrows, P.kv_sr);
+      r1 = r0;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      int off;
+      int r, c;
       if constexpr (F == kFmtE4m3) {
-        const int r = 8 * u + (lane >> 3);
-        off = (t + r) * kRowBytes + 16 * ((lane & 7) ^ swz8(r));
+        r = 8 * u + (lane >> 3);
+        c = (lane & 7) ^ swz8(r);
       } else {
-        const int r = 4 * u + (lane >> 4);
-        off = (t + r) * kRowBytes + 16 * vchunk(r, lane & 15);
+        r = 4 * u + (lane >> 4);
+        c = vchunk(r, lane & 15);
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kind ? rv : rk,
+      // in paged mode the second half of an E4M3 tile has its own resource
+      const bool second = kPaged && kRows == 32 && u >= 2;
+      const int off = (int)((second ? r - 16 : r) * P.kv_sr) + 16 * c;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? r1 : r0,
                                                (lds_void_t*)(st + kind * 4096 + u * 1024), 16,
                                                off, 0, 0, kNonTemporal);
     }
@@ -729,7 +797,7 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
 // group) into `nxt` and the q slot; wait for the current tile; fold it in.
 // Loads complete in issue order, so "all but the newest N" waits are exact
 // (vector stores issued in between only make them wait longer).
-template <int F>
+template <int F, bool kPaged>
 __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, int par,
                                           e16_t* nxt, e16_t* qslot, bool first,
                                           bool has_next, const Seg& nseg, int nt,
@@ -739,7 +807,7 @@ __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, i
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
     read_q(qslot, qb);
   }
-  issue_tile<F>(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
+  issue_tile<F, kPaged>(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
   if constexpr (F == kFmtE4m3)
     compute_tile8(la, par, qb, t, hi, P.scale_log2, acc);
@@ -809,7 +877,8 @@ __device__ __forceinline__ long long slot_of(long long seg_off, long long piece_
 __device__ __forceinline__ long long piece_len(const Params& P, long long total) {
   if (P.forced_piece > 0) return P.forced_piece;
   long long Q = (total + P.pieces - 1) / P.pieces;
-  return Q < P.min_piece ? P.min_piece : Q;
+  Q = Q < P.min_piece ? P.min_piece : Q;
+  return cost_len(P, Q);
 }
 
 __device__ long long this_piece_start(const Params& P, long long total) {
@@ -832,7 +901,7 @@ __device__ __forceinline__ void zero_empty_sequences(const Params& P, int lens_v
 }
 
 // ---------------------------------------------------------------- kernel 1
-template <int F>
+template <int F, bool kPaged>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(Params P) {
   constexpr bool kBf16 = F == kFmtBf16;
@@ -857,7 +926,7 @@ void gqa_decode_pieces(Params P) {
   } else {
     long long part = 0;
     for (int b = tid; b < P.batch; b += kThreads)
-      part += seq_cost(clamp_len(P.seq_lens[b], P.capacity), P.seg_cost);
+      part += seq_cost(P, clamp_len(P.seq_lens[b], P.capacity));
     total = block_sum(part, red);
     p0 = this_piece_start(P, total);
     found_b = -1;
@@ -884,7 +953,7 @@ void gqa_decode_pieces(Params P) {
   s.b = found_b;
   s.len = P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, s.b)
                         : __builtin_amdgcn_readfirstlane(found_len);
-  const long long stride = (long long)s.len + P.seg_cost;
+  const long long stride = cost_len(P, s.len) + P.seg_cost;
   s.g = (int)((p0 - found) / stride);
   s.off = found + (long long)s.g * stride + P.seg_cost;
   seg_set_range(s, p0, p1);
@@ -901,7 +970,7 @@ void gqa_decode_pieces(Params P) {
   Seg pf = s;
   int pt = s.lo + kRows * wv;
   const bool pf_ok = tile_first<kRows>(P, pf, pt, p1, wv, lens_v);
-  issue_tile<F>(P, pf, pt, pf_ok, true, st0, qslot);
+  issue_tile<F, kPaged>(P, pf, pt, pf_ok, true, st0, qslot);
   zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
 
@@ -917,7 +986,7 @@ void gqa_decode_pieces(Params P) {
       Seg nf = pf;
       int nt = pt;
       const bool n_ok = tile_next<kRows>(P, nf, nt, p1, wv, lens_v);
-      tile_step<F>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
+      tile_step<F, kPaged>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
                 nf.off != s.off, t, s.hi, qb, acc);
       pf = nf;
       pt = nt;
@@ -1022,24 +1091,26 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
 }  // namespace
 
 int resident_workgroups_per_cu() {
-  int n[3] = {0, 0, 0};
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], gqa_decode_pieces<kFmtF16>, kThreads, 0) !=
-          hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], gqa_decode_pieces<kFmtBf16>, kThreads, 0) !=
-          hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], gqa_decode_pieces<kFmtE4m3>, kThreads, 0) !=
-          hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
+  const void* kernels[6] = {
+      (const void*)gqa_decode_pieces<kFmtF16, false>, (const void*)gqa_decode_pieces<kFmtBf16, false>,
+      (const void*)gqa_decode_pieces<kFmtE4m3, false>, (const void*)gqa_decode_pieces<kFmtF16, true>,
+      (const void*)gqa_decode_pieces<kFmtBf16, true>, (const void*)gqa_decode_pieces<kFmtE4m3, true>};
+  int m = 1 << 30;
+  for (const void* k : kernels) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    m = n < m ? n : m;
   }
-  int m = n[0];
-  for (int i = 1; i < 3; ++i) m = n[i] < m ? n[i] : m;
   return m;
 }
 
 long long grid_for(int batch, int capacity, const SplitConfig& cfg) {
   if (cfg.forced_piece > 0) {
-    const long long rows = 8LL * batch * capacity;
+    const long long a = cfg.row_align > 1 ? cfg.row_align : 1;
+    const long long rows = 8LL * batch * ((capacity + a - 1) / a * a);
     return (rows + cfg.forced_piece - 1) / cfg.forced_piece;
   }
   return cfg.pieces;
@@ -1053,7 +1124,7 @@ size_t segment_bytes_for_batch(int batch) {
   return ((size_t)batch * kKvHeads * sizeof(int2) + 255) & ~(size_t)255;
 }
 
-template <int F>
+template <int F, bool kPaged>
 hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
                           hipEvent_t* events) {
   hipError_t err = hipSuccess;
@@ -1061,23 +1132,23 @@ hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_
   if (events) {
     // Start/stop events attached to the dispatches: they time each kernel's
     // execution without extra packets between the kernels.
-    hipExtLaunchKernelGGL(gqa_decode_pieces<F>, pieces_grid, block, 0, stream, events[0],
+    hipExtLaunchKernelGGL(gqa_decode_pieces<F, kPaged>, pieces_grid, block, 0, stream, events[0],
                           events[1], 0, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     hipExtLaunchKernelGGL(gqa_decode_combine<F>, combine_grid, block, 0, stream, events[2],
                           events[3], 0, P);
     return hipGetLastError();
   }
-  gqa_decode_pieces<F><<<pieces_grid, block, 0, stream>>>(P);
+  gqa_decode_pieces<F, kPaged><<<pieces_grid, block, 0, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   gqa_decode_combine<F><<<combine_grid, block, 0, stream>>>(P);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
-                         ElemType elem, float score_scale_log2, float out_scale, int batch,
-                         int capacity, const SplitConfig& cfg, long long grid, void* partials,
-                         hipStream_t stream, hipEvent_t* events) {
+                         ElemType elem, const Layout& layout, float score_scale_log2,
+                         float out_scale, int batch, int capacity, const SplitConfig& cfg,
+                         long long grid, void* partials, hipStream_t stream, hipEvent_t* events) {
   Params P;
   P.q = static_cast<const e16_t*>(q);
   P.kv = static_cast<const e16_t*>(kv);
@@ -1094,11 +1165,29 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.seg_cost = cfg.forced_piece > 0 ? 0 : cfg.seg_cost;
   P.scale_log2 = score_scale_log2;
   P.out_scale = out_scale;
+  P.q_sb = layout.q_sb;
+  P.q_sh = layout.q_sh;
+  P.kv_sb = layout.kv_sb;
+  P.kv_sk = layout.kv_sk;
+  P.kv_sh = layout.kv_sh;
+  P.kv_sr = layout.kv_sr;
+  P.block_table = layout.block_table;
+  P.max_pages = layout.max_pages;
+  P.page_shift = layout.page_shift;
+  P.num_pages = layout.num_pages;
+  P.row_align = cfg.row_align > 1 ? cfg.row_align : 1;
 
+  const bool paged = layout.block_table != nullptr;
   switch (elem) {
-    case ElemType::kBf16: return launch_kernels<kFmtBf16>(P, grid, batch, stream, events);
-    case ElemType::kE4m3Kv: return launch_kernels<kFmtE4m3>(P, grid, batch, stream, events);
-    default: return launch_kernels<kFmtF16>(P, grid, batch, stream, events);
+    case ElemType::kBf16:
+      return paged ? launch_kernels<kFmtBf16, true>(P, grid, batch, stream, events)
+                   : launch_kernels<kFmtBf16, false>(P, grid, batch, stream, events);
+    case ElemType::kE4m3Kv:
+      return paged ? launch_kernels<kFmtE4m3, true>(P, grid, batch, stream, events)
+                   : launch_kernels<kFmtE4m3, false>(P, grid, batch, stream, events);
+    default:
+      return paged ? launch_kernels<kFmtF16, true>(P, grid, batch, stream, events)
+                   : launch_kernels<kFmtF16, false>(P, grid, batch, stream, events);
   }
 }
 

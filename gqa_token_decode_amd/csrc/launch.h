@@ -13,18 +13,29 @@ namespace gqa {
 // OCP FP8 E4M3 kv.
 enum class ElemType { kF16, kBf16, kE4m3Kv };
 
+// Addressing of q and kv, in bytes (see the kernel's Params). A non-null
+// block_table selects the paged kernels: kv_sb is then the page stride, and
+// pages hold 2^page_shift positions (page_shift >= 4).
+struct Layout {
+  long long q_sb, q_sh, kv_sb, kv_sk, kv_sh, kv_sr;
+  const int32_t* block_table;
+  int max_pages, page_shift, num_pages;
+};
+
 // How the device-side planner cuts the valid rows into pieces.
 struct SplitConfig {
   int pieces;         // automatic split: number of equal pieces (one workgroup each)
   int min_piece;      // automatic split: lower bound on the piece length (rows)
   int forced_piece;   // > 0: fixed piece length; the grid then covers batch*capacity rows
   int seg_cost;       // automatic split: fixed cost units per (sequence, KV head) segment
+  int row_align;      // 1, or 16 for paged caches (pieces and segments 16-row aligned)
 };
 
 // Workgroups of the pieces kernel that fit on one CU at once (0 on error).
 int resident_workgroups_per_cu();
 
-// Number of workgroups launched for this shape and split.
+// Number of workgroups launched for this shape and split (forced pieces must
+// already be a multiple of cfg.row_align).
 long long grid_for(int batch, int capacity, const SplitConfig& cfg);
 
 // Bytes of fp32 partial-result storage for a grid (two slots per workgroup).
@@ -38,8 +49,8 @@ size_t segment_bytes_for_batch(int batch);
 // `events` (may be null) points at four events: start and stop of the pieces
 // kernel, then start and stop of the combine kernel.
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
-                         ElemType elem, float score_scale_log2, float out_scale, int batch,
-                         int capacity,
+                         ElemType elem, const Layout& layout, float score_scale_log2,
+                         float out_scale, int batch, int capacity,
                          const SplitConfig& cfg, long long grid, void* partials,
                          hipStream_t stream, hipEvent_t* events);
 

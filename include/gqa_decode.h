@@ -151,6 +151,60 @@ int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, voi
                      int chunk_len, hipStream_t stream);
 
 /*
+ * Memory layout of q and kv for gqa_decode_ex. Strides count elements of the
+ * tensor they describe (not bytes), must be non-negative, and must keep
+ * every row 16-byte aligned (stride * element size a multiple of 16); each
+ * 128-element head row is contiguous. The values for the contiguous layouts
+ * of gqa_decode are given in brackets (C = capacity).
+ *
+ * Paged cache (block_table != NULL): kv holds num_pages pages, each
+ * [2][8][page_size][128] under the strides below (kv_stride_batch is then the
+ * stride between pages); position i of sequence b is row i % page_size of
+ * page block_table[b * max_pages + i / page_size]. This is the HND page
+ * layout named on the FlashInfer NVFP4 paged-context attention page.
+ * Positions at or beyond a sequence's length are never read, so their
+ * table entries are never read either. A page id outside [0, num_pages)
+ * for a position inside the length reads as zeros (no fault; the result
+ * for that sequence is then meaningless).
+ */
+typedef struct gqa_layout {
+  int64_t q_stride_batch;    /* q[b] -> q[b+1]                      [32*128]        */
+  int64_t q_stride_head;     /* q[b,h] -> q[b,h+1]                  [128]           */
+  int64_t kv_stride_batch;   /* kv[b] -> kv[b+1], or page -> page   [2*8*C*128]     */
+  int64_t kv_stride_kind;    /* K -> V                              [8*C*128]       */
+  int64_t kv_stride_head;    /* KV head g -> g+1                    [C*128]         */
+  int64_t kv_stride_row;     /* position i -> i+1                   [128]           */
+  const int32_t* block_table; /* NULL, or device int32 [batch][max_pages], 4-byte
+                                 aligned, on the same device as kv                   */
+  int max_pages;             /* paged: entries per block_table row                   */
+  int page_size;             /* paged: positions per page, a power of two >= 16      */
+  int num_pages;             /* paged: pages in kv                                   */
+} gqa_layout;
+
+/*
+ * gqa_decode_ex -- gqa_decode_typed with explicit strides and an optional
+ * page table.
+ *
+ * layout  NULL means the contiguous layouts (then identical to
+ *         gqa_decode_typed). out stays a contiguous [batch, 32, 128] tensor.
+ * capacity  the largest position count of a sequence (lengths are clamped
+ *         to it); for a paged cache at most max_pages * page_size.
+ * chunk_len  as for gqa_decode_chunked; for a paged cache it is rounded up
+ *         to a multiple of 16.
+ * Limits (GQA_ERR_BAD_ARG): kv_stride_row must cover a row (256 B, or 128 B
+ * for E4M3); kv_stride_row in bytes times capacity (paged: page_size) and
+ * q_stride_head in bytes times 3 plus 256 must stay below 2^31 (32-bit
+ * buffer offsets). The overlap check for out uses each tensor's address
+ * range under its strides.
+ * Use: strided views (e.g. q as a slice of a packed projection output, or
+ * an NHD cache [batch, capacity, 2, 8, 128] seen as [batch, 2, 8, capacity,
+ * 128]) and paged caches, without copies.
+ */
+int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
+                  const gqa_layout* layout, float q_scale, float k_scale, float v_scale,
+                  int batch, int capacity, int chunk_len, hipStream_t stream);
+
+/*
  * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace
  * the automatic split needs for (batch, capacity) on the current device
  * (a per-segment descriptor table plus two partial slots per workgroup).

@@ -51,7 +51,8 @@ def _gpu_visible():
 def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     assert names == sorted([
-        "gqa_decode", "gqa_decode_chunked", "gqa_decode_typed", "gqa_decode_workspace_bytes",
+        "gqa_decode", "gqa_decode_chunked", "gqa_decode_typed", "gqa_decode_ex",
+        "gqa_decode_workspace_bytes",
         "gqa_decode_release_workspace", "gqa_decode_status_string", "gqa_decode_last_error",
         "gqa_decode_profile_begin", "gqa_decode_profile_end"])
 
@@ -186,3 +187,50 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", text), f
+
+
+def _layout(**kw):
+    from gqa_token_decode_amd import _Layout
+
+    C = kw.pop("C", 64)
+    d = dict(q_stride_batch=4096, q_stride_head=128, kv_stride_batch=2 * 8 * C * 128,
+             kv_stride_kind=8 * C * 128, kv_stride_head=C * 128, kv_stride_row=128,
+             block_table=None, max_pages=0, page_size=0, num_pages=0)
+    d.update(kw)
+    return _Layout(**d)
+
+
+def _call_ex(lib, lay, dtype=0, B=2, C=64, chunk=0, q=0x10000, kv=0x20000000, out=0x40000):
+    return lib.gqa_decode_ex(q, kv, 0x30000, out, dtype, ctypes.byref(lay) if lay else None,
+                             1.0, 1.0, 1.0, B, C, chunk, None)
+
+
+def test_layout_argument_errors(lib):
+    expected = MISMATCH if _gpu_visible() else NO_DEVICE
+    assert _call_ex(lib, None) == expected                      # contiguous
+    assert _call_ex(lib, _layout()) == expected
+    assert _call_ex(lib, _layout(q_stride_head=-128)) == BAD_ARG
+    assert _call_ex(lib, _layout(kv_stride_row=132)) == BAD_ARG  # rows not 16-byte aligned
+    assert _call_ex(lib, _layout(q_stride_batch=4100)) == BAD_ARG
+    assert _call_ex(lib, _layout(kv_stride_row=64)) == BAD_ARG   # does not cover a row
+    assert "row" in lib.gqa_decode_last_error().decode()
+    # E4M3 rows are 128 B: strides count bytes there
+    assert _call_ex(lib, _layout(kv_stride_row=64), dtype=2) == BAD_ARG
+    assert _call_ex(lib, _layout(kv_stride_row=136), dtype=2) == BAD_ARG
+    assert _call_ex(lib, _layout(kv_stride_row=144), dtype=2) == expected
+    # 32-bit buffer offsets: row stride times capacity
+    assert _call_ex(lib, _layout(kv_stride_row=1 << 20, C=4096), C=4096) == BAD_ARG
+    assert _call_ex(lib, _layout(q_stride_head=1 << 29)) == BAD_ARG
+    # paged caches
+    bt = 0x50000
+    assert _call_ex(lib, _layout(block_table=bt, max_pages=4, page_size=16, num_pages=9)) == expected
+    assert _call_ex(lib, _layout(block_table=bt, max_pages=4, page_size=24, num_pages=9)) == BAD_ARG
+    assert _call_ex(lib, _layout(block_table=bt, max_pages=4, page_size=8, num_pages=9)) == BAD_ARG
+    assert _call_ex(lib, _layout(block_table=bt, max_pages=3, page_size=16, num_pages=9)) == BAD_ARG
+    assert "capacity" in lib.gqa_decode_last_error().decode()
+    assert _call_ex(lib, _layout(block_table=bt, max_pages=4, page_size=16, num_pages=0)) == BAD_ARG
+    assert _call_ex(lib, _layout(block_table=bt + 2, max_pages=4, page_size=16, num_pages=9)) == MISALIGNED
+    # out overlapping q under q's strides, or the block table
+    assert _call_ex(lib, _layout(q_stride_batch=1 << 20), out=0x10000 + (1 << 20)) == ALIAS
+    assert _call_ex(lib, _layout(block_table=0x40000 + 4096, max_pages=4, page_size=16,
+                                 num_pages=9)) == ALIAS
