@@ -169,6 +169,27 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int) 
     ])
 
 
+def _paginate(kv, page_size, seed):
+    """The cache [B, 2, 8, C, 128] as shuffled HND pages [B * C/P, 2, 8, P,
+    128] and its block table [B, C/P] (C padded to a multiple of P)."""
+    import numpy as np
+    import torch
+
+    B, _, H, C, D = kv.shape
+    P = page_size
+    maxp = -(-C // P)
+    raw = kv.view(torch.int16 if kv.element_size() == 2 else torch.uint8)
+    if maxp * P != C:
+        pad = torch.zeros((B, 2, H, maxp * P - C, D), dtype=raw.dtype, device=kv.device)
+        raw = torch.cat([raw, pad], dim=3)
+    ordered = raw.reshape(B, 2, H, maxp, P, D).permute(0, 3, 1, 2, 4, 5).reshape(B * maxp, 2, H, P, D)
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(B * maxp)).to(kv.device)
+    pages = torch.empty_like(ordered)
+    pages[perm] = ordered
+    table = perm.to(torch.int32).reshape(B, maxp).contiguous()
+    return pages.view(kv.dtype), table
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +200,9 @@ def main(argv=None):
                     help="element type: f16 (default), bf16 (q, kv, out), or e4m3 (fp16 q and "
                          "out, FP8 E4M3 kv with per-tensor scales); non-f16 types use the typed "
                          "entry point")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="> 0: read the cache as shuffled HND pages of this many positions "
+                         "(gqa_decode_paged); 0: the contiguous cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -216,11 +240,18 @@ def main(argv=None):
     rot = min(rot, ROTATE_MAX_COPIES, max(1, int(40e9 // (kv0.numel() * kv0.element_size()))))
     kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
     out = torch.empty_like(q)
+    tables = None
+    if args.page_size > 0:
+        kvs, tables = zip(*[_paginate(kv, args.page_size, seed=i) for i, kv in enumerate(kvs)])
     torch.cuda.synchronize()
 
     def step(i):
-        g.gqa_decode(q, kvs[i % rot], lens, out=out, q_scale=w.q_scale, k_scale=w.k_scale,
-                     v_scale=w.v_scale)
+        if tables is not None:
+            g.gqa_decode_paged(q, kvs[i % rot], tables[i % rot], lens, out=out,
+                               q_scale=w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
+        else:
+            g.gqa_decode(q, kvs[i % rot], lens, out=out, q_scale=w.q_scale, k_scale=w.k_scale,
+                         v_scale=w.v_scale)
 
     for i in range(args.warmup):
         step(i)
@@ -298,6 +329,8 @@ def main(argv=None):
             "batch": w.batch, "capacity": w.capacity, "q_heads": 32, "kv_heads": 8,
             "head_dim": 128, "sum_valid_len": sum_len, "kv_bytes_per_step": kv_bytes,
             "kv_copies_rotated": rot, "accumulate": "f32",
+            "kv_layout": (f"paged, {args.page_size} positions per page, shuffled"
+                          if args.page_size > 0 else "contiguous"),
         },
         "kernel_us": {"pieces": round(pieces_us, 3), "combine": round(combine_us, 3),
                       "sum": round(pieces_us + combine_us, 3)},
