@@ -236,34 +236,57 @@ __device__ void locate(long long p, const Params& P, long long* red, long long* 
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips): within each 16-lane row by shifts of
+// 1, 2, 4 and 8, then row 0's total into rows 1 and 3 (row_bcast:15) and
+// rows 0-1's total into rows 2 and 3 (row_bcast:31). Lanes whose source is
+// outside the row, or disabled by the row mask, add 0.
+__device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+// Piece length Q for this call (total < 2^32: 32-bit division).
+__device__ __forceinline__ long long piece_len32(const Params& P, unsigned total) {
+  if (P.forced_piece > 0) return P.forced_piece;
+  unsigned Q = total / (unsigned)P.pieces + (total % (unsigned)P.pieces != 0);
+  Q = Q < (unsigned)P.min_piece ? (unsigned)P.min_piece : Q;
+  return cost_len(P, Q);
+}
+
 // Small batches (<= 64): every wave finds the total and the batch entry of
-// flat row p on its own (lane b holds sequence b), with no workgroup barrier.
-// Returns the total cost; *found_b = -1 if p is past it. *lens_v
-// keeps the clamped lengths (lane b holds sequence b's), so later segment
-// steps read them with readlane instead of a dependent memory load.
-__device__ long long wave_plan(const Params& P, long long (*piece_start)(const Params&, long long),
-                               long long* p_out, long long* found, int* found_b, int* lens_v) {
+// this workgroup's first cost position on its own (lane b holds sequence b),
+// with no workgroup barrier and no LDS traffic. The total fits 32 bits: at
+// most 64 * 8 * (2^22 + 16 + c0) units. Returns the total; *found_b = -1 if
+// the piece starts past it. *lens_v keeps the clamped lengths (lane b holds
+// sequence b's), so later segment steps read them with readlane instead of a
+// dependent memory load.
+__device__ long long wave_plan(const Params& P, long long* p_out, long long* q_out,
+                               long long* found, int* found_b, int* lens_v) {
   const int lane = threadIdx.x & 63;
   const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
   *lens_v = (int)len;
-  const long long cost = seq_cost(P, len);
-  long long incl = cost;
-  for (int o = 1; o < 64; o <<= 1) {
-    const long long t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  const long long total = __shfl(incl, 63);
-  const long long p = piece_start(P, total);
+  const unsigned cost = (unsigned)seq_cost(P, len);
+  const unsigned incl = wave_incl_scan(cost);
+  const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
+  const long long Q = piece_len32(P, total);
+  const long long p = (long long)blockIdx.x * Q;
   *p_out = p;
-  const long long lo = incl - cost;
-  const unsigned long long hit = __ballot(cost > 0 && p >= lo && p < incl);
+  *q_out = Q;
+  const long long lo = (long long)(incl - cost);
+  const unsigned long long hit = __ballot(cost > 0 && p >= lo && p < (long long)incl);
   if (hit == 0) {
     *found_b = -1;
     return total;
   }
   const int b = __ffsll((long long)hit) - 1;
   *found_b = b;
-  *found = __shfl(lo, b);
+  *found = (unsigned)__builtin_amdgcn_readlane((int)(incl - cost), b);
   return total;
 }
 
@@ -918,11 +941,11 @@ void gqa_decode_pieces(Params P) {
   const int G = lane >> 4, j = lane & 15;
   const int w = blockIdx.x;
 
-  long long total, p0, found;
+  long long total, p0, found, Qw = 0;
   int found_b, found_len = 0;
   int lens_v = 0;
   if (P.batch <= 64) {
-    total = wave_plan(P, this_piece_start, &p0, &found, &found_b, &lens_v);
+    total = wave_plan(P, &p0, &Qw, &found, &found_b, &lens_v);
   } else {
     long long part = 0;
     for (int b = tid; b < P.batch; b += kThreads)
@@ -946,7 +969,7 @@ void gqa_decode_pieces(Params P) {
   }
   found = uniform64(found);
   found_b = __builtin_amdgcn_readfirstlane(found_b);
-  const long long Q = piece_len(P, total);
+  const long long Q = P.batch <= 64 ? uniform64(Qw) : piece_len(P, total);
   const long long p1 = p0 + Q < total ? p0 + Q : total;
 
   Seg s;
@@ -954,7 +977,10 @@ void gqa_decode_pieces(Params P) {
   s.len = P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, s.b)
                         : __builtin_amdgcn_readfirstlane(found_len);
   const long long stride = cost_len(P, s.len) + P.seg_cost;
-  s.g = (int)((p0 - found) / stride);
+  // (p0 - found) / stride, which is below 8: by comparison, no division
+  const long long rel = p0 - found;
+  s.g = 0;
+  while (s.g < kKvHeads - 1 && (long long)(s.g + 1) * stride <= rel) ++s.g;
   s.off = found + (long long)s.g * stride + P.seg_cost;
   seg_set_range(s, p0, p1);
   if (s.hi <= s.lo) {                               // only fixed-cost units in this piece
