@@ -1,0 +1,105 @@
+"""The decode inside HIP graphs and on concurrent streams.
+
+A captured graph holds only kernel nodes (the host never reads the lengths
+and the workspace exists before capture), so every replay must reproduce the
+eager result bitwise, also with other eager work and synchronisations
+between replays and with lengths changed on the device between replays.
+Two streams decoding at once use separate workspaces and must not disturb
+each other.
+"""
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _g():
+    import gqa_token_decode_amd as g
+    return g
+
+
+def _bits(t):
+    torch = _torch()
+    return t.view(torch.int16).cpu().numpy()
+
+
+@pytest.mark.parametrize("elem", ["f16", "e4m3"])
+def test_graph_replays_match_eager_bitwise(elem):
+    torch = _torch()
+    g = _g()
+    ws = [workloads.build(f"graph {elem} {i}", 90 + i, 2048, lens, elem=elem)
+          for i, lens in enumerate([[2048, 5, 700], [1, 1500, 33], [0, 64, 2048]])]
+    qs = [w.q_to_device(DEV) for w in ws]
+    kvs = [w.kv_to_device(DEV) for w in ws]
+    lens = [torch.from_numpy(w.seq_lens).to(DEV) for w in ws]
+    outs = [torch.empty_like(q) for q in qs]
+
+    def calls():
+        for w, q, kv, ln, o in zip(ws, qs, kvs, lens, outs):
+            g.gqa_decode(q, kv, ln, out=o, q_scale=w.q_scale, k_scale=w.k_scale,
+                         v_scale=w.v_scale)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()                        # eager on the capture stream: creates its workspace
+    s.synchronize()
+    eager = [_bits(o) for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()      # unrelated eager work
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for i, o in enumerate(outs):
+            assert np.array_equal(_bits(o), eager[i]), f"replay {rep}, call {i}"
+    # lengths live on the device: change them in place and replay
+    lens[0].copy_(torch.tensor([3, 2048, 0], dtype=torch.int32))
+    graph.replay()
+    torch.cuda.synchronize()
+    w2 = workloads.build("graph relen", 90, 2048, [2048, 5, 700], elem=elem)
+    q2, kv2 = w2.q_to_device(DEV), w2.kv_to_device(DEV)
+    ref = g.gqa_decode(q2, kv2, torch.tensor([3, 2048, 0], dtype=torch.int32, device=DEV),
+                       q_scale=w2.q_scale, k_scale=w2.k_scale, v_scale=w2.v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(outs[0]), _bits(ref))
+
+
+def test_two_streams_decode_concurrently():
+    torch = _torch()
+    g = _g()
+    a = workloads.get("b8_c4096_nanfill")
+    b = workloads.build("stream b", 95, 8192, [8192, 100, 4000, 1, 7000, 3, 8000, 2], elem="f16")
+    qa, kva, la = a.q_to_device(DEV), a.kv_to_device(DEV), torch.from_numpy(a.seq_lens).to(DEV)
+    qb, kvb, lb = b.q_to_device(DEV), b.kv_to_device(DEV), torch.from_numpy(b.seq_lens).to(DEV)
+    ref_a = _bits(g.gqa_decode(qa, kva, la))
+    ref_b = _bits(g.gqa_decode(qb, kvb, lb))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs_a, outs_b = [], []
+    for _ in range(10):
+        with torch.cuda.stream(s1):
+            outs_a.append(g.gqa_decode(qa, kva, la))
+        with torch.cuda.stream(s2):
+            outs_b.append(g.gqa_decode(qb, kvb, lb))
+    torch.cuda.synchronize()
+    for oa, ob in zip(outs_a, outs_b):
+        assert np.array_equal(_bits(oa), ref_a)
+        assert np.array_equal(_bits(ob), ref_b)
