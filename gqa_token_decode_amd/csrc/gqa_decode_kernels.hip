@@ -1045,72 +1045,79 @@ void gqa_decode_pieces(Params P) {
 }
 
 // ---------------------------------------------------------------- kernel 2
-constexpr int kCombineSubsets = kThreads / 32;   // 8 subsets x 32 four-column groups
+constexpr int kCombineSubsets = 4;   // x 64 (head, 8-column group) pairs = 256 threads
 
-// One workgroup per (b, query head): if kernel 1 cut the segment (b, h / 4)
-// into several pieces, merge their partials for head h and write the output
-// row; otherwise exit. Each of 8 thread subsets merges every 8th partial
-// with a running max (its loads do not depend on each other), then the
-// subsets are merged through LDS.
+// One workgroup per segment (b, g): if kernel 1 cut it into several pieces,
+// merge their partials for the group's 4 query heads and write the output
+// rows; otherwise exit. Thread t takes head (t / 16) % 4, columns
+// 8 * (t % 16) .. +7, and every 4th partial from t / 64: a running max over
+// independent loads. The 4 subsets are then merged through LDS, in a fixed
+// order, so results do not depend on timing. (One workgroup per segment
+// rather than per query head: 4x fewer waves to dispatch for large batches,
+// where most segments are not cut and their workgroups exit at once.)
 template <int F>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
   constexpr bool kBf16 = F == kFmtBf16;
-  __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][32][6];
+  __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][64][10];
 
   const int tid = threadIdx.x;
-  const int b = blockIdx.x / kQHeads, head = blockIdx.x - b * kQHeads;
-  const int g = head / kGroup, hh = head - g * kGroup;
-  const int2 desc = P.seg_desc[b * kKvHeads + g];
+  const int seg = blockIdx.x, b = seg / kKvHeads, g = seg - b * kKvHeads;
+  const int2 desc = P.seg_desc[seg];
   const int n = desc.y >> 1;
-  if (n <= 1) return;                  // empty (zero row) or finished by kernel 1
+  if (n <= 1) return;                  // empty (zero rows) or finished by kernel 1
   const int first_w = desc.x;
   // Partial i lives in piece first_w + i: the first piece may hold it in its
   // second slot, every later piece holds it as its first segment.
   const long long slot0 = 2LL * first_w + (desc.y & 1);
 
-  const int sub = tid >> 5, c4 = (tid & 31) * 4;
+  const int pair = tid & 63, sub = tid >> 6;
+  const int hh = pair >> 4, c8 = (pair & 15) * 8;
   const float kNegInf = -__builtin_inff();
   float M = kNegInf, den = 0.f;
-  float4_t num = {0.f, 0.f, 0.f, 0.f};
+  float4_t na = {0.f, 0.f, 0.f, 0.f}, nb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
   for (int i = sub; i < n; i += kCombineSubsets) {
     const long long sl = i == 0 ? slot0 : 2LL * (first_w + i);
     const float2 ml = P.ws_ml[sl * kGroup + hh];
-    const float4_t a = *reinterpret_cast<const float4_t*>(P.ws_acc + (sl * kGroup + hh) * kDim + c4);
+    const float* src = P.ws_acc + (sl * kGroup + hh) * kDim + c8;
+    const float4_t a0 = *reinterpret_cast<const float4_t*>(src);
+    const float4_t a1 = *reinterpret_cast<const float4_t*>(src + 4);
     const float Mn = fmaxf(M, ml.x);
     const float s_old = exp2_hw(M - Mn), s_new = exp2_hw(ml.x - Mn);
     den = den * s_old + ml.y * s_new;
-    num = num * s_old + a * s_new;
+    na = na * s_old + a0 * s_new;
+    nb = nb * s_old + a1 * s_new;
     M = Mn;
   }
-  float* x = xs[sub][tid & 31];
+  float* x = xs[sub][pair];
   x[0] = M;
   x[1] = den;
-  x[2] = num[0];
-  x[3] = num[1];
-  x[4] = num[2];
-  x[5] = num[3];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 + k] = na[k];
+    x[6 + k] = nb[k];
+  }
   __syncthreads();
-  if (tid < 32) {
+  if (tid < 64) {
     float Mx = kNegInf;
 #pragma unroll
-    for (int k = 0; k < kCombineSubsets; ++k) Mx = fmaxf(Mx, xs[k][tid][0]);
-    float d = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int k = 0; k < kCombineSubsets; ++k) Mx = fmaxf(Mx, xs[k][pair][0]);
+    float d = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kCombineSubsets; ++k) {
-      const float* y = xs[k][tid];
+      const float* y = xs[k][pair];
       const float wt = (y[0] == kNegInf) ? 0.f : exp2_hw(y[0] - Mx);   // subsets without partials
       d += wt * y[1];
-      o0 += wt * y[2];
-      o1 += wt * y[3];
-      o2 += wt * y[4];
-      o3 += wt * y[5];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] += wt * y[2 + c];
     }
     const float vs = P.out_scale;
-    uint2 o;
-    o.x = (unsigned)to_elem<kBf16>(o0 / d * vs) | ((unsigned)to_elem<kBf16>(o1 / d * vs) << 16);
-    o.y = (unsigned)to_elem<kBf16>(o2 / d * vs) | ((unsigned)to_elem<kBf16>(o3 / d * vs) << 16);
-    *reinterpret_cast<uint2*>(P.out + ((size_t)b * kQHeads + head) * kDim + 4 * tid) = o;
+    uint4_t r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      r[c] = (unsigned)to_elem<kBf16>(o[2 * c] / d * vs) |
+             ((unsigned)to_elem<kBf16>(o[2 * c + 1] / d * vs) << 16);
+    *reinterpret_cast<uint4_t*>(P.out + ((size_t)b * kQHeads + g * kGroup + hh) * kDim + c8) = r;
   }
 }
 
@@ -1154,7 +1161,7 @@ template <int F, bool kPaged>
 hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
                           hipEvent_t* events) {
   hipError_t err = hipSuccess;
-  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * kQHeads)), block(kThreads);
+  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * kKvHeads)), block(kThreads);
   if (events) {
     // Start/stop events attached to the dispatches: they time each kernel's
     // execution without extra packets between the kernels.
