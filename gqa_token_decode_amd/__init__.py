@@ -77,6 +77,8 @@ def load_library():
     lib.gqa_decode_status_string.restype = ctypes.c_char_p
     lib.gqa_decode_last_error.argtypes = []
     lib.gqa_decode_last_error.restype = ctypes.c_char_p
+    lib.gqa_decode_set_launch_form.argtypes = [i32]
+    lib.gqa_decode_set_launch_form.restype = i32
     lib.gqa_decode_profile_begin.argtypes = []
     lib.gqa_decode_profile_begin.restype = i32
     dp = ctypes.POINTER(ctypes.c_double)
@@ -277,6 +279,22 @@ def workspace_bytes(batch: int, capacity: int) -> int:
 
 def release_workspace() -> None:
     load_library().gqa_decode_release_workspace()
+
+
+_LAUNCH_FORMS = {"auto": 0, "single": 1, "two": 2}
+
+
+def set_launch_form(form: str) -> None:
+    """Select how later calls run the combine step: "single" (one kernel; the
+    last workgroup of each cut segment merges it), "two" (pieces kernel, then
+    combine kernel) or "auto" (single launch for capacities up to 512 with at
+    most 16384 cache rows in all). The forms return the same bits."""
+    if form not in _LAUNCH_FORMS:
+        raise ValueError(f"launch form must be one of {sorted(_LAUNCH_FORMS)}, got {form!r}")
+    lib = load_library()
+    st = lib.gqa_decode_set_launch_form(_LAUNCH_FORMS[form])
+    if st != 0:
+        _raise(lib, st)
 
 
 class KernelTimer:

@@ -54,19 +54,26 @@ struct DeviceInfo {
   std::string arch;
 };
 
-// fp32 partial results, cached per (device, stream).
+// fp32 partial results, cached per (device, stream), and the single-launch
+// form's per-segment tickets (zeroed once when allocated; every call leaves
+// them zero).
 struct Workspace {
   int device;
   hipStream_t stream;
   void* ptr;
   size_t bytes;
+  int* tickets;
+  size_t ticket_bytes;
 };
 
 struct ProfileRecord {
   hipEvent_t ev[4];   // pieces start, stop; combine start, stop
+  bool two_kernels;   // the combine events were recorded (two-launch form)
 };
 
 std::mutex g_mu;
+// gqa_launch_form of later calls (guarded by g_mu).
+int g_launch_form = -1;   // -1: not yet read from the environment
 std::vector<DeviceInfo> g_devices;
 std::vector<Workspace> g_workspaces;
 bool g_profiling = false;
@@ -149,7 +156,7 @@ void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
     if (w.device == dev && w.stream == stream) ws = &w;
   if (ws && ws->bytes >= bytes) return ws->ptr;
   if (!ws) {
-    g_workspaces.push_back(Workspace{dev, stream, nullptr, 0});
+    g_workspaces.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0});
     ws = &g_workspaces.back();
   }
   if (ws->ptr) {
@@ -171,6 +178,52 @@ void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
   }
   ws->bytes = bytes;
   return ws->ptr;
+}
+
+// Ticket array of at least `count` ints for (dev, stream), all zero. Only
+// allocated and cleared outside graph capture (a captured memset node is not
+// used here), so the first call on a stream must be eager. Caller holds g_mu
+// and has made `dev` current; the workspace entry exists.
+int* get_tickets(int dev, hipStream_t stream, size_t count, int* status) {
+  Workspace* ws = nullptr;
+  for (Workspace& w : g_workspaces)
+    if (w.device == dev && w.stream == stream) ws = &w;
+  const size_t bytes = (count * sizeof(int) + 255) & ~(size_t)255;
+  if (ws && ws->ticket_bytes >= bytes) return ws->tickets;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (!ws || hipStreamIsCapturing(stream, &cap) != hipSuccess ||
+      cap != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    *status = fail(GQA_ERR_ALLOC,
+                   "gqa_decode: the first call with this batch size on a stream must run "
+                   "outside graph capture");
+    return nullptr;
+  }
+  if (ws->tickets) {
+    const bool ok = hipStreamSynchronize(stream) == hipSuccess && hipFree(ws->tickets) == hipSuccess;
+    ws->tickets = nullptr;
+    ws->ticket_bytes = 0;
+    if (!ok) {
+      (void)hipGetLastError();
+      *status = fail(GQA_ERR_LAUNCH, "gqa_decode: could not release the old ticket array");
+      return nullptr;
+    }
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu ticket bytes failed", bytes);
+    return nullptr;
+  }
+  if (hipMemsetAsync(p, 0, bytes, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(p);
+    *status = fail(GQA_ERR_LAUNCH, "gqa_decode: clearing the ticket array failed");
+    return nullptr;
+  }
+  ws->tickets = static_cast<int*>(p);
+  ws->ticket_bytes = bytes;
+  return ws->tickets;
 }
 
 // Strides resolved to bytes, with the address range each of q and kv spans.
@@ -335,7 +388,15 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
                   chunk_len, batch, capacity, pbytes);
       } else {
         void* ws = get_workspace(dev, stream, pbytes, &st);
-        if (ws) {
+        if (g_launch_form < 0)
+          g_launch_form = env_int("GQA_DECODE_LAUNCH_FORM", GQA_LAUNCH_AUTO, 0, 2);
+        const bool single = g_launch_form == GQA_LAUNCH_SINGLE ||
+                            (g_launch_form == GQA_LAUNCH_AUTO &&
+                             capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY &&
+                             (long long)batch * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS);
+        int* tickets = nullptr;
+        if (ws && single) tickets = get_tickets(dev, stream, (size_t)batch * 8, &st);
+        if (ws && (tickets || !single)) {
           // Scores are formed as dot * q_scale * k_scale / sqrt(128) * log2(e),
           // so the kernel can use the hardware base-2 exponential.
           const double scale = (double)q_scale * (double)k_scale /
@@ -350,14 +411,18 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
               for (int i = 0; i < 4; ++i) ok = ok && hipEventCreate(&rec.ev[i]) == hipSuccess;
               if (ok) g_profile.push_back(rec);
             }
-            if (g_profile_used < g_profile.size()) ev = g_profile[g_profile_used++].ev;
+            if (g_profile_used < g_profile.size()) {
+              ProfileRecord& rec = g_profile[g_profile_used++];
+              rec.two_kernels = !single;
+              ev = rec.ev;
+            }
           }
           const gqa::ElemType elem = dtype == GQA_DTYPE_BF16      ? gqa::ElemType::kBf16
                                      : dtype == GQA_DTYPE_E4M3_KV ? gqa::ElemType::kE4m3Kv
                                                                   : gqa::ElemType::kF16;
           const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, elem, res.lay,
                                                   (float)scale, v_scale, batch, capacity, cfg,
-                                                  grid, ws, stream, ev);
+                                                  grid, ws, tickets, stream, ev);
           if (e != hipSuccess)
             st = fail(GQA_ERR_LAUNCH, "gqa_decode: kernel launch failed: %s", hipGetErrorString(e));
         }
@@ -420,11 +485,20 @@ void gqa_decode_release_workspace(void) {
     if (hipSetDevice(w.device) == hipSuccess) {
       (void)hipDeviceSynchronize();
       (void)hipFree(w.ptr);
+      if (w.tickets) (void)hipFree(w.tickets);
     }
   }
   g_workspaces.clear();
   if (prev >= 0) (void)hipSetDevice(prev);
   (void)hipGetLastError();
+}
+
+int gqa_decode_set_launch_form(int form) {
+  if (form < GQA_LAUNCH_AUTO || form > GQA_LAUNCH_TWO)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode_set_launch_form: unknown form %d", form);
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_launch_form = form;
+  return GQA_OK;
 }
 
 const char* gqa_decode_status_string(int status) {
@@ -460,9 +534,9 @@ int gqa_decode_profile_end(double* pieces_ms, double* combine_ms, int* calls) {
   for (size_t i = 0; i < g_profile_used; ++i) {
     const ProfileRecord& r = g_profile[i];
     float a = 0.f, c = 0.f;
-    if (hipEventSynchronize(r.ev[3]) != hipSuccess ||
+    if (hipEventSynchronize(r.ev[r.two_kernels ? 3 : 1]) != hipSuccess ||
         hipEventElapsedTime(&a, r.ev[0], r.ev[1]) != hipSuccess ||
-        hipEventElapsedTime(&c, r.ev[2], r.ev[3]) != hipSuccess) {
+        (r.two_kernels && hipEventElapsedTime(&c, r.ev[2], r.ev[3]) != hipSuccess)) {
       (void)hipGetLastError();
       st = fail(GQA_ERR_LAUNCH, "gqa_decode_profile_end: event query failed");
     } else {

@@ -101,6 +101,9 @@ struct Params {
   float2* ws_ml;       // [2 * grid][4] (max, denominator) per partial and head
   float* ws_acc;       // [2 * grid][4][128] unnormalised weighted V sums
   int2* seg_desc;      // [8 * batch] per segment: first piece, 2 * pieces + second-slot bit
+  int* tickets;        // [8 * batch] single launch: pieces of each segment done so far
+                       // (zero between calls: the last piece resets its count)
+  int fused;           // 1: the last piece of a cut segment merges its partials
   int batch;
   int capacity;
   int pieces;          // automatic split: number of equal pieces
@@ -405,6 +408,21 @@ __device__ __forceinline__ long long page_base(const Params& P, int b, int i) {
   return (page >= 0 && page < P.num_pages) ? (long long)page * P.kv_sb : -1;
 }
 
+// Byte offsets of the pages holding rows t and t + 16 of a tile of segment
+// s (-1: no rows there, or an invalid page id). Unused for contiguous caches.
+struct PageBases {
+  long long p0 = -1, p1 = -1;
+};
+
+template <int kRows>
+__device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, int t, bool live) {
+  PageBases pb;
+  const int nrows = live ? s.hi - t : 0;
+  if (nrows > 0) pb.p0 = page_base(P, s.b, t);
+  if (kRows == 32 && nrows > 16) pb.p1 = page_base(P, s.b, t + 16);
+  return pb;
+}
+
 // Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
 // an LDS stage (K, then V) and the segment's 4 query rows into the wave's q
 // slot, in this order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros.
@@ -415,10 +433,11 @@ __device__ __forceinline__ long long page_base(const Params& P, int b, int i) {
 // slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
 // rows of 128 B (E4M3). In LDS the rows are dense whatever the strides.
 // Paged caches (page size a multiple of 16): each 16-row half of a tile
-// lies in one page.
+// lies in one page, whose offset the caller passes in pb.
 template <int F, bool kPaged>
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
-                                           bool live_q, e16_t* stage, e16_t* qslot) {
+                                           bool live_q, e16_t* stage, e16_t* qslot,
+                                           const PageBases& pb) {
   constexpr int kRowBytes = row_bytes<F>();
   constexpr int kRows = tile_rows<F>();
   const int lane = threadIdx.x & 63;
@@ -435,12 +454,8 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
   // holding logical chunk (l%8) ^ swz8(row). Both swizzles are their own
   // inverse.
   char* st = reinterpret_cast<char*>(stage);
-  // Paged: byte offsets of the pages holding rows t and t + 16 (-1: none).
-  long long pb0 = -1, pb1 = -1;
-  if constexpr (kPaged) {
-    pb0 = nrows > 0 ? page_base(P, s.b, t) : -1;
-    if constexpr (kRows == 32) pb1 = nrows > 16 ? page_base(P, s.b, t + 16) : -1;
-  }
+  // Paged: pb holds the byte offsets of the pages of rows t and t + 16.
+  const long long pb0 = pb.p0, pb1 = pb.p1;
 #pragma unroll
   for (int kind = 0; kind < 2; ++kind) {
     __amdgpu_buffer_rsrc_t r0, r1;   // rows [0, 16) and [16, 32) of the tile
@@ -824,13 +839,13 @@ template <int F, bool kPaged>
 __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, int par,
                                           e16_t* nxt, e16_t* qslot, bool first,
                                           bool has_next, const Seg& nseg, int nt,
-                                          bool next_new_seg, int t, int hi, uint4_t (&qb)[4],
-                                          WaveAcc& acc) {
+                                          bool next_new_seg, const PageBases& npb, int t, int hi,
+                                          uint4_t (&qb)[4], WaveAcc& acc) {
   if (first) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
     read_q(qslot, qb);
   }
-  issue_tile<F, kPaged>(P, nseg, nt, has_next, next_new_seg, nxt, qslot);
+  issue_tile<F, kPaged>(P, nseg, nt, has_next, next_new_seg, nxt, qslot, npb);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
   if constexpr (F == kFmtE4m3)
     compute_tile8(la, par, qb, t, hi, P.scale_log2, acc);
@@ -918,8 +933,128 @@ __device__ __forceinline__ void zero_empty_sequences(const Params& P, int lens_v
       uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * kQHeads * kDim);
       dst[tid] = (uint4_t){0u, 0u, 0u, 0u};
       dst[tid + kThreads] = (uint4_t){0u, 0u, 0u, 0u};
-      if (tid < kKvHeads) P.seg_desc[b * kKvHeads + tid] = make_int2(0, 0);
+      if (!P.fused && tid < kKvHeads) P.seg_desc[b * kKvHeads + tid] = make_int2(0, 0);
     }
+  }
+}
+
+// ---------------------------------------------------------------- combine
+// Partial results of the single-launch form are written and read as
+// device-scope (agent) relaxed atomics: each access is then coherent across
+// the XCDs' L2 caches by itself (the stores write through to memory, the
+// loads do not hit stale L2 lines), so no L2 write-back or invalidate is
+// needed around the ticket. Ordering: the writer waits for its stores to
+// complete before its ticket is taken, and the merging workgroup issues its
+// loads only after its ticket has returned.
+__device__ __forceinline__ void store_partial(float2* p, float2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 load_partial(const float2* p) {
+  return __builtin_bit_cast(
+      float2, __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT));
+}
+
+constexpr int kCombineSubsets = 4;   // x 64 (head, 8-column group) pairs = 256 threads
+
+struct CombineLds {
+  float xs[kCombineSubsets][64][10];
+};
+
+// Merge the n partials of segment (b, g), which kernel 1 cut into pieces
+// first_w .. first_w + n - 1, and write the group's 4 output rows. All 256
+// threads take part. Thread t takes head (t / 16) % 4, columns 8 * (t % 16)
+// .. +7, and every 4th partial from t / 64: a running max over independent
+// loads. The 4 subsets are then merged through LDS, in a fixed order, so
+// results do not depend on timing or on which workgroup runs the merge.
+// Partial i lives in piece first_w + i: the first piece holds it in its
+// second slot if the segment starts inside that piece (bit), every later
+// piece holds it as its first segment.
+// kCoherent: the partials were written in this launch (single-launch form)
+// and are read with device-scope loads.
+template <bool kBf16, bool kCoherent>
+__device__ __forceinline__ void combine_segment(const Params& P, int b, int g, int first_w, int n,
+                                                int bit, CombineLds& lds) {
+  const int tid = threadIdx.x;
+  const long long slot0 = 2LL * first_w + bit;
+  const int pair = tid & 63, sub = tid >> 6;
+  const int hh = pair >> 4, c8 = (pair & 15) * 8;
+  const float kNegInf = -__builtin_inff();
+  float M = kNegInf, den = 0.f;
+  float4_t na = {0.f, 0.f, 0.f, 0.f}, nb = {0.f, 0.f, 0.f, 0.f};
+  // Partials sub, sub + 4, ... in batches of kBatch: a batch's loads are all
+  // issued before its first use, then merged one by one in index order.
+  constexpr int kBatch = 4;
+  for (int i0 = sub; i0 < n; i0 += kBatch * kCombineSubsets) {
+    float2 ml[kBatch];
+    float4_t a0[kBatch], a1[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kCombineSubsets;
+      if (i >= n) break;
+      const long long sl = i == 0 ? slot0 : 2LL * (first_w + i);
+      const float* src = P.ws_acc + (sl * kGroup + hh) * kDim + c8;
+      if constexpr (kCoherent) {
+        ml[u] = load_partial(P.ws_ml + sl * kGroup + hh);
+        const float2* s2 = reinterpret_cast<const float2*>(src);
+        const float2 x0 = load_partial(s2), x1 = load_partial(s2 + 1);
+        const float2 x2 = load_partial(s2 + 2), x3 = load_partial(s2 + 3);
+        a0[u] = (float4_t){x0.x, x0.y, x1.x, x1.y};
+        a1[u] = (float4_t){x2.x, x2.y, x3.x, x3.y};
+      } else {
+        ml[u] = P.ws_ml[sl * kGroup + hh];
+        a0[u] = *reinterpret_cast<const float4_t*>(src);
+        a1[u] = *reinterpret_cast<const float4_t*>(src + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (i0 + u * kCombineSubsets >= n) break;
+      // Explicit fused multiply-adds: the same operations wherever this
+      // function is inlined (the two launch forms must agree bitwise).
+      const float Mn = fmaxf(M, ml[u].x);
+      const float s_old = exp2_hw(M - Mn), s_new = exp2_hw(ml[u].x - Mn);
+      den = __builtin_fmaf(den, s_old, ml[u].y * s_new);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        na[k] = __builtin_fmaf(na[k], s_old, a0[u][k] * s_new);
+        nb[k] = __builtin_fmaf(nb[k], s_old, a1[u][k] * s_new);
+      }
+      M = Mn;
+    }
+  }
+  float* x = lds.xs[sub][pair];
+  x[0] = M;
+  x[1] = den;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 + k] = na[k];
+    x[6 + k] = nb[k];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float Mx = kNegInf;
+#pragma unroll
+    for (int k = 0; k < kCombineSubsets; ++k) Mx = fmaxf(Mx, lds.xs[k][pair][0]);
+    float d = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kCombineSubsets; ++k) {
+      const float* y = lds.xs[k][pair];
+      const float wt = (y[0] == kNegInf) ? 0.f : exp2_hw(y[0] - Mx);   // subsets without partials
+      d = __builtin_fmaf(wt, y[1], d);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] = __builtin_fmaf(wt, y[2 + c], o[c]);
+    }
+    const float vs = P.out_scale;
+    uint4_t r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      r[c] = (unsigned)to_elem<kBf16>(o[2 * c] / d * vs) |
+             ((unsigned)to_elem<kBf16>(o[2 * c + 1] / d * vs) << 16);
+    *reinterpret_cast<uint4_t*>(P.out + ((size_t)b * kQHeads + g * kGroup + hh) * kDim + c8) = r;
   }
 }
 
@@ -934,7 +1069,13 @@ void gqa_decode_pieces(Params P) {
   __shared__ int sh_found_b, sh_found_len;
   __shared__ __attribute__((aligned(16))) e16_t stages[kWaves][2][kStageHalves];
   __shared__ __attribute__((aligned(16))) e16_t qslots[kWaves][kQHalves];
-  __shared__ __attribute__((aligned(16))) MergeLds sm;
+  // The wave merge and the single-launch combine use the same LDS.
+  __shared__ __attribute__((aligned(16))) union {
+    MergeLds merge;
+    CombineLds combine;
+  } tail;
+  __shared__ int sh_last[2];
+  __shared__ int sh_cut[2][3];   // single launch: (8 * b + g, first piece, n2) of cut segments
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
@@ -996,9 +1137,14 @@ void gqa_decode_pieces(Params P) {
   Seg pf = s;
   int pt = s.lo + kRows * wv;
   const bool pf_ok = tile_first<kRows>(P, pf, pt, p1, wv, lens_v);
-  issue_tile<F, kPaged>(P, pf, pt, pf_ok, true, st0, qslot);
+  PageBases pbs;                                    // paged: pages of the issued tile
+  if constexpr (kPaged) pbs = page_bases<kRows>(P, pf, pt, pf_ok);
+  issue_tile<F, kPaged>(P, pf, pt, pf_ok, true, st0, qslot, pbs);
   zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
+  // Single launch: the number of segments this piece cut (at most its first
+  // and its last); sh_cut keeps them (in LDS, off the loop's registers).
+  int ncut = 0;
 
   while (true) {
     WaveAcc acc;
@@ -1012,22 +1158,25 @@ void gqa_decode_pieces(Params P) {
       Seg nf = pf;
       int nt = pt;
       const bool n_ok = tile_next<kRows>(P, nf, nt, p1, wv, lens_v);
+      if constexpr (kPaged) pbs = page_bases<kRows>(P, nf, nt, n_ok);
       tile_step<F, kPaged>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
-                nf.off != s.off, t, s.hi, qb, acc);
+                nf.off != s.off, pbs, t, s.hi, qb, acc);
       pf = nf;
       pt = nt;
       par ^= 1;
     }
 
     float M, den, n0, n1;
-    merge_waves(acc, sm, M, den, n0, n1);
+    merge_waves(acc, tail.merge, M, den, n0, n1);
     const int hh = tid >> 6, d = (tid & 63) * 2;
 
     const long long seg_end = s.off + s.len;
     const long long first_w = s.off / Q, last_w = (seg_end - 1) / Q;
-    if (first_w == w && tid == 0)                    // the segment starts in this piece
-      P.seg_desc[s.b * kKvHeads + s.g] =
-          make_int2(w, (int)(2 * (last_w - first_w + 1)) + (s.off > p0 ? 1 : 0));
+    // 2 * (pieces holding rows of the segment) + (it starts inside its first
+    // piece, whose second slot then holds its partial)
+    const int n2 = (int)(2 * (last_w - first_w + 1)) + (s.off > first_w * Q ? 1 : 0);
+    if (!P.fused && first_w == w && tid == 0)        // the segment starts in this piece
+      P.seg_desc[s.b * kKvHeads + s.g] = make_int2(w, n2);
     if (first_w == last_w) {                         // the segment lies in this piece
       const float vs = P.out_scale;
       const unsigned o = (unsigned)to_elem<kBf16>(n0 / den * vs) |
@@ -1035,90 +1184,73 @@ void gqa_decode_pieces(Params P) {
       *reinterpret_cast<unsigned*>(P.out + ((size_t)s.b * kQHeads + s.g * kGroup + hh) * kDim + d) = o;
     } else {
       const long long slot = slot_of(s.off, p0, w);
-      *reinterpret_cast<float2*>(P.ws_acc + (slot * kGroup + hh) * kDim + d) = make_float2(n0, n1);
-      if (d == 0) P.ws_ml[slot * kGroup + hh] = make_float2(M, den);
+      float2* acc_dst = reinterpret_cast<float2*>(P.ws_acc + (slot * kGroup + hh) * kDim + d);
+      float2* ml_dst = P.ws_ml + slot * kGroup + hh;
+      if (P.fused) {
+        store_partial(acc_dst, make_float2(n0, n1));
+        if (d == 0) store_partial(ml_dst, make_float2(M, den));
+      } else {
+        *acc_dst = make_float2(n0, n1);
+        if (d == 0) *ml_dst = make_float2(M, den);
+      }
+      if (P.fused && tid == 0) {
+        sh_cut[ncut][0] = s.b * kKvHeads + s.g;
+        sh_cut[ncut][1] = (int)first_w;
+        sh_cut[ncut][2] = n2;
+      }
+      ++ncut;
     }
 
     if (!more_segments(P, s, p1)) break;
     seg_next(P, s, p1, lens_v);
   }
+
+  // Single launch: take a ticket for each cut segment; the piece that
+  // completes a segment merges its partials (in the same fixed order as the
+  // combine kernel, so both forms give the same bits). Tickets are taken
+  // after all of this piece's segments, so the pipeline never waits on them.
+  if (P.fused && ncut > 0) {
+    // Every wave's partial stores (device-scope) complete before the
+    // tickets are taken.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid < ncut) {
+      const int seg = sh_cut[tid][0], n = sh_cut[tid][2] >> 1;
+      const int done = __hip_atomic_fetch_add(P.tickets + seg, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = done == n - 1;
+      if (last) __hip_atomic_store(P.tickets + seg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh_last[tid] = last ? 1 : 0;
+    }
+    __syncthreads();
+    bool merged = false;
+    for (int i = 0; i < ncut; ++i) {
+      if (sh_last[i] == 0) continue;               // uniform
+      if (merged) __syncthreads();                 // the previous merge's LDS reads are done
+      merged = true;
+      const int seg = __builtin_amdgcn_readfirstlane(sh_cut[i][0]);
+      const int fw = __builtin_amdgcn_readfirstlane(sh_cut[i][1]);
+      const int n2 = __builtin_amdgcn_readfirstlane(sh_cut[i][2]);
+      combine_segment<kBf16, true>(P, seg / kKvHeads, seg % kKvHeads, fw, n2 >> 1, n2 & 1,
+                                   tail.combine);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- kernel 2
-constexpr int kCombineSubsets = 4;   // x 64 (head, 8-column group) pairs = 256 threads
-
-// One workgroup per segment (b, g): if kernel 1 cut it into several pieces,
-// merge their partials for the group's 4 query heads and write the output
-// rows; otherwise exit. Thread t takes head (t / 16) % 4, columns
-// 8 * (t % 16) .. +7, and every 4th partial from t / 64: a running max over
-// independent loads. The 4 subsets are then merged through LDS, in a fixed
-// order, so results do not depend on timing. (One workgroup per segment
-// rather than per query head: 4x fewer waves to dispatch for large batches,
-// where most segments are not cut and their workgroups exit at once.)
+// Two-launch form: one workgroup per segment (b, g); if kernel 1 cut it into
+// several pieces, merge their partials, else exit. (One workgroup per
+// segment rather than per query head: 4x fewer waves to dispatch for large
+// batches, where most segments are not cut and their workgroups exit at
+// once.)
 template <int F>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
-  constexpr bool kBf16 = F == kFmtBf16;
-  __shared__ __attribute__((aligned(16))) float xs[kCombineSubsets][64][10];
-
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) CombineLds lds;
   const int seg = blockIdx.x, b = seg / kKvHeads, g = seg - b * kKvHeads;
   const int2 desc = P.seg_desc[seg];
   const int n = desc.y >> 1;
   if (n <= 1) return;                  // empty (zero rows) or finished by kernel 1
-  const int first_w = desc.x;
-  // Partial i lives in piece first_w + i: the first piece may hold it in its
-  // second slot, every later piece holds it as its first segment.
-  const long long slot0 = 2LL * first_w + (desc.y & 1);
-
-  const int pair = tid & 63, sub = tid >> 6;
-  const int hh = pair >> 4, c8 = (pair & 15) * 8;
-  const float kNegInf = -__builtin_inff();
-  float M = kNegInf, den = 0.f;
-  float4_t na = {0.f, 0.f, 0.f, 0.f}, nb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int i = sub; i < n; i += kCombineSubsets) {
-    const long long sl = i == 0 ? slot0 : 2LL * (first_w + i);
-    const float2 ml = P.ws_ml[sl * kGroup + hh];
-    const float* src = P.ws_acc + (sl * kGroup + hh) * kDim + c8;
-    const float4_t a0 = *reinterpret_cast<const float4_t*>(src);
-    const float4_t a1 = *reinterpret_cast<const float4_t*>(src + 4);
-    const float Mn = fmaxf(M, ml.x);
-    const float s_old = exp2_hw(M - Mn), s_new = exp2_hw(ml.x - Mn);
-    den = den * s_old + ml.y * s_new;
-    na = na * s_old + a0 * s_new;
-    nb = nb * s_old + a1 * s_new;
-    M = Mn;
-  }
-  float* x = xs[sub][pair];
-  x[0] = M;
-  x[1] = den;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    x[2 + k] = na[k];
-    x[6 + k] = nb[k];
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float Mx = kNegInf;
-#pragma unroll
-    for (int k = 0; k < kCombineSubsets; ++k) Mx = fmaxf(Mx, xs[k][pair][0]);
-    float d = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < kCombineSubsets; ++k) {
-      const float* y = xs[k][pair];
-      const float wt = (y[0] == kNegInf) ? 0.f : exp2_hw(y[0] - Mx);   // subsets without partials
-      d += wt * y[1];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[c] += wt * y[2 + c];
-    }
-    const float vs = P.out_scale;
-    uint4_t r;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      r[c] = (unsigned)to_elem<kBf16>(o[2 * c] / d * vs) |
-             ((unsigned)to_elem<kBf16>(o[2 * c + 1] / d * vs) << 16);
-    *reinterpret_cast<uint4_t*>(P.out + ((size_t)b * kQHeads + g * kGroup + hh) * kDim + c8) = r;
-  }
+  combine_segment<F == kFmtBf16, false>(P, b, g, desc.x, n, desc.y & 1, lds);
 }
 
 }  // namespace
@@ -1167,13 +1299,13 @@ hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_
     // execution without extra packets between the kernels.
     hipExtLaunchKernelGGL(gqa_decode_pieces<F, kPaged>, pieces_grid, block, 0, stream, events[0],
                           events[1], 0, P);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
     hipExtLaunchKernelGGL(gqa_decode_combine<F>, combine_grid, block, 0, stream, events[2],
                           events[3], 0, P);
     return hipGetLastError();
   }
   gqa_decode_pieces<F, kPaged><<<pieces_grid, block, 0, stream>>>(P);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
   gqa_decode_combine<F><<<combine_grid, block, 0, stream>>>(P);
   return hipGetLastError();
 }
@@ -1181,8 +1313,11 @@ hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                          ElemType elem, const Layout& layout, float score_scale_log2,
                          float out_scale, int batch, int capacity, const SplitConfig& cfg,
-                         long long grid, void* partials, hipStream_t stream, hipEvent_t* events) {
+                         long long grid, void* partials, int* tickets, hipStream_t stream,
+                         hipEvent_t* events) {
   Params P;
+  P.tickets = tickets;
+  P.fused = tickets != nullptr ? 1 : 0;
   P.q = static_cast<const e16_t*>(q);
   P.kv = static_cast<const e16_t*>(kv);
   P.seq_lens = seq_lens;

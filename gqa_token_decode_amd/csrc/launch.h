@@ -44,14 +44,17 @@ size_t partial_bytes_for_grid(long long grid);
 // Bytes of per-segment descriptors for a batch (rounded to 256).
 size_t segment_bytes_for_batch(int batch);
 
-// Enqueue the two decode kernels (pieces, then combine). `partials` must
-// hold segment_bytes_for_batch(batch) + partial_bytes_for_grid(grid) bytes.
-// `events` (may be null) points at four events: start and stop of the pieces
-// kernel, then start and stop of the combine kernel.
+// Enqueue the decode. `partials` must hold segment_bytes_for_batch(batch) +
+// partial_bytes_for_grid(grid) bytes. With `tickets` (8 * batch ints, zero
+// before the call and left zero by it) one launch does everything: the last
+// piece of each cut segment merges its partials. Without, two kernels run
+// (pieces, then combine). `events` (may be null) points at four events:
+// start and stop of the pieces kernel, then start and stop of the combine
+// kernel (the last two are not recorded in the single-launch form).
 hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                          ElemType elem, const Layout& layout, float score_scale_log2,
                          float out_scale, int batch, int capacity,
-                         const SplitConfig& cfg, long long grid, void* partials,
+                         const SplitConfig& cfg, long long grid, void* partials, int* tickets,
                          hipStream_t stream, hipEvent_t* events);
 
 }  // namespace gqa

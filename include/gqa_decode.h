@@ -84,14 +84,17 @@ typedef enum gqa_status {
  * stream   HIP stream to enqueue on (NULL = the device's null stream).
  *
  * All buffers must live on one device; the kernels run on that device and
- * the caller's current device is restored before returning. Two kernels are
- * enqueued: the split-KV pieces kernel and the log-sum-exp combine kernel.
- * The library keeps a cached fp32 workspace per (device, stream) for the
- * partial results of sequences split across workgroups. It is allocated on
- * first need, so the first call on a new stream, or one needing a larger
- * workspace, must not be under graph capture; later calls allocate nothing
- * and can be captured. Calls on one stream are ordered by the stream; calls
- * on different streams use different workspaces.
+ * the caller's current device is restored before returning. The split-KV
+ * pieces kernel runs, followed by the log-sum-exp combine kernel, or (see
+ * gqa_decode_set_launch_form) the pieces kernel alone, whose last workgroup
+ * per cut segment does the combine. The library keeps a cached fp32
+ * workspace per (device, stream) for the partial results of sequences split
+ * across workgroups, and for the single launch an int array of 8 * batch
+ * tickets, zeroed when allocated and left zero by every call. Both are
+ * allocated on first need, so the first call on a new stream, or one needing
+ * a larger workspace or batch, must not be under graph capture; later calls
+ * allocate nothing and can be captured. Calls on one stream are ordered by
+ * the stream; calls on different streams use different workspaces.
  *
  * Returns GQA_OK, or a negative gqa_status with nothing enqueued.
  */
@@ -219,6 +222,32 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity);
  */
 void gqa_decode_release_workspace(void);
 
+/* How a decode call runs its combine step. */
+typedef enum gqa_launch_form {
+  GQA_LAUNCH_AUTO = 0,    /* single launch when capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY
+                             and batch * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS, else two
+                             kernels (the default)                                           */
+  GQA_LAUNCH_SINGLE = 1,  /* one kernel: the last workgroup to finish a cut (sequence, KV
+                             head) segment merges its partial results, found through a
+                             per-segment atomic ticket                                       */
+  GQA_LAUNCH_TWO = 2      /* two kernels: split-KV pieces, then the log-sum-exp combine      */
+} gqa_launch_form;
+
+/* Bounds within which GQA_LAUNCH_AUTO picks the single launch (short
+ * caches, where saving the second launch outweighs the ticket round trips). */
+#define GQA_SINGLE_LAUNCH_MAX_CAPACITY 512
+#define GQA_SINGLE_LAUNCH_MAX_ROWS 16384
+
+/*
+ * gqa_decode_set_launch_form -- select the launch form of later calls (all
+ * threads, all devices). Both forms cut the work identically and merge
+ * partial results in the same fixed order, so they return the same bits;
+ * they differ only in speed. Returns GQA_OK, or GQA_ERR_BAD_ARG for a value
+ * outside gqa_launch_form. The environment variable GQA_DECODE_LAUNCH_FORM
+ * (0, 1 or 2) sets the initial value.
+ */
+int gqa_decode_set_launch_form(int form);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* gqa_decode_status_string(int status);
 
@@ -232,7 +261,8 @@ const char* gqa_decode_last_error(void);
  * each of their two kernels on the call's stream, so the events time the
  * kernels' execution. gqa_decode_profile_end() waits for the recorded
  * events, returns the summed durations in milliseconds of the pieces kernel
- * and of the combine kernel and the number of calls recorded, then stops
+ * and of the combine kernel (no time for single-launch calls, whose pieces
+ * kernel includes the combine) and the number of calls recorded, then stops
  * recording. Any output pointer may be NULL. Calls made while their stream
  * is being captured into a graph are not timed (nor counted).
  */

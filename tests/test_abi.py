@@ -52,7 +52,7 @@ def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     assert names == sorted([
         "gqa_decode", "gqa_decode_chunked", "gqa_decode_typed", "gqa_decode_ex",
-        "gqa_decode_workspace_bytes",
+        "gqa_decode_workspace_bytes", "gqa_decode_set_launch_form",
         "gqa_decode_release_workspace", "gqa_decode_status_string", "gqa_decode_last_error",
         "gqa_decode_profile_begin", "gqa_decode_profile_end"])
 
@@ -156,6 +156,15 @@ def test_helpers_without_device(lib):
     assert lib.gqa_decode_profile_begin() == OK
     assert lib.gqa_decode_profile_end(ctypes.byref(p), ctypes.byref(c), ctypes.byref(n)) == OK
     assert n.value == 0
+
+
+def test_launch_form_selection(lib):
+    # needs no device: the form is a library-wide setting
+    for form in (1, 2, 0):
+        assert lib.gqa_decode_set_launch_form(form) == OK
+    assert lib.gqa_decode_set_launch_form(3) == BAD_ARG
+    assert lib.gqa_decode_set_launch_form(-1) == BAD_ARG
+    assert "form" in lib.gqa_decode_last_error().decode()
 
 
 def test_python_binding_rejects_bad_tensors_before_the_library():

@@ -273,4 +273,13 @@ def test_kernel_timer_reports_kernel_time():
         for _ in range(3):
             g.gqa_decode(q, kv, lens, q_scale=w.q_scale)
     torch.cuda.synchronize()
+    # capacity 8192: the automatic choice runs two kernels
     assert t.calls == 3 and t.pieces_ms > 0 and t.combine_ms > 0
+    g.set_launch_form("single")
+    try:
+        with g.KernelTimer() as t:
+            g.gqa_decode(q, kv, lens, q_scale=w.q_scale)
+        torch.cuda.synchronize()
+    finally:
+        g.set_launch_form("auto")
+    assert t.calls == 1 and t.pieces_ms > 0 and t.combine_ms == 0
