@@ -22,6 +22,12 @@ design notes):
 Rows at or beyond L are sliced away, never read, so their contents (NaN or
 garbage) cannot influence the result.
 
+Extension beyond the page (other head counts): with Hq query heads and Hkv
+KV heads (Hq a multiple of Hkv), query head h uses KV head h // (Hq / Hkv),
+the contiguous grouping that SDPA's ``enable_gqa`` applies for any ratio;
+the head counts are read from the shapes of q and kv. The page's 32/8 case
+is the default everywhere.
+
 Extension beyond the page (the library's typed entry point): stored K and V
 values may stand for k_scale * K and v_scale * V (per-tensor scales, float32
 at the ABI). The definition is unchanged with K and V replaced by those
@@ -60,25 +66,32 @@ def decode_head(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -
     return (w @ V) / w.sum()
 
 
+def _group_of(n_q_heads: int, n_kv_heads: int) -> int:
+    assert n_q_heads >= 1 and n_kv_heads >= 1 and n_q_heads % n_kv_heads == 0, \
+        (n_q_heads, n_kv_heads)
+    return n_q_heads // n_kv_heads
+
+
 def decode(q: np.ndarray, kv: np.ndarray, seq_lens, q_scale: float = 1.0,
            rows=None, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Decode one token for every (batch, query head); float64 result.
 
-    q: [B, 32, 128]; kv: [B, 2, 8, C, 128], any float dtype holding the
-    element values exactly (fp16, or bf16 widened with formats.bf16_to_f64);
-    seq_lens: int [B]. ``rows`` optionally restricts the work to a list of
-    (b, h) pairs; the other output rows are left as NaN (used for sampled
-    checks on large inputs).
+    q: [B, Hq, 128] (Hq = 32 on the page); kv: [B, 2, Hkv, C, 128] (Hkv = 8),
+    any float dtype holding the element values exactly (fp16, or bf16
+    widened with formats.bf16_to_f64); seq_lens: int [B]. ``rows``
+    optionally restricts the work to a list of (b, h) pairs; the other
+    output rows are left as NaN (used for sampled checks on large inputs).
     """
     q = np.asarray(q)
-    B = q.shape[0]
-    C = kv.shape[3]
-    assert q.shape == (B, NUM_Q_HEADS, HEAD_DIM)
-    assert kv.shape == (B, 2, NUM_KV_HEADS, C, HEAD_DIM)
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv, C = kv.shape[2], kv.shape[3]
+    assert q.shape == (B, Hq, HEAD_DIM)
+    assert kv.shape == (B, 2, Hkv, C, HEAD_DIM)
+    group = _group_of(Hq, Hkv)
     lens = np.asarray(seq_lens).astype(np.int64)
     scale = effective_scale(q_scale, k_scale)
     vs = float(np.float32(v_scale))
-    out = np.full((B, NUM_Q_HEADS, HEAD_DIM), np.nan if rows is not None else 0.0)
+    out = np.full((B, Hq, HEAD_DIM), np.nan if rows is not None else 0.0)
     wanted = None
     if rows is not None:
         wanted = {}
@@ -88,8 +101,8 @@ def decode(q: np.ndarray, kv: np.ndarray, seq_lens, q_scale: float = 1.0,
         if wanted is not None and b not in wanted:
             continue
         L = int(min(max(lens[b], 0), C))
-        for g in range(NUM_KV_HEADS):
-            heads = [h for h in range(g * GROUP, (g + 1) * GROUP)
+        for g in range(Hkv):
+            heads = [h for h in range(g * group, (g + 1) * group)
                      if wanted is None or h in wanted[b]]
             if not heads:
                 continue
@@ -104,17 +117,20 @@ def decode_ragged(q: np.ndarray, k_valid, v_valid, q_scale: float = 1.0,
                   k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Same definition, taking each sequence's valid K/V rows directly.
 
-    k_valid[b], v_valid[b]: [8, L_b, 128]. Avoids building a dense cache.
+    k_valid[b], v_valid[b]: [Hkv, L_b, 128]. Avoids building a dense cache.
     """
-    B = q.shape[0]
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv = len(k_valid[0]) if B else NUM_KV_HEADS
+    group = _group_of(Hq, Hkv)
     scale = effective_scale(q_scale, k_scale)
     vs = float(np.float32(v_scale))
-    out = np.zeros((B, NUM_Q_HEADS, HEAD_DIM))
+    out = np.zeros((B, Hq, HEAD_DIM))
     for b in range(B):
-        for g in range(NUM_KV_HEADS):
+        assert len(k_valid[b]) == Hkv and len(v_valid[b]) == Hkv
+        for g in range(Hkv):
             K = np.asarray(k_valid[b][g], dtype=np.float64)
             V = np.asarray(v_valid[b][g], dtype=np.float64)
-            for h in range(g * GROUP, (g + 1) * GROUP):
+            for h in range(g * group, (g + 1) * group):
                 out[b, h] = vs * decode_head(q[b, h].astype(np.float64), K, V, scale)
     return out
 

@@ -460,3 +460,74 @@ def test_e4m3_cache_matches_sdpa_on_dequantised_tensors():
                                          tk, tv, attn_mask=mask, scale=effective_scale(1.0),
                                          enable_gqa=True).squeeze(2).numpy()
     assert np.abs(got - ref).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- other head counts
+# The page fixes 32 query and 8 KV heads; the library also takes other
+# counts (Hq a multiple of Hkv, Hq / Hkv <= 8), with query head h reading KV
+# head h // (Hq / Hkv) as SDPA's enable_gqa does for any ratio.
+HEAD_COUNTS = [(64, 8), (28, 4), (16, 16), (32, 16), (8, 1), (40, 8), (12, 4), (1, 1)]
+
+
+def _rand_heads(rng, B, C, Hq, Hkv):
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    kv = rng.standard_normal((B, 2, Hkv, C, D)).astype(np.float16)
+    return q, kv
+
+
+@pytest.mark.parametrize("Hq,Hkv", HEAD_COUNTS)
+def test_other_head_counts_match_brute_force(Hq, Hkv):
+    rng = np.random.default_rng(700 + Hq + Hkv)
+    C = 3
+    lens = [0, 1, 2, 3, 7]
+    q, kv = _rand_heads(rng, len(lens), C, Hq, Hkv)
+    got = decode(q, kv, np.array(lens, np.int32), 1.3)
+    ref = np.array(brute.decode_brute(q.astype(np.float64).tolist(),
+                                      kv.astype(np.float64).tolist(), lens, 1.3,
+                                      n_kv_heads=Hkv))
+    assert got.shape == (len(lens), Hq, D)
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, float(np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("Hq,Hkv", HEAD_COUNTS)
+def test_other_head_counts_match_torch_sdpa(Hq, Hkv):
+    rng = np.random.default_rng(800 + Hq + Hkv)
+    q, kv = _rand_heads(rng, 3, 67, Hq, Hkv)
+    lens = np.array([67, 1, 40], np.int32)
+    got = decode(q, kv, lens, 0.75)
+    ref = _sdpa_f64(q, kv, lens, 0.75)
+    assert np.abs(got - ref).max() <= 1e-12
+    # the ragged form reads the same heads
+    k_valid = [kv[b, 0, :, :lens[b]] for b in range(3)]
+    v_valid = [kv[b, 1, :, :lens[b]] for b in range(3)]
+    assert np.abs(decode_ragged(q, k_valid, v_valid, 0.75) - got).max() <= 1e-15
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(64, 8), (28, 4), (8, 1), (12, 4)])
+def test_other_head_counts_use_contiguous_groups(Hq, Hkv):
+    # V of KV head g is the constant g + 1: query head h must return
+    # h // (Hq / Hkv) + 1 (a strided map h % Hkv would differ).
+    rng = np.random.default_rng(900 + Hq)
+    q, kv = _rand_heads(rng, 1, 5, Hq, Hkv)
+    for g in range(Hkv):
+        kv[0, 1, g] = np.float16(g + 1)
+    got = decode(q, kv, np.array([5], np.int32), 1.0)
+    grp = Hq // Hkv
+    for h in range(Hq):
+        assert np.abs(got[0, h] - float(h // grp + 1)).max() <= 1e-14
+
+
+def test_one_query_head_per_kv_head_is_per_head_attention():
+    # Hq == Hkv: every head attends over its own K/V, the textbook
+    # multi-head case, written out here with a softmax per head.
+    rng = np.random.default_rng(901)
+    Hh, C = 6, 9
+    q, kv = _rand_heads(rng, 1, C, Hh, Hh)
+    got = decode(q, kv, np.array([C], np.int32), 1.0)
+    for h in range(Hh):
+        K = kv[0, 0, h].astype(np.float64)
+        V = kv[0, 1, h].astype(np.float64)
+        s = (K @ q[0, h].astype(np.float64)) / math.sqrt(D)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        assert np.abs(got[0, h] - p @ V).max() <= 1e-13

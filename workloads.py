@@ -52,18 +52,19 @@ class Workload:
     """One decode step's inputs, with the valid K/V prefixes kept ragged.
 
     ``k_valid[b]`` and ``v_valid[b]`` are fp16 arrays of shape
-    ``[8, L_b, 128]``; the dense stacked cache is materialised on demand by
+    ``[Hkv, L_b, 128]`` (Hkv = 8 unless built with other head counts); the
+    dense stacked cache is materialised on demand by
     :meth:`dense_kv` (host) or :meth:`kv_to_device` (GPU), so that a 4 GiB
     cache is never built on the host unless asked for.
     """
 
     name: str
-    q: np.ndarray                 # fp16 [B, 32, 128] (uint16 bit patterns for bf16)
+    q: np.ndarray                 # fp16 [B, Hq, 128] (uint16 bit patterns for bf16)
     seq_lens: np.ndarray          # int32 [B]
     capacity: int
     q_scale: float
-    k_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
-    v_valid: List[np.ndarray]     # fp16 [8, L_b, 128] per b
+    k_valid: List[np.ndarray]     # fp16 [Hkv, L_b, 128] per b
+    v_valid: List[np.ndarray]     # fp16 [Hkv, L_b, 128] per b
     fill: str = "zero"            # "zero" or "nan": contents beyond L_b
     elem: str = "f16"             # "f16", "bf16" or "e4m3" (kv only)
     k_scale: float = 1.0          # e4m3: the stored codes stand for K / k_scale
@@ -74,15 +75,23 @@ class Workload:
         return int(self.q.shape[0])
 
     @property
+    def q_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def kv_heads(self) -> int:
+        return int(self.k_valid[0].shape[0]) if self.k_valid else NUM_KV_HEADS
+
+    @property
     def valid_lengths(self) -> np.ndarray:
         """Lengths clamped to [0, capacity], as the decode interprets them."""
         return np.clip(self.seq_lens.astype(np.int64), 0, self.capacity)
 
     @property
     def kv_bytes_read(self) -> int:
-        """K+V bytes of the valid prefixes: sum(L_b) * 2 * 8 * 128 * (2 B, or
-        1 B for e4m3)."""
-        return int(self.valid_lengths.sum()) * 2 * NUM_KV_HEADS * HEAD_DIM * self.kv_elem_bytes
+        """K+V bytes of the valid prefixes: sum(L_b) * 2 * Hkv * 128 * (2 B,
+        or 1 B for e4m3)."""
+        return int(self.valid_lengths.sum()) * 2 * self.kv_heads * HEAD_DIM * self.kv_elem_bytes
 
     @property
     def kv_elem_bytes(self) -> int:
@@ -111,10 +120,10 @@ class Workload:
         return t.to(device)
 
     def dense_kv(self) -> np.ndarray:
-        """Host ``[B, 2, 8, C, 128]`` cache (fp16, or bf16 bit patterns)
+        """Host ``[B, 2, Hkv, C, 128]`` cache (fp16, or bf16 bit patterns)
         with the fill beyond L_b."""
         B, C = self.batch, self.capacity
-        kv = np.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=self._host_dtype())
+        kv = np.empty((B, 2, self.kv_heads, C, HEAD_DIM), dtype=self._host_dtype())
         kv.view(np.uint16)[...] = self.fill_value_bits()
         for b in range(B):
             L = self.k_valid[b].shape[1]
@@ -127,7 +136,7 @@ class Workload:
         import torch
 
         B, C = self.batch, self.capacity
-        kv = torch.empty((B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=self._torch_dtype(),
+        kv = torch.empty((B, 2, self.kv_heads, C, HEAD_DIM), dtype=self._torch_dtype(),
                          device=device)
         if self.elem == "e4m3":
             raw, host_raw = kv.view(torch.uint8), np.uint8
@@ -172,11 +181,14 @@ def build(
     sigma_v: float = 1.0,
     fill: str = "zero",
     elem: str = "f16",
+    q_heads: int = NUM_Q_HEADS,
+    kv_heads: int = NUM_KV_HEADS,
 ) -> Workload:
     """Draw a workload. ``lengths`` is a list or a callable taking the rng.
 
     Lengths may lie outside [0, capacity] (tests of clamping); only
-    ``clip(L_b, 0, capacity)`` rows are drawn.
+    ``clip(L_b, 0, capacity)`` rows are drawn. Draw order: lengths, q, then
+    per sequence K and V (the same order for any head counts).
     """
     rng = np.random.default_rng(seed)
     if callable(lengths):
@@ -186,12 +198,12 @@ def build(
     B = int(lens.shape[0])
     assert elem in ("f16", "bf16", "e4m3"), elem
     kv_scale = E4M3_SCALE if elem == "e4m3" else 1.0
-    q = _normal(rng, (B, NUM_Q_HEADS, HEAD_DIM), sigma_q, "f16" if elem == "e4m3" else elem)
+    q = _normal(rng, (B, q_heads, HEAD_DIM), sigma_q, "f16" if elem == "e4m3" else elem)
     k_valid, v_valid = [], []
     for b in range(B):
         L = int(min(max(lens[b], 0), capacity))
-        k_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_k, elem, kv_scale))
-        v_valid.append(_normal(rng, (NUM_KV_HEADS, L, HEAD_DIM), sigma_v, elem, kv_scale))
+        k_valid.append(_normal(rng, (kv_heads, L, HEAD_DIM), sigma_k, elem, kv_scale))
+        v_valid.append(_normal(rng, (kv_heads, L, HEAD_DIM), sigma_v, elem, kv_scale))
     return Workload(name, q, lens.astype(np.int32), int(capacity), float(q_scale),
                     k_valid, v_valid, fill, elem, kv_scale, kv_scale)
 
