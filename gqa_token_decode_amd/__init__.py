@@ -10,7 +10,8 @@ never goes through torch operators.
 
 Public API (names and keyword arguments follow the ``sm110_gqa_decode``
 entry point documented on the FlashInfer PR #5052 analysis page, section 1;
-bf16 tensors and the K/V scales are this library's extension):
+bf16 tensors, the K/V scales, other head counts and paged caches are this
+library's extension):
     gqa_decode(q, kv, sequence_lengths, *, out=None, q_scale=1.0, chunk_len=0,
                k_scale=1.0, v_scale=1.0)
     gqa_decode_paged(q, kv_pages, block_table, sequence_lengths, *, ...)
@@ -30,6 +31,7 @@ __all__ = ["gqa_decode", "gqa_decode_paged", "workspace_bytes", "release_workspa
 NUM_Q_HEADS = 32
 NUM_KV_HEADS = 8
 HEAD_DIM = 128
+MAX_GROUP = 8          # query heads per KV head, at most
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libgqa_decode.so"
@@ -121,7 +123,8 @@ class _Layout(ctypes.Structure):
                 ("kv_stride_batch", ctypes.c_int64), ("kv_stride_kind", ctypes.c_int64),
                 ("kv_stride_head", ctypes.c_int64), ("kv_stride_row", ctypes.c_int64),
                 ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int),
-                ("page_size", ctypes.c_int), ("num_pages", ctypes.c_int)]
+                ("page_size", ctypes.c_int), ("num_pages", ctypes.c_int),
+                ("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int)]
 
 
 def _check_view(name, t, dtype, shape_len):
@@ -149,10 +152,14 @@ def _prepare(q, kv, sequence_lengths, out, kv_shape_check):
     _check_view("q", q, dtype, 3)
     _check_view("kv", kv, kv.dtype if fp8_kv else dtype, 5)
     _check_tensor("sequence_lengths", sequence_lengths, torch.int32, 1)
-    B = q.shape[0]
-    if q.shape[1] != NUM_Q_HEADS or q.shape[2] != HEAD_DIM:
-        raise ValueError(f"q must have shape [batch, 32, 128], got {tuple(q.shape)}")
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must have shape [batch, heads, 128], got {tuple(q.shape)}")
     kv_shape_check(B)
+    Hkv = kv.shape[2]
+    if Hkv < 1 or Hq < 1 or Hq % Hkv != 0 or Hq // Hkv > MAX_GROUP:
+        raise ValueError(f"{Hq} query heads over {Hkv} KV heads: need a positive multiple with "
+                         f"at most {MAX_GROUP} query heads per KV head")
     if sequence_lengths.shape[0] != B:
         raise ValueError(f"sequence_lengths must have shape [{B}], got {tuple(sequence_lengths.shape)}")
     dev = q.device
@@ -185,10 +192,13 @@ def _check_chunk(chunk_len):
 def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor, *,
                out: Optional[torch.Tensor] = None, q_scale: float = 1.0,
                chunk_len: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
-    """Decode one token of GQA (32 query heads, 8 KV heads, dim 128).
+    """Decode one token of GQA (32 query heads over 8 KV heads, dim 128, on
+    the page; other head counts too).
 
-    q: fp16 or bf16 [batch, 32, 128]; kv: same dtype [batch, 2, 8, capacity,
-    128] with K at index 0 and V at index 1 of axis 1, or, with fp16 q, an
+    q: fp16 or bf16 [batch, Hq, 128]; kv: same dtype [batch, 2, Hkv,
+    capacity, 128] with K at index 0 and V at index 1 of axis 1 (Hq a
+    multiple of Hkv, at most 8 query heads per KV head; query head h reads
+    KV head h // (Hq // Hkv)), or, with fp16 q, an
     OCP FP8 E4M3 cache (torch.float8_e4m3fn, or uint8 holding E4M3 bytes)
     dequantised by k_scale and v_scale; sequence_lengths:
     int32 [batch] on the same device (values clamped to [0, capacity]).
@@ -203,18 +213,21 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
     """
     def kv_shape(B):
         ks = kv.shape
-        if ks[0] != B or ks[1] != 2 or ks[2] != NUM_KV_HEADS or ks[4] != HEAD_DIM:
-            raise ValueError(f"kv must have shape [{B}, 2, 8, capacity, 128], got {tuple(ks)}")
+        if ks[0] != B or ks[1] != 2 or ks[4] != HEAD_DIM:
+            raise ValueError(f"kv must have shape [{B}, 2, kv_heads, capacity, 128], "
+                             f"got {tuple(ks)}")
 
     code, fp8_kv, out = _prepare(q, kv, sequence_lengths, out, kv_shape)
     _check_chunk(chunk_len)
     B, C = q.shape[0], kv.shape[3]
+    Hq, Hkv = q.shape[1], kv.shape[2]
     lib = _lib if _lib is not None else load_library()
     stream = _stream_of(q.device)
     args = (q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(), out.data_ptr())
-    if not (q.is_contiguous() and kv.is_contiguous()):
+    if (not (q.is_contiguous() and kv.is_contiguous())
+            or (Hq, Hkv) != (NUM_Q_HEADS, NUM_KV_HEADS)):
         lay = _Layout(q.stride(0), q.stride(1), kv.stride(0), kv.stride(1), kv.stride(2),
-                      kv.stride(3), None, 0, 0, 0)
+                      kv.stride(3), None, 0, 0, 0, Hq, Hkv)
         st = lib.gqa_decode_ex(*args, code, ctypes.byref(lay), float(q_scale), float(k_scale),
                                float(v_scale), B, C, chunk_len, stream)
     elif code != 0 or k_scale != 1.0 or v_scale != 1.0:
@@ -235,7 +248,7 @@ def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch
                      v_scale: float = 1.0) -> torch.Tensor:
     """Decode one token of GQA from a paged KV cache.
 
-    kv_pages: [num_pages, 2, 8, page_size, 128] (HND pages; fp16, bf16 or an
+    kv_pages: [num_pages, 2, Hkv, page_size, 128] (HND pages; fp16, bf16 or an
     E4M3 cache as for gqa_decode; strided views with a contiguous last axis
     allowed), page_size a power of two >= 16. block_table: int32 [batch,
     max_pages] on the same device; position i of sequence b lives in page
@@ -245,9 +258,9 @@ def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch
     """
     def kv_shape(B):
         ks = kv_pages.shape
-        if ks[1] != 2 or ks[2] != NUM_KV_HEADS or ks[4] != HEAD_DIM:
-            raise ValueError(f"kv_pages must have shape [num_pages, 2, 8, page_size, 128], "
-                             f"got {tuple(ks)}")
+        if ks[1] != 2 or ks[4] != HEAD_DIM:
+            raise ValueError(f"kv_pages must have shape [num_pages, 2, kv_heads, page_size, "
+                             f"128], got {tuple(ks)}")
         _check_tensor("block_table", block_table, torch.int32, 2)
         if block_table.shape[0] != B:
             raise ValueError(f"block_table must have {B} rows, got {tuple(block_table.shape)}")
@@ -262,7 +275,7 @@ def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch
     max_pages = block_table.shape[1]
     lay = _Layout(q.stride(0), q.stride(1), kv_pages.stride(0), kv_pages.stride(1),
                   kv_pages.stride(2), kv_pages.stride(3), block_table.data_ptr(), max_pages,
-                  page_size, num_pages)
+                  page_size, num_pages, q.shape[1], kv_pages.shape[2])
     lib = _lib if _lib is not None else load_library()
     st = lib.gqa_decode_ex(q.data_ptr(), kv_pages.data_ptr(), sequence_lengths.data_ptr(),
                            out.data_ptr(), code, ctypes.byref(lay), float(q_scale),
@@ -288,7 +301,8 @@ def set_launch_form(form: str) -> None:
     """Select how later calls run the combine step: "single" (one kernel; the
     last workgroup of each cut segment merges it), "two" (pieces kernel, then
     combine kernel) or "auto" (single launch for capacities up to 512 with at
-    most 16384 cache rows in all). The forms return the same bits."""
+    most 131072 cache rows, batch x KV heads x capacity, in all). The forms
+    return the same bits."""
     if form not in _LAUNCH_FORMS:
         raise ValueError(f"launch form must be one of {sorted(_LAUNCH_FORMS)}, got {form!r}")
     lib = load_library()

@@ -27,7 +27,6 @@
 
 namespace {
 
-constexpr size_t kQBytesPerSeq = (size_t)GQA_NUM_Q_HEADS * GQA_HEAD_DIM * 2;           // 8 KiB
 constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
 constexpr int kMinPieceDefault = 128;      // cost units: two 64-row steps of a workgroup
 constexpr int kSegCostDefault = 128;       // fixed cost of a segment, in row units
@@ -247,6 +246,18 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
     L.kv_stride_kind = GQA_NUM_KV_HEADS * C * GQA_HEAD_DIM;
     L.kv_stride_batch = 2 * L.kv_stride_kind;
   }
+  if (L.num_q_heads == 0 && L.num_kv_heads == 0) {
+    L.num_q_heads = GQA_NUM_Q_HEADS;
+    L.num_kv_heads = GQA_NUM_KV_HEADS;
+  }
+  const int Hq = L.num_q_heads, Hkv = L.num_kv_heads;
+  if (Hq <= 0 || Hkv <= 0 || Hkv > GQA_MAX_KV_HEADS || Hq % Hkv != 0 || Hq / Hkv > GQA_MAX_GROUP)
+    return fail(GQA_ERR_BAD_ARG,
+                "gqa_decode: %d query heads over %d KV heads: need a positive multiple with at "
+                "most %d query heads per KV head and at most %d KV heads",
+                Hq, Hkv, GQA_MAX_GROUP, GQA_MAX_KV_HEADS);
+  if ((long long)batch * Hkv > GQA_MAX_SEGMENTS)
+    return fail(GQA_ERR_BAD_SHAPE, "gqa_decode: batch * num_kv_heads exceeds 2^27");
   const long long qs[2] = {L.q_stride_batch, L.q_stride_head};
   const long long ks[4] = {L.kv_stride_batch, L.kv_stride_kind, L.kv_stride_head, L.kv_stride_row};
   const long long kLimit = 1LL << 40;   // elements; keeps every product below 2^62
@@ -260,7 +271,7 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
   const long long sr = L.kv_stride_row * (long long)kv_eb;
   if (sr < row_bytes)
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: kv_stride_row must cover a %lld-byte row", row_bytes);
-  if (3 * L.q_stride_head * 2 + 2 * GQA_HEAD_DIM >= (1LL << 31))
+  if ((GQA_MAX_GROUP - 1) * L.q_stride_head * 2 + 2 * GQA_HEAD_DIM >= (1LL << 31))
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: q_stride_head is too large for 32-bit offsets");
   const bool paged = L.block_table != nullptr;
   long long rows_per_block = C;
@@ -282,9 +293,9 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
                 paged ? "page_size" : "capacity");
   const long long blocks = paged ? L.num_pages : batch;
   r->q_extent = (size_t)(((long long)(batch - 1) * L.q_stride_batch +
-                          (GQA_NUM_Q_HEADS - 1) * L.q_stride_head + GQA_HEAD_DIM) * 2);
+                          (long long)(Hq - 1) * L.q_stride_head + GQA_HEAD_DIM) * 2);
   r->kv_extent = (size_t)(((blocks - 1) * L.kv_stride_batch + L.kv_stride_kind +
-                           (GQA_NUM_KV_HEADS - 1) * L.kv_stride_head +
+                           (long long)(Hkv - 1) * L.kv_stride_head +
                            (rows_per_block - 1) * L.kv_stride_row + GQA_HEAD_DIM) * (long long)kv_eb);
   r->table_bytes = paged ? (size_t)batch * (size_t)L.max_pages * 4 : 0;
   r->lay.q_sb = L.q_stride_batch * 2;
@@ -300,6 +311,8 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
   while (paged && (1 << shift) < L.page_size) ++shift;
   r->lay.page_shift = shift;
   r->row_align = paged ? 16 : 1;
+  r->lay.q_heads = Hq;
+  r->lay.kv_heads = Hkv;
   return GQA_OK;
 }
 
@@ -326,7 +339,7 @@ int check_args(const void* q, const void* kv, const int32_t* seq_lens, const voi
 
 int check_alias(const void* q, const void* kv, const int32_t* seq_lens, const void* out,
                 int batch, const Resolved& r) {
-  const size_t ob = (size_t)batch * kQBytesPerSeq;
+  const size_t ob = (size_t)batch * r.lay.q_heads * GQA_HEAD_DIM * 2;
   if (overlaps(out, ob, q, r.q_extent) || overlaps(out, ob, kv, r.kv_extent) ||
       overlaps(out, ob, seq_lens, (size_t)batch * 4) ||
       (r.table_bytes && overlaps(out, ob, r.lay.block_table, r.table_bytes)))
@@ -376,9 +389,12 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
                 di.arch.c_str());
     } else {
       const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align);
-      const long long grid = gqa::grid_for(batch, capacity, cfg);
+      const int Hkv = res.lay.kv_heads, group = res.lay.q_heads / res.lay.kv_heads;
+      const long long grid = gqa::grid_for(batch, capacity, Hkv, cfg);
       const size_t pbytes =
-          grid > 0 ? gqa::segment_bytes_for_batch(batch) + gqa::partial_bytes_for_grid(grid) : 0;
+          grid > 0 ? gqa::segment_bytes_for_batch(batch, Hkv) +
+                         gqa::partial_bytes_for_grid(grid, group)
+                   : 0;
       if (grid <= 0 || grid > 0x7fffffffLL) {
         st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs more than 2^31 workgroups");
       } else if (chunk_len > 0 && pbytes > kMaxForcedWorkspace) {
@@ -393,9 +409,9 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
         const bool single = g_launch_form == GQA_LAUNCH_SINGLE ||
                             (g_launch_form == GQA_LAUNCH_AUTO &&
                              capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY &&
-                             (long long)batch * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS);
+                             (long long)batch * Hkv * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS);
         int* tickets = nullptr;
-        if (ws && single) tickets = get_tickets(dev, stream, (size_t)batch * 8, &st);
+        if (ws && single) tickets = get_tickets(dev, stream, (size_t)batch * Hkv, &st);
         if (ws && (tickets || !single)) {
           // Scores are formed as dot * q_scale * k_scale / sqrt(128) * log2(e),
           // so the kernel can use the hardware base-2 exponential.
@@ -473,8 +489,9 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   std::lock_guard<std::mutex> lock(g_mu);
   const DeviceInfo& di = device_info(dev);
   if (di.status != GQA_OK) return 0;
-  const long long grid = gqa::grid_for(batch, capacity, split_config(di, 0));
-  return gqa::segment_bytes_for_batch(batch) + gqa::partial_bytes_for_grid(grid);
+  const long long grid = gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0));
+  return gqa::segment_bytes_for_batch(batch, GQA_NUM_KV_HEADS) +
+         gqa::partial_bytes_for_grid(grid, GQA_NUM_Q_HEADS / GQA_NUM_KV_HEADS);
 }
 
 void gqa_decode_release_workspace(void) {

@@ -2,7 +2,9 @@
 //
 // Operation (FlashInfer PR #5052 analysis page, "SM110 FP16 GQA decode":
 // section 1 docstring, section 2 specialisation, section 3 SDPA comparator):
-// for batch entry b and query head h, with g = h / 4 and L = clamp(len, 0, C),
+// for batch entry b and query head h, with g = h / G (G = Hq / Hkv query
+// heads per KV head; the page's case is Hq = 32, Hkv = 8, G = 4) and
+// L = clamp(len, 0, C),
 //   out[b,h] = softmax_i(q_scale / sqrt(128) * q[b,h] . K[b,g,i]) . V[b,g,i],  i < L.
 //
 // Work split (decided on the device from seq_lens; the host never reads them)
@@ -15,12 +17,11 @@
 //   one segment, any number of whole segments and the head of another; a
 //   piece that holds only fixed-cost units of a segment skips it.
 //   A segment inside one piece is finished by that workgroup (normalised
-//   fp16 output). A segment cut by piece boundaries gets one fp32 partial
+//   output). A segment cut by piece boundaries gets one fp32 partial
 //   (running max, softmax denominator, unnormalised weighted V sum) per
-//   piece, and a second kernel (one workgroup per sequence and query head)
-//   merges them with a log-sum-exp rescale. The kernel boundary makes the partials visible
-//   across XCDs; merging inside the first kernel would need device-scope
-//   release fences (an L2 write-back per workgroup), which cost far more.
+//   piece, merged with a log-sum-exp rescale in a fixed order, either by a
+//   second kernel (one workgroup per segment) or, in the single-launch form,
+//   by the piece that completes the segment (per-segment atomic ticket).
 //
 // Per-wave compute on the matrix cores (fp32 accumulate), 16 rows per step;
 // the 4 waves of a workgroup take interleaved 16-row tiles of each segment.
@@ -31,22 +32,25 @@
 //   register staging; 16-byte chunks of K/V rows XOR-swizzled by row). The
 //   buffer resources are bounded by the segment's rows in this piece, so rows
 //   past the range read as zeros, never as stored data.
-//   QK (v_mfma_f32_16x16x32_f16): A = 16 K rows x 32 depth (lane (G, j)
-//   reads row j, depth 32kk + 8G .. +7), B = q^T with the group's 4 heads in
-//   columns 0..3 and zero columns 4..15; D gives lane (G, j) the scores of
-//   rows 4G..4G+3 for head j.
+//   QK (v_mfma_f32_16x16x32_f16): A = 16 K rows x 32 depth (lane (G4, j)
+//   reads row j, depth 32kk + 8 G4 .. +7), B = q^T with the group's G <= 8
+//   heads in columns 0..G-1 and zero columns G..15; D gives lane (G4, j) the
+//   scores of rows 4 G4 .. 4 G4 + 3 for head j.
 //   Online softmax in base 2 (scores carry log2(e)); rows at or beyond the
 //   range end get score -inf and weight 0 by selects.
-//   PV (v_mfma_f32_16x16x16_f16): A = weights (rows = heads, k = 16 rows);
-//   the QK D layout already is this A layout, so the weights stay in their
-//   lanes. B = 16 V rows x 16 head-dim columns, read transposed from LDS with
-//   ds_read_b64_tr_b16. Weights are split into fp16 high and low parts (two
-//   MFMAs) so the sum keeps fp32-level accuracy; the denominator sums the
-//   fp32 weights.
+//   PV (v_mfma_f32_16x16x16_f16) computes O^T = V^T P^T: A = 16 V rows read
+//   transposed from LDS (ds_read_b64_tr_b16: lane (G4, i) holds head-dim
+//   column 16 db + i of rows 4 G4 .. +3), B = the weights, whose QK D layout
+//   already is this B layout (lane (G4, j): head j, rows 4 G4 .. +3), so they
+//   stay in their lanes. D gives lane (G4, j) head j's output columns
+//   16 db + 4 G4 .. +3, so each lane rescales its accumulators by its own
+//   head's factor. Weights are split into fp16 high and low parts (two MFMAs)
+//   so the sum keeps fp32-level accuracy; the denominator sums the fp32
+//   weights.
 //   LDS reads of a stage are issued from asm blocks with their own waits: the
 //   compiler cannot tell the two stages apart and would otherwise wait for the
 //   next tile's loads, which are in flight by design.
-// Each K/V row crosses HBM once, for all 4 query heads of its group.
+// Each K/V row crosses HBM once, for all G query heads of its group.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -70,9 +74,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef unsigned uint4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-constexpr int kQHeads = 32;
-constexpr int kKvHeads = 8;
-constexpr int kGroup = kQHeads / kKvHeads;   // 4 query heads per KV head
+constexpr int kMaxGroup = 8;                 // query heads per KV head, at most
 constexpr int kDim = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -80,8 +82,13 @@ constexpr int kTileRows = 16;                // rows per wave per step
 constexpr int kStepRows = kWaves * kTileRows;     // rows per workgroup step
 constexpr int kTileHalves = kTileRows * kDim;     // one K or V tile in LDS (4 KiB)
 constexpr int kStageHalves = 2 * kTileHalves;     // one pipeline stage: K then V
-constexpr int kQHalves = kGroup * kDim;           // the group's 4 query rows (1 KiB)
-constexpr int kLoadsPerTile = 9;             // per lane: q, 4 x K, 4 x V
+// Kernels come in two forms: kG4 for exactly 4 query heads per KV head (the
+// page's 32/8 case: group size, q loads and merge layout fixed at compile
+// time) and a general form for any group of 1..8 heads.
+template <bool kG4> constexpr int q_halves() { return (kG4 ? 4 : kMaxGroup) * kDim; }
+// Loads per tile and lane: 1 or 2 q loads (1 KiB each), 4 x K, 4 x V.
+template <bool kG4> constexpr int loads_per_tile() { return kG4 ? 9 : 10; }
+
 
 // Element formats: q, K, V and out in fp16 or bf16 (16-row tiles of 256-byte
 // rows), or fp16 q and out with OCP FP8 E4M3 K and V (32-row tiles of
@@ -91,21 +98,25 @@ template <int F> constexpr int tile_rows() { return F == kFmtE4m3 ? 32 : 16; }
 template <int F> constexpr int row_bytes() { return F == kFmtE4m3 ? kDim : 2 * kDim; }
 constexpr unsigned kBufferFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
-constexpr int kSlotFloats = kGroup * (2 + kDim);   // one partial: 4 x (max, den) + 4 x 128 sums
+constexpr int kHeadSlotFloats = 2 + kDim;   // one head of a partial: (max, den) + 128 sums
 
 struct Params {
   const e16_t* q;
   const e16_t* kv;
   const int32_t* seq_lens;
   e16_t* out;
-  float2* ws_ml;       // [2 * grid][4] (max, denominator) per partial and head
-  float* ws_acc;       // [2 * grid][4][128] unnormalised weighted V sums
-  int2* seg_desc;      // [8 * batch] per segment: first piece, 2 * pieces + second-slot bit
-  int* tickets;        // [8 * batch] single launch: pieces of each segment done so far
+  float2* ws_ml;       // [2 * grid][G] (max, denominator) per partial and head
+  float* ws_acc;       // [2 * grid][G][128] unnormalised weighted V sums
+  int2* seg_desc;      // [Hkv * batch] per segment: first piece, 2 * pieces + second-slot bit
+  int* tickets;        // [Hkv * batch] single launch: pieces of each segment done so far
                        // (zero between calls: the last piece resets its count)
   int fused;           // 1: the last piece of a cut segment merges its partials
   int batch;
   int capacity;
+  int kv_heads;        // Hkv: segments per sequence
+  int group;           // G = Hq / Hkv, 1 .. kMaxGroup
+  int q_heads;         // Hq (rows of out per sequence)
+  int wave_planner;    // 1: batch <= 64 and every cost total fits 32 bits
   int pieces;          // automatic split: number of equal pieces
   int min_piece;       // automatic split: lower bound on the piece length
   int forced_piece;    // > 0: fixed piece length
@@ -123,6 +134,12 @@ struct Params {
                                 // start at multiples of 16 rows
 };
 
+// Query heads per KV head: a compile-time 4 in the kG4 kernels.
+template <bool kG4>
+__device__ __forceinline__ int group_of(const Params& P) {
+  return kG4 ? 4 : P.group;
+}
+
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
 // Rows a segment of length len occupies on the cost line: len rounded up to
@@ -132,9 +149,9 @@ __device__ __forceinline__ long long cost_len(const Params& P, long long len) {
   return (len + P.row_align - 1) & ~(long long)(P.row_align - 1);
 }
 
-// Cost of sequence b on the cost line: 8 segments of c0 + L units, or 0.
+// Cost of sequence b on the cost line: Hkv segments of c0 + L units, or 0.
 __device__ __forceinline__ long long seq_cost(const Params& P, long long len) {
-  return len > 0 ? 8 * (cost_len(P, len) + P.seg_cost) : 0;
+  return len > 0 ? (long long)P.kv_heads * (cost_len(P, len) + P.seg_cost) : 0;
 }
 
 // Length of sequence b read through the scalar path (b must be uniform), so
@@ -174,11 +191,6 @@ __device__ __forceinline__ float sum_over_row_groups(float x) {
   x = bitsf(a[0]) + bitsf(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
   return bitsf(b[0]) + bitsf(b[1]);
-}
-
-// Value of x in lane `src` (uniform), through a scalar register.
-__device__ __forceinline__ float lane_value(float x, int src) {
-  return bitsf((unsigned)__builtin_amdgcn_readlane((int)fbits(x), src));
 }
 
 // ---------------------------------------------------------------- planning
@@ -274,7 +286,9 @@ __device__ long long wave_plan(const Params& P, long long* p_out, long long* q_o
   const int lane = threadIdx.x & 63;
   const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
   *lens_v = (int)len;
-  const unsigned cost = (unsigned)seq_cost(P, len);
+  // 32-bit cost (the planner is only used when every total fits 32 bits)
+  const unsigned cost =
+      len > 0 ? (unsigned)P.kv_heads * (unsigned)(cost_len(P, len) + P.seg_cost) : 0u;
   const unsigned incl = wave_incl_scan(cost);
   const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
   const long long Q = piece_len32(P, total);
@@ -324,7 +338,7 @@ __device__ __forceinline__ bool more_segments(const Params& P, const Seg& s, lon
 // Clamped length of sequence b (b uniform): from the wave's length register
 // for batches <= 64 (lane b holds it), else through the scalar path.
 __device__ __forceinline__ int seq_len_of(const Params& P, int lens_v, int b) {
-  return P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, b)
+  return P.wave_planner ? __builtin_amdgcn_readlane(lens_v, b)
                        : seq_len_uniform(P.seq_lens, b, P.capacity);
 }
 
@@ -332,7 +346,7 @@ __device__ __forceinline__ int seq_len_of(const Params& P, int lens_v, int b) {
 // sequence). Only called while rows remain below p_end, so one exists.
 __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end, int lens_v) {
   const long long end = s.off + cost_len(P, s.len) + P.seg_cost;
-  if (s.g + 1 < kKvHeads) {
+  if (s.g + 1 < P.kv_heads) {
     s.g += 1;
   } else {
     int nb = s.b + 1;
@@ -382,9 +396,9 @@ __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (((r >> 4) & 1) << 2); }
 
 // Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
-// an LDS stage (K, then V) and the segment's 4 query rows into the wave's q
-// slot, in this order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros.
-// With live == false the buffers are empty: the same 9 loads return zeros
+// an LDS stage (K, then V) and the segment's G query rows into the wave's q
+// slot, in this order: q (1 or 2 loads), 4 x K, 4 x V. Rows at or past s.hi
+// read as zeros. With live == false the buffers are empty: the same loads return zeros
 // without touching memory, so every pipeline step has the same shape. The q
 // load is live only for a wave's first tile of a segment (live_q); later
 // tiles reuse the q registers, and their empty q load leaves zeros in the
@@ -434,19 +448,25 @@ __device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, i
 // rows of 128 B (E4M3). In LDS the rows are dense whatever the strides.
 // Paged caches (page size a multiple of 16): each 16-row half of a tile
 // lies in one page, whose offset the caller passes in pb.
-template <int F, bool kPaged>
+template <int F, bool kPaged, bool kG4>
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
                                            bool live_q, e16_t* stage, e16_t* qslot,
                                            const PageBases& pb) {
   constexpr int kRowBytes = row_bytes<F>();
   constexpr int kRows = tile_rows<F>();
   const int lane = threadIdx.x & 63;
-  const char* qg = reinterpret_cast<const char*>(P.q) + s.b * P.q_sb + (s.g * kGroup) * P.q_sh;
+  const int group = group_of<kG4>(P);
+  const char* qg = reinterpret_cast<const char*>(P.q) + s.b * P.q_sb + (s.g * group) * P.q_sh;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)qg, 0, live && live_q ? (int)(3 * P.q_sh + 2 * kDim) : 0, kBufferFlags);
-  // q: lane l loads 16 B of query row l/16 (of the group's 4), chunk l%16.
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_t*)qslot, 16,
-                                           (int)((lane >> 4) * P.q_sh) + 16 * (lane & 15), 0, 0, 0);
+      (void*)qg, 0, live && live_q ? (int)((group - 1) * P.q_sh + 2 * kDim) : 0, kBufferFlags);
+  // q: load u (one, or two in the general form) gives lane l 16 B of the
+  // group's query row 4u + l/16, chunk l%16; rows at or past G lie beyond
+  // the resource (or are masked when q rows overlap) and read as zeros.
+#pragma unroll
+  for (int u = 0; u < (kG4 ? 1 : 2); ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rq, (lds_void_t*)(reinterpret_cast<char*>(qslot) + 1024 * u), 16,
+        (int)((4 * u + (lane >> 4)) * P.q_sh) + 16 * (lane & 15), 0, 0, 0);
   const int nrows = live ? s.hi - t : 0;          // rows of this tile below s.hi
   // DMA lane l writes 16 B at LDS offset 16*l of the 1 KiB block u: for
   // 16-bit formats row 4u + l/16, physical chunk l%16, which holds logical
@@ -499,16 +519,18 @@ __device__ __forceinline__ unsigned lds_addr(const e16_t* p) {
 }
 
 struct WaveAcc {
-  float4_t O[8];     // PV accumulators (D layout): lane (0, j), reg r = head r, column 16*db + j
+  float4_t O[8];     // O^T accumulators (D layout): lane (G4, j), reg r = head j,
+                     // output column 16 db + 4 G4 + r
   float m;           // running max of head j (same in the 4 lane groups)
   float l;           // this lane group's share of head j's denominator
 };
 
-// q^T as the QK B operand, read from the wave's q slot: lane (G, j) takes
-// head j, depth 32kk + 8G .. +7; columns j >= 4 are zero.
-__device__ __forceinline__ void read_q(const e16_t* qslot, uint4_t (&qb)[4]) {
+// q^T as the QK B operand, read from the wave's q slot: lane (G4, j) takes
+// head j, depth 32kk + 8 G4 .. +7; columns j >= G are zero.
+template <bool kG4>
+__device__ __forceinline__ void read_q(const e16_t* qslot, int group, uint4_t (&qb)[4]) {
   const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
-  int row = j & 3;
+  int row = j & (kG4 ? 3 : 7);
   asm volatile("" : "+v"(row));
   const unsigned base = lds_addr(qslot) + 2 * (row * kDim + 8 * G);
   uint4_t x0, x1, x2, x3;
@@ -522,10 +544,10 @@ __device__ __forceinline__ void read_q(const e16_t* qslot, uint4_t (&qb)[4]) {
       : "v"(base)
       : "memory");
   const uint4_t zero = {0u, 0u, 0u, 0u};
-  qb[0] = j < kGroup ? x0 : zero;
-  qb[1] = j < kGroup ? x1 : zero;
-  qb[2] = j < kGroup ? x2 : zero;
-  qb[3] = j < kGroup ? x3 : zero;
+  qb[0] = j < group ? x0 : zero;
+  qb[1] = j < group ? x1 : zero;
+  qb[2] = j < group ? x2 : zero;
+  qb[3] = j < group ? x3 : zero;
 }
 
 // LDS addresses of this lane's operand reads in stage 0 of its wave; stage 1
@@ -744,20 +766,14 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   }
   acc.l = acc.l * alpha + psum;
 
-  const float a0 = lane_value(alpha, 0), a1 = lane_value(alpha, 1), a2 = lane_value(alpha, 2),
-              a3 = lane_value(alpha, 3);
+  // O^T = V^T P^T: every accumulator of this lane belongs to head j.
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    acc.O[db][0] *= a0;
-    acc.O[db][1] *= a1;
-    acc.O[db][2] *= a2;
-    acc.O[db][3] *= a3;
-  }
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    const half8_t vb = e4m3x8_to_f16(vr[db]);
-    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vb, acc.O[db], 0, 0, 0);
-    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, acc.O[db], 0, 0, 0);
+    const half8_t va = e4m3x8_to_f16(vr[db]);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, ph, acc.O[db], 0, 0, 0);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pl, acc.O[db], 0, 0, 0);
   }
 }
 
@@ -811,22 +827,15 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   }
   acc.l = acc.l * alpha + psum;
 
-  // Row r of every PV tile is head r; lane h holds head h's alpha.
-  const float a0 = lane_value(alpha, 0), a1 = lane_value(alpha, 1), a2 = lane_value(alpha, 2),
-              a3 = lane_value(alpha, 3);
+  // O^T = V^T P^T: every accumulator of this lane belongs to head j.
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    acc.O[db][0] *= a0;
-    acc.O[db][1] *= a1;
-    acc.O[db][2] *= a2;
-    acc.O[db][3] *= a3;
-  }
+  for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
 
   const short4_t vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    acc.O[db] = mfma_pv<kBf16>(ph, vv[db], acc.O[db]);
-    acc.O[db] = mfma_pv<kBf16>(pl, vv[db], acc.O[db]);
+    acc.O[db] = mfma_pv<kBf16>(vv[db], ph, acc.O[db]);
+    acc.O[db] = mfma_pv<kBf16>(vv[db], pl, acc.O[db]);
   }
 }
 
@@ -835,18 +844,19 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
 // group) into `nxt` and the q slot; wait for the current tile; fold it in.
 // Loads complete in issue order, so "all but the newest N" waits are exact
 // (vector stores issued in between only make them wait longer).
-template <int F, bool kPaged>
+template <int F, bool kPaged, bool kG4>
 __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, int par,
                                           e16_t* nxt, e16_t* qslot, bool first,
                                           bool has_next, const Seg& nseg, int nt,
                                           bool next_new_seg, const PageBases& npb, int t, int hi,
                                           uint4_t (&qb)[4], WaveAcc& acc) {
   if (first) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile - 1) : "memory");   // q landed
-    read_q(qslot, qb);
+    // the q loads (the first 1 or 2 of the group) landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<kG4>() - (kG4 ? 1 : 2)) : "memory");
+    read_q<kG4>(qslot, group_of<kG4>(P), qb);
   }
-  issue_tile<F, kPaged>(P, nseg, nt, has_next, next_new_seg, nxt, qslot, npb);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerTile) : "memory");       // K, V landed
+  issue_tile<F, kPaged, kG4>(P, nseg, nt, has_next, next_new_seg, nxt, qslot, npb);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<kG4>()) : "memory");   // K, V landed
   if constexpr (F == kFmtE4m3)
     compute_tile8(la, par, qb, t, hi, P.scale_log2, acc);
   else
@@ -860,48 +870,118 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Softmax state of each wave for the wave merge. In the general form the
+// waves' O^T rows go to each wave's free LDS stage (the stage no load is in
+// flight into), so the merge needs no LDS of its own beyond these words; the
+// kG4 form has a dedicated buffer for its 4 rows per wave (MergeRows4).
 struct MergeLds {
-  float m[kWaves][kGroup];
-  float l[kWaves][kGroup];
-  float acc[kWaves][kGroup][kDim];
+  float m[kWaves][kMaxGroup];
+  float l[kWaves][kMaxGroup];
+  int free_stage[kWaves];
 };
 
-// Merge the 4 waves' states. Thread t ends with head hh = t / 64 and the
-// columns d, d+1 (d = 2 * (t % 64)): max M, denominator den, sums n0, n1.
-__device__ __forceinline__ void merge_waves(const WaveAcc& acc, MergeLds& sm, float& M,
-                                            float& den, float& n0, float& n1) {
+constexpr int kMergeRow = kDim + 4;   // floats per head row in a merge buffer (bank spread)
+static_assert(kWaves == 4, "merge_waves reads one row per wave in a 4-read asm block");
+
+struct MergeRows4 {
+  float acc[kWaves][4][kMergeRow];
+};
+struct NoRows {
+  int unused;
+};
+template <bool kG4> struct MergeRowsOf { typedef NoRows type; };
+template <> struct MergeRowsOf<true> { typedef MergeRows4 type; };
+
+// Merge outputs per thread: heads t / 64 + 4k for k below this.
+template <bool kG4> constexpr int heads_per_thread() { return kG4 ? 1 : kMaxGroup / kWaves; }
+
+// Merge the 4 waves' states. Thread t ends with heads hh = t / 64 + 4k
+// (k < heads_per_thread, for hh < G) and the columns d, d + 1
+// (d = 2 * (t % 64)): max M[k], denominator den[k], sums n0[k], n1[k].
+// General form: `par` is this wave's pipeline parity, and stage par ^ 1 of
+// the wave is free; the last barrier orders every read of the free stages
+// before the waves' next loads into them. kG4 form: rows4 is reused from
+// segment to segment, so the first barrier orders the previous merge's
+// reads before this merge's writes.
+template <bool kG4>
+__device__ __forceinline__ void merge_waves(const WaveAcc& acc, int group, int par, MergeLds& sm,
+                                            e16_t (*stages)[2][kStageHalves], MergeRows4* rows4,
+                                            float (&M)[heads_per_thread<kG4>()],
+                                            float (&den)[heads_per_thread<kG4>()],
+                                            float (&n0)[heads_per_thread<kG4>()],
+                                            float (&n1)[heads_per_thread<kG4>()]) {
+  constexpr int kHeads = heads_per_thread<kG4>();
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int G = lane >> 4, j = lane & 15;
+  const int G4 = lane >> 4, j = lane & 15;
   const float kNegInf = -__builtin_inff();
   const float l = sum_over_row_groups(acc.l);
-  lds_barrier();     // earlier readers of sm are done
-  if (lane < kGroup) {
+  if constexpr (kG4) lds_barrier();     // the previous merge's readers are done
+  if (lane < group) {
     sm.m[wv][lane] = acc.m;
     sm.l[wv][lane] = l;
   }
-  if (G == 0) {
+  if constexpr (kG4) {
+    if (j < 4) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<float4_t*>(&rows4->acc[wv][j][16 * db + 4 * G4]) = acc.O[db];
+    }
+  } else {
+    if (lane == 0) sm.free_stage[wv] = par ^ 1;
+    // The stage accesses are asm: the compiler would otherwise make them wait
+    // for every load in flight (the next tile's loads also write LDS stages).
+    if (j < group) {
+      const unsigned base = lds_addr(stages[wv][par ^ 1]) + 4 * (j * kMergeRow + 4 * G4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.acc[wv][r][16 * db + j] = acc.O[db][r];
+      for (int db = 0; db < 8; ++db)
+        asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(base), "v"(acc.O[db]), "i"(64 * db)
+                     : "memory");
     }
   }
   lds_barrier();
-  const int hh = tid >> 6, d = (tid & 63) * 2;
-  M = kNegInf;
+  const int d = (tid & 63) * 2;
+  unsigned bufs[kWaves];
+  if constexpr (!kG4) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][hh]);
-  den = 0.f;
-  n0 = 0.f;
-  n1 = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float ms = sm.m[w][hh];
-    const float wt = (ms == kNegInf) ? 0.f : exp2_hw(ms - M);   // waves without rows
-    den += wt * sm.l[w][hh];
-    n0 += wt * sm.acc[w][hh][d];
-    n1 += wt * sm.acc[w][hh][d + 1];
+    for (int w = 0; w < kWaves; ++w) bufs[w] = lds_addr(stages[w][sm.free_stage[w]]);
   }
+#pragma unroll
+  for (int k = 0; k < kHeads; ++k) {
+    const int hh = (tid >> 6) + kWaves * k;
+    M[k] = kNegInf;
+    den[k] = 0.f;
+    n0[k] = 0.f;
+    n1[k] = 0.f;
+    if (hh >= group) continue;
+    float2 x[kWaves];
+    if constexpr (kG4) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        x[w] = *reinterpret_cast<const float2*>(&rows4->acc[w][hh][d]);
+    } else {
+      const unsigned off = 4 * (hh * kMergeRow + d);
+      asm volatile(
+          "ds_read_b64 %0, %4\n\t"
+          "ds_read_b64 %1, %5\n\t"
+          "ds_read_b64 %2, %6\n\t"
+          "ds_read_b64 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+          : "v"(bufs[0] + off), "v"(bufs[1] + off), "v"(bufs[2] + off), "v"(bufs[3] + off)
+          : "memory");
+    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M[k] = fmaxf(M[k], sm.m[w][hh]);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float ms = sm.m[w][hh];
+      const float wt = (ms == kNegInf) ? 0.f : exp2_hw(ms - M[k]);   // waves without rows
+      den[k] = __builtin_fmaf(wt, sm.l[w][hh], den[k]);
+      n0[k] = __builtin_fmaf(wt, x[w].x, n0[k]);
+      n1[k] = __builtin_fmaf(wt, x[w].y, n1[k]);
+    }
+  }
+  if constexpr (!kG4) lds_barrier();
 }
 
 // Partial slot of a segment in piece w: 2w for the piece's first segment,
@@ -930,10 +1010,11 @@ __device__ __forceinline__ void zero_empty_sequences(const Params& P, int lens_v
   const int tid = threadIdx.x;
   for (int b = w; b < P.batch; b += gridDim.x) {
     if (seq_len_of(P, lens_v, b) == 0) {
-      uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * kQHeads * kDim);
-      dst[tid] = (uint4_t){0u, 0u, 0u, 0u};
-      dst[tid + kThreads] = (uint4_t){0u, 0u, 0u, 0u};
-      if (!P.fused && tid < kKvHeads) P.seg_desc[b * kKvHeads + tid] = make_int2(0, 0);
+      uint4_t* dst = reinterpret_cast<uint4_t*>(P.out + (size_t)b * P.q_heads * kDim);
+      for (int i = tid; i < P.q_heads * (kDim / 8); i += kThreads) dst[i] = (uint4_t){0u, 0u, 0u, 0u};
+      if (!P.fused)
+        for (int g = tid; g < P.kv_heads; g += kThreads)
+          P.seg_desc[(size_t)b * P.kv_heads + g] = make_int2(0, 0);
     }
   }
 }
@@ -958,61 +1039,63 @@ __device__ __forceinline__ float2 load_partial(const float2* p) {
                                 __HIP_MEMORY_SCOPE_AGENT));
 }
 
-constexpr int kCombineSubsets = 4;   // x 64 (head, 8-column group) pairs = 256 threads
-
 struct CombineLds {
-  float xs[kCombineSubsets][64][10];
+  float xs[kThreads][10];
 };
 
 // Merge the n partials of segment (b, g), which kernel 1 cut into pieces
-// first_w .. first_w + n - 1, and write the group's 4 output rows. All 256
-// threads take part. Thread t takes head (t / 16) % 4, columns 8 * (t % 16)
-// .. +7, and every 4th partial from t / 64: a running max over independent
-// loads. The 4 subsets are then merged through LDS, in a fixed order, so
-// results do not depend on timing or on which workgroup runs the merge.
+// first_w .. first_w + n - 1, and write the group's G output rows. The 16 G
+// (head, 8-column group) pairs are spread over the 256 threads: thread t
+// takes pair t % 16G (head pair / 16, columns 8 (pair % 16) .. +7) and, as
+// subset t / 16G of S = 256 / 16G subsets (threads past S subsets idle),
+// every S-th partial: a running max over batches of independent loads. The
+// subsets are then merged through LDS, in a fixed order, so results do not
+// depend on timing or on which workgroup runs the merge.
 // Partial i lives in piece first_w + i: the first piece holds it in its
 // second slot if the segment starts inside that piece (bit), every later
 // piece holds it as its first segment.
 // kCoherent: the partials were written in this launch (single-launch form)
 // and are read with device-scope loads.
-template <bool kBf16, bool kCoherent>
+template <bool kBf16, bool kCoherent, bool kG4>
 __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, int first_w, int n,
                                                 int bit, CombineLds& lds) {
   const int tid = threadIdx.x;
+  const int group = group_of<kG4>(P), npairs = 16 * group, nsub = kThreads / npairs;
   const long long slot0 = 2LL * first_w + bit;
-  const int pair = tid & 63, sub = tid >> 6;
+  const int pair = tid % npairs, sub = tid / npairs;
   const int hh = pair >> 4, c8 = (pair & 15) * 8;
   const float kNegInf = -__builtin_inff();
   float M = kNegInf, den = 0.f;
   float4_t na = {0.f, 0.f, 0.f, 0.f}, nb = {0.f, 0.f, 0.f, 0.f};
-  // Partials sub, sub + 4, ... in batches of kBatch: a batch's loads are all
+  // Partials sub, sub + S, ... in batches of kBatch: a batch's loads are all
   // issued before its first use, then merged one by one in index order.
   constexpr int kBatch = 4;
-  for (int i0 = sub; i0 < n; i0 += kBatch * kCombineSubsets) {
+  const int first = sub < nsub ? sub : n;            // idle threads take no partials
+  for (int i0 = first; i0 < n; i0 += kBatch * nsub) {
     float2 ml[kBatch];
     float4_t a0[kBatch], a1[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * kCombineSubsets;
+      const int i = i0 + u * nsub;
       if (i >= n) break;
       const long long sl = i == 0 ? slot0 : 2LL * (first_w + i);
-      const float* src = P.ws_acc + (sl * kGroup + hh) * kDim + c8;
+      const float* src = P.ws_acc + (sl * group + hh) * kDim + c8;
       if constexpr (kCoherent) {
-        ml[u] = load_partial(P.ws_ml + sl * kGroup + hh);
+        ml[u] = load_partial(P.ws_ml + sl * group + hh);
         const float2* s2 = reinterpret_cast<const float2*>(src);
         const float2 x0 = load_partial(s2), x1 = load_partial(s2 + 1);
         const float2 x2 = load_partial(s2 + 2), x3 = load_partial(s2 + 3);
         a0[u] = (float4_t){x0.x, x0.y, x1.x, x1.y};
         a1[u] = (float4_t){x2.x, x2.y, x3.x, x3.y};
       } else {
-        ml[u] = P.ws_ml[sl * kGroup + hh];
+        ml[u] = P.ws_ml[sl * group + hh];
         a0[u] = *reinterpret_cast<const float4_t*>(src);
         a1[u] = *reinterpret_cast<const float4_t*>(src + 4);
       }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      if (i0 + u * kCombineSubsets >= n) break;
+      if (i0 + u * nsub >= n) break;
       // Explicit fused multiply-adds: the same operations wherever this
       // function is inlined (the two launch forms must agree bitwise).
       const float Mn = fmaxf(M, ml[u].x);
@@ -1026,7 +1109,7 @@ __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, i
       M = Mn;
     }
   }
-  float* x = lds.xs[sub][pair];
+  float* x = lds.xs[tid];
   x[0] = M;
   x[1] = den;
 #pragma unroll
@@ -1035,14 +1118,12 @@ __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, i
     x[6 + k] = nb[k];
   }
   __syncthreads();
-  if (tid < 64) {
+  if (tid < npairs) {
     float Mx = kNegInf;
-#pragma unroll
-    for (int k = 0; k < kCombineSubsets; ++k) Mx = fmaxf(Mx, lds.xs[k][pair][0]);
+    for (int k = 0; k < nsub; ++k) Mx = fmaxf(Mx, lds.xs[k * npairs + pair][0]);
     float d = 0.f, o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < kCombineSubsets; ++k) {
-      const float* y = lds.xs[k][pair];
+    for (int k = 0; k < nsub; ++k) {
+      const float* y = lds.xs[k * npairs + pair];
       const float wt = (y[0] == kNegInf) ? 0.f : exp2_hw(y[0] - Mx);   // subsets without partials
       d = __builtin_fmaf(wt, y[1], d);
 #pragma unroll
@@ -1054,12 +1135,12 @@ __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, i
     for (int c = 0; c < 4; ++c)
       r[c] = (unsigned)to_elem<kBf16>(o[2 * c] / d * vs) |
              ((unsigned)to_elem<kBf16>(o[2 * c + 1] / d * vs) << 16);
-    *reinterpret_cast<uint4_t*>(P.out + ((size_t)b * kQHeads + g * kGroup + hh) * kDim + c8) = r;
+    *reinterpret_cast<uint4_t*>(P.out + ((size_t)b * P.q_heads + g * group + hh) * kDim + c8) = r;
   }
 }
 
 // ---------------------------------------------------------------- kernel 1
-template <int F, bool kPaged>
+template <int F, bool kPaged, bool kG4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(Params P) {
   constexpr bool kBf16 = F == kFmtBf16;
@@ -1068,14 +1149,13 @@ void gqa_decode_pieces(Params P) {
   __shared__ long long sh_found;
   __shared__ int sh_found_b, sh_found_len;
   __shared__ __attribute__((aligned(16))) e16_t stages[kWaves][2][kStageHalves];
-  __shared__ __attribute__((aligned(16))) e16_t qslots[kWaves][kQHalves];
-  // The wave merge and the single-launch combine use the same LDS.
-  __shared__ __attribute__((aligned(16))) union {
-    MergeLds merge;
-    CombineLds combine;
-  } tail;
+  __shared__ __attribute__((aligned(16))) e16_t qslots[kWaves][q_halves<kG4>()];
+  __shared__ MergeLds sm;
+  __shared__ __attribute__((aligned(16))) typename MergeRowsOf<kG4>::type rows4_lds;
+  MergeRows4* rows4 = nullptr;
+  if constexpr (kG4) rows4 = &rows4_lds;
   __shared__ int sh_last[2];
-  __shared__ int sh_cut[2][3];   // single launch: (8 * b + g, first piece, n2) of cut segments
+  __shared__ int sh_cut[2][3];   // single launch: (Hkv * b + g, first piece, n2) of cut segments
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
@@ -1085,7 +1165,7 @@ void gqa_decode_pieces(Params P) {
   long long total, p0, found, Qw = 0;
   int found_b, found_len = 0;
   int lens_v = 0;
-  if (P.batch <= 64) {
+  if (P.wave_planner) {
     total = wave_plan(P, &p0, &Qw, &found, &found_b, &lens_v);
   } else {
     long long part = 0;
@@ -1110,18 +1190,21 @@ void gqa_decode_pieces(Params P) {
   }
   found = uniform64(found);
   found_b = __builtin_amdgcn_readfirstlane(found_b);
-  const long long Q = P.batch <= 64 ? uniform64(Qw) : piece_len(P, total);
+  const long long Q = P.wave_planner ? uniform64(Qw) : piece_len(P, total);
   const long long p1 = p0 + Q < total ? p0 + Q : total;
 
   Seg s;
   s.b = found_b;
-  s.len = P.batch <= 64 ? __builtin_amdgcn_readlane(lens_v, s.b)
-                        : __builtin_amdgcn_readfirstlane(found_len);
+  s.len = P.wave_planner ? __builtin_amdgcn_readlane(lens_v, s.b)
+                         : __builtin_amdgcn_readfirstlane(found_len);
   const long long stride = cost_len(P, s.len) + P.seg_cost;
-  // (p0 - found) / stride, which is below 8: by comparison, no division
+  // g = (p0 - found) / stride, which is below Hkv: a float estimate (off by
+  // at most one), then exact integer corrections; no 64-bit division.
   const long long rel = p0 - found;
-  s.g = 0;
-  while (s.g < kKvHeads - 1 && (long long)(s.g + 1) * stride <= rel) ++s.g;
+  s.g = (int)((float)rel * __builtin_amdgcn_rcpf((float)stride));
+  s.g = s.g < 0 ? 0 : (s.g > P.kv_heads - 1 ? P.kv_heads - 1 : s.g);
+  while (s.g > 0 && (long long)s.g * stride > rel) --s.g;
+  while (s.g < P.kv_heads - 1 && (long long)(s.g + 1) * stride <= rel) ++s.g;
   s.off = found + (long long)s.g * stride + P.seg_cost;
   seg_set_range(s, p0, p1);
   if (s.hi <= s.lo) {                               // only fixed-cost units in this piece
@@ -1139,7 +1222,7 @@ void gqa_decode_pieces(Params P) {
   const bool pf_ok = tile_first<kRows>(P, pf, pt, p1, wv, lens_v);
   PageBases pbs;                                    // paged: pages of the issued tile
   if constexpr (kPaged) pbs = page_bases<kRows>(P, pf, pt, pf_ok);
-  issue_tile<F, kPaged>(P, pf, pt, pf_ok, true, st0, qslot, pbs);
+  issue_tile<F, kPaged, kG4>(P, pf, pt, pf_ok, true, st0, qslot, pbs);
   zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
   // Single launch: the number of segments this piece cut (at most its first
@@ -1159,16 +1242,19 @@ void gqa_decode_pieces(Params P) {
       int nt = pt;
       const bool n_ok = tile_next<kRows>(P, nf, nt, p1, wv, lens_v);
       if constexpr (kPaged) pbs = page_bases<kRows>(P, nf, nt, n_ok);
-      tile_step<F, kPaged>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
+      tile_step<F, kPaged, kG4>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
                 nf.off != s.off, pbs, t, s.hi, qb, acc);
       pf = nf;
       pt = nt;
       par ^= 1;
     }
 
-    float M, den, n0, n1;
-    merge_waves(acc, tail.merge, M, den, n0, n1);
-    const int hh = tid >> 6, d = (tid & 63) * 2;
+    constexpr int kHeads = heads_per_thread<kG4>();
+    const int group = group_of<kG4>(P);
+    float M[kHeads], den[kHeads], n0[kHeads], n1[kHeads];
+    merge_waves<kG4>(acc, group, par, sm, stages, rows4, M, den, n0, n1);
+    const int d = (tid & 63) * 2;
+    const int seg_id = s.b * P.kv_heads + s.g;
 
     const long long seg_end = s.off + s.len;
     const long long first_w = s.off / Q, last_w = (seg_end - 1) / Q;
@@ -1176,25 +1262,36 @@ void gqa_decode_pieces(Params P) {
     // piece, whose second slot then holds its partial)
     const int n2 = (int)(2 * (last_w - first_w + 1)) + (s.off > first_w * Q ? 1 : 0);
     if (!P.fused && first_w == w && tid == 0)        // the segment starts in this piece
-      P.seg_desc[s.b * kKvHeads + s.g] = make_int2(w, n2);
+      P.seg_desc[seg_id] = make_int2(w, n2);
     if (first_w == last_w) {                         // the segment lies in this piece
       const float vs = P.out_scale;
-      const unsigned o = (unsigned)to_elem<kBf16>(n0 / den * vs) |
-                         ((unsigned)to_elem<kBf16>(n1 / den * vs) << 16);
-      *reinterpret_cast<unsigned*>(P.out + ((size_t)s.b * kQHeads + s.g * kGroup + hh) * kDim + d) = o;
+#pragma unroll
+      for (int k = 0; k < kHeads; ++k) {
+        const int hh = (tid >> 6) + kWaves * k;
+        if (hh >= group) continue;
+        const unsigned o = (unsigned)to_elem<kBf16>(n0[k] / den[k] * vs) |
+                           ((unsigned)to_elem<kBf16>(n1[k] / den[k] * vs) << 16);
+        *reinterpret_cast<unsigned*>(
+            P.out + ((size_t)s.b * P.q_heads + s.g * group + hh) * kDim + d) = o;
+      }
     } else {
       const long long slot = slot_of(s.off, p0, w);
-      float2* acc_dst = reinterpret_cast<float2*>(P.ws_acc + (slot * kGroup + hh) * kDim + d);
-      float2* ml_dst = P.ws_ml + slot * kGroup + hh;
-      if (P.fused) {
-        store_partial(acc_dst, make_float2(n0, n1));
-        if (d == 0) store_partial(ml_dst, make_float2(M, den));
-      } else {
-        *acc_dst = make_float2(n0, n1);
-        if (d == 0) *ml_dst = make_float2(M, den);
+#pragma unroll
+      for (int k = 0; k < kHeads; ++k) {
+        const int hh = (tid >> 6) + kWaves * k;
+        if (hh >= group) continue;
+        float2* acc_dst = reinterpret_cast<float2*>(P.ws_acc + (slot * group + hh) * kDim + d);
+        float2* ml_dst = P.ws_ml + slot * group + hh;
+        if (P.fused) {
+          store_partial(acc_dst, make_float2(n0[k], n1[k]));
+          if (d == 0) store_partial(ml_dst, make_float2(M[k], den[k]));
+        } else {
+          *acc_dst = make_float2(n0[k], n1[k]);
+          if (d == 0) *ml_dst = make_float2(M[k], den[k]);
+        }
       }
       if (P.fused && tid == 0) {
-        sh_cut[ncut][0] = s.b * kKvHeads + s.g;
+        sh_cut[ncut][0] = seg_id;
         sh_cut[ncut][1] = (int)first_w;
         sh_cut[ncut][2] = n2;
       }
@@ -1211,7 +1308,8 @@ void gqa_decode_pieces(Params P) {
   // after all of this piece's segments, so the pipeline never waits on them.
   if (P.fused && ncut > 0) {
     // Every wave's partial stores (device-scope) complete before the
-    // tickets are taken.
+    // tickets are taken. This also drains the last (empty) tile loads into
+    // LDS, so the stages are free for the merge below.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid < ncut) {
@@ -1231,8 +1329,8 @@ void gqa_decode_pieces(Params P) {
       const int seg = __builtin_amdgcn_readfirstlane(sh_cut[i][0]);
       const int fw = __builtin_amdgcn_readfirstlane(sh_cut[i][1]);
       const int n2 = __builtin_amdgcn_readfirstlane(sh_cut[i][2]);
-      combine_segment<kBf16, true>(P, seg / kKvHeads, seg % kKvHeads, fw, n2 >> 1, n2 & 1,
-                                   tail.combine);
+      combine_segment<kBf16, true, kG4>(P, seg / P.kv_heads, seg % P.kv_heads, fw, n2 >> 1,
+                                        n2 & 1, *reinterpret_cast<CombineLds*>(&stages[0][0][0]));
     }
   }
 }
@@ -1243,23 +1341,32 @@ void gqa_decode_pieces(Params P) {
 // segment rather than per query head: 4x fewer waves to dispatch for large
 // batches, where most segments are not cut and their workgroups exit at
 // once.)
-template <int F>
+template <int F, bool kG4>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
   __shared__ __attribute__((aligned(16))) CombineLds lds;
-  const int seg = blockIdx.x, b = seg / kKvHeads, g = seg - b * kKvHeads;
+  const int seg = blockIdx.x, b = seg / P.kv_heads, g = seg - b * P.kv_heads;
   const int2 desc = P.seg_desc[seg];
   const int n = desc.y >> 1;
   if (n <= 1) return;                  // empty (zero rows) or finished by kernel 1
-  combine_segment<F == kFmtBf16, false>(P, b, g, desc.x, n, desc.y & 1, lds);
+  combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1, lds);
 }
 
 }  // namespace
 
 int resident_workgroups_per_cu() {
-  const void* kernels[6] = {
-      (const void*)gqa_decode_pieces<kFmtF16, false>, (const void*)gqa_decode_pieces<kFmtBf16, false>,
-      (const void*)gqa_decode_pieces<kFmtE4m3, false>, (const void*)gqa_decode_pieces<kFmtF16, true>,
-      (const void*)gqa_decode_pieces<kFmtBf16, true>, (const void*)gqa_decode_pieces<kFmtE4m3, true>};
+  const void* kernels[12] = {
+      (const void*)gqa_decode_pieces<kFmtF16, false, true>,
+      (const void*)gqa_decode_pieces<kFmtBf16, false, true>,
+      (const void*)gqa_decode_pieces<kFmtE4m3, false, true>,
+      (const void*)gqa_decode_pieces<kFmtF16, true, true>,
+      (const void*)gqa_decode_pieces<kFmtBf16, true, true>,
+      (const void*)gqa_decode_pieces<kFmtE4m3, true, true>,
+      (const void*)gqa_decode_pieces<kFmtF16, false, false>,
+      (const void*)gqa_decode_pieces<kFmtBf16, false, false>,
+      (const void*)gqa_decode_pieces<kFmtE4m3, false, false>,
+      (const void*)gqa_decode_pieces<kFmtF16, true, false>,
+      (const void*)gqa_decode_pieces<kFmtBf16, true, false>,
+      (const void*)gqa_decode_pieces<kFmtE4m3, true, false>};
   int m = 1 << 30;
   for (const void* k : kernels) {
     int n = 0;
@@ -1272,41 +1379,42 @@ int resident_workgroups_per_cu() {
   return m;
 }
 
-long long grid_for(int batch, int capacity, const SplitConfig& cfg) {
+long long grid_for(int batch, int capacity, int kv_heads, const SplitConfig& cfg) {
   if (cfg.forced_piece > 0) {
     const long long a = cfg.row_align > 1 ? cfg.row_align : 1;
-    const long long rows = 8LL * batch * ((capacity + a - 1) / a * a);
+    const long long rows = (long long)kv_heads * batch * ((capacity + a - 1) / a * a);
     return (rows + cfg.forced_piece - 1) / cfg.forced_piece;
   }
   return cfg.pieces;
 }
 
-size_t partial_bytes_for_grid(long long grid) {
-  return (size_t)(2 * grid) * kSlotFloats * sizeof(float);
+size_t partial_bytes_for_grid(long long grid, int group) {
+  return (size_t)(2 * grid) * group * kHeadSlotFloats * sizeof(float);
 }
 
-size_t segment_bytes_for_batch(int batch) {
-  return ((size_t)batch * kKvHeads * sizeof(int2) + 255) & ~(size_t)255;
+size_t segment_bytes_for_batch(int batch, int kv_heads) {
+  return ((size_t)batch * kv_heads * sizeof(int2) + 255) & ~(size_t)255;
 }
 
-template <int F, bool kPaged>
+template <int F, bool kPaged, bool kG4>
 hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
                           hipEvent_t* events) {
   hipError_t err = hipSuccess;
-  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * kKvHeads)), block(kThreads);
+  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * P.kv_heads)),
+      block(kThreads);
   if (events) {
     // Start/stop events attached to the dispatches: they time each kernel's
     // execution without extra packets between the kernels.
-    hipExtLaunchKernelGGL(gqa_decode_pieces<F, kPaged>, pieces_grid, block, 0, stream, events[0],
+    hipExtLaunchKernelGGL(gqa_decode_pieces<F, kPaged, kG4>, pieces_grid, block, 0, stream, events[0],
                           events[1], 0, P);
     if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
-    hipExtLaunchKernelGGL(gqa_decode_combine<F>, combine_grid, block, 0, stream, events[2],
+    hipExtLaunchKernelGGL(gqa_decode_combine<F, kG4>, combine_grid, block, 0, stream, events[2],
                           events[3], 0, P);
     return hipGetLastError();
   }
-  gqa_decode_pieces<F, kPaged><<<pieces_grid, block, 0, stream>>>(P);
+  gqa_decode_pieces<F, kPaged, kG4><<<pieces_grid, block, 0, stream>>>(P);
   if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
-  gqa_decode_combine<F><<<combine_grid, block, 0, stream>>>(P);
+  gqa_decode_combine<F, kG4><<<combine_grid, block, 0, stream>>>(P);
   return hipGetLastError();
 }
 
@@ -1322,11 +1430,16 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.kv = static_cast<const e16_t*>(kv);
   P.seq_lens = seq_lens;
   P.out = static_cast<e16_t*>(out);
+  const int group = layout.q_heads / layout.kv_heads;
   P.seg_desc = reinterpret_cast<int2*>(partials);
-  P.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) + segment_bytes_for_batch(batch));
-  P.ws_acc = reinterpret_cast<float*>(P.ws_ml + (size_t)(2 * grid) * kGroup);
+  P.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(partials) +
+                                      segment_bytes_for_batch(batch, layout.kv_heads));
+  P.ws_acc = reinterpret_cast<float*>(P.ws_ml + (size_t)(2 * grid) * group);
   P.batch = batch;
   P.capacity = capacity;
+  P.kv_heads = layout.kv_heads;
+  P.q_heads = layout.q_heads;
+  P.group = group;
   P.pieces = (int)grid;
   P.min_piece = cfg.min_piece;
   P.forced_piece = cfg.forced_piece;
@@ -1344,19 +1457,29 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.page_shift = layout.page_shift;
   P.num_pages = layout.num_pages;
   P.row_align = cfg.row_align > 1 ? cfg.row_align : 1;
+  // The one-wave planner adds up to 64 sequence costs in 32 bits.
+  {
+    const long long a = P.row_align;
+    const long long seg_max = (capacity + a - 1) / a * a + P.seg_cost;
+    P.wave_planner = batch <= 64 && (long long)batch * layout.kv_heads * seg_max < (1LL << 32);
+  }
 
   const bool paged = layout.block_table != nullptr;
+  const bool g4 = group == 4;
+#define GQA_LAUNCH(F)                                                              \
+  (paged ? (g4 ? launch_kernels<F, true, true>(P, grid, batch, stream, events)      \
+               : launch_kernels<F, true, false>(P, grid, batch, stream, events))    \
+         : (g4 ? launch_kernels<F, false, true>(P, grid, batch, stream, events)     \
+               : launch_kernels<F, false, false>(P, grid, batch, stream, events)))
   switch (elem) {
     case ElemType::kBf16:
-      return paged ? launch_kernels<kFmtBf16, true>(P, grid, batch, stream, events)
-                   : launch_kernels<kFmtBf16, false>(P, grid, batch, stream, events);
+      return GQA_LAUNCH(kFmtBf16);
     case ElemType::kE4m3Kv:
-      return paged ? launch_kernels<kFmtE4m3, true>(P, grid, batch, stream, events)
-                   : launch_kernels<kFmtE4m3, false>(P, grid, batch, stream, events);
+      return GQA_LAUNCH(kFmtE4m3);
     default:
-      return paged ? launch_kernels<kFmtF16, true>(P, grid, batch, stream, events)
-                   : launch_kernels<kFmtF16, false>(P, grid, batch, stream, events);
+      return GQA_LAUNCH(kFmtF16);
   }
+#undef GQA_LAUNCH
 }
 
 }  // namespace gqa

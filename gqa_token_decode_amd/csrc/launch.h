@@ -20,6 +20,7 @@ struct Layout {
   long long q_sb, q_sh, kv_sb, kv_sk, kv_sh, kv_sr;
   const int32_t* block_table;
   int max_pages, page_shift, num_pages;
+  int q_heads, kv_heads;   // q_heads a multiple of kv_heads, at most 8 times it
 };
 
 // How the device-side planner cuts the valid rows into pieces.
@@ -36,18 +37,20 @@ int resident_workgroups_per_cu();
 
 // Number of workgroups launched for this shape and split (forced pieces must
 // already be a multiple of cfg.row_align).
-long long grid_for(int batch, int capacity, const SplitConfig& cfg);
+long long grid_for(int batch, int capacity, int kv_heads, const SplitConfig& cfg);
 
-// Bytes of fp32 partial-result storage for a grid (two slots per workgroup).
-size_t partial_bytes_for_grid(long long grid);
+// Bytes of fp32 partial-result storage for a grid (two slots per workgroup,
+// `group` query heads each).
+size_t partial_bytes_for_grid(long long grid, int group);
 
 // Bytes of per-segment descriptors for a batch (rounded to 256).
-size_t segment_bytes_for_batch(int batch);
+size_t segment_bytes_for_batch(int batch, int kv_heads);
 
-// Enqueue the decode. `partials` must hold segment_bytes_for_batch(batch) +
-// partial_bytes_for_grid(grid) bytes. With `tickets` (8 * batch ints, zero
-// before the call and left zero by it) one launch does everything: the last
-// piece of each cut segment merges its partials. Without, two kernels run
+// Enqueue the decode. `partials` must hold segment_bytes_for_batch(batch,
+// kv_heads) + partial_bytes_for_grid(grid, group) bytes. With `tickets`
+// (kv_heads * batch ints, zero before the call and left zero by it) one
+// launch does everything: the last piece of each cut segment merges its
+// partials. Without, two kernels run
 // (pieces, then combine). `events` (may be null) points at four events:
 // start and stop of the pieces kernel, then start and stop of the combine
 // kernel (the last two are not recorded in the single-launch form).

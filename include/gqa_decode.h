@@ -44,6 +44,13 @@ extern "C" {
 #define GQA_NUM_KV_HEADS 8
 #define GQA_HEAD_DIM 128
 
+/* Other head counts (gqa_decode_ex): at most GQA_MAX_GROUP query heads share
+ * one KV head, at most GQA_MAX_KV_HEADS KV heads, and batch * num_kv_heads
+ * stays at or below GQA_MAX_SEGMENTS. */
+#define GQA_MAX_GROUP 8
+#define GQA_MAX_KV_HEADS 1024
+#define GQA_MAX_SEGMENTS (1 << 27)
+
 /* Largest supported capacity (rows per (sequence, KV head)). The kernels
  * address one (sequence, KV head) block of K or V with 32-bit byte offsets,
  * so a block stays below 2 GiB: 2^22 rows x 256 B = 1 GiB. */
@@ -158,7 +165,15 @@ int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, voi
  * tensor they describe (not bytes), must be non-negative, and must keep
  * every row 16-byte aligned (stride * element size a multiple of 16); each
  * 128-element head row is contiguous. The values for the contiguous layouts
- * of gqa_decode are given in brackets (C = capacity).
+ * of gqa_decode are given in brackets (C = capacity, Hq and Hkv the head
+ * counts).
+ *
+ * Head counts: num_q_heads (Hq) query heads and num_kv_heads (Hkv) KV heads;
+ * 0 for both selects the page's 32 and 8. Hq must be a multiple of Hkv with
+ * at most GQA_MAX_GROUP query heads per KV head; query head h reads KV head
+ * h / (Hq / Hkv) (contiguous groups, as SDPA's enable_gqa). q and out are
+ * then [batch, Hq, 128] and kv [batch, 2, Hkv, capacity, 128]. Multi-head
+ * (Hq = Hkv) and multi-query (Hkv = 1, Hq <= 8) attention are special cases.
  *
  * Paged cache (block_table != NULL): kv holds num_pages pages, each
  * [2][8][page_size][128] under the strides below (kv_stride_batch is then the
@@ -171,10 +186,10 @@ int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, voi
  * for that sequence is then meaningless).
  */
 typedef struct gqa_layout {
-  int64_t q_stride_batch;    /* q[b] -> q[b+1]                      [32*128]        */
+  int64_t q_stride_batch;    /* q[b] -> q[b+1]                      [Hq*128]        */
   int64_t q_stride_head;     /* q[b,h] -> q[b,h+1]                  [128]           */
-  int64_t kv_stride_batch;   /* kv[b] -> kv[b+1], or page -> page   [2*8*C*128]     */
-  int64_t kv_stride_kind;    /* K -> V                              [8*C*128]       */
+  int64_t kv_stride_batch;   /* kv[b] -> kv[b+1], or page -> page   [2*Hkv*C*128]   */
+  int64_t kv_stride_kind;    /* K -> V                              [Hkv*C*128]     */
   int64_t kv_stride_head;    /* KV head g -> g+1                    [C*128]         */
   int64_t kv_stride_row;     /* position i -> i+1                   [128]           */
   const int32_t* block_table; /* NULL, or device int32 [batch][max_pages], 4-byte
@@ -182,23 +197,26 @@ typedef struct gqa_layout {
   int max_pages;             /* paged: entries per block_table row                   */
   int page_size;             /* paged: positions per page, a power of two >= 16      */
   int num_pages;             /* paged: pages in kv                                   */
+  int num_q_heads;           /* Hq, or 0 (with num_kv_heads 0) for 32                */
+  int num_kv_heads;          /* Hkv, or 0 (with num_q_heads 0) for 8                 */
 } gqa_layout;
 
 /*
  * gqa_decode_ex -- gqa_decode_typed with explicit strides and an optional
  * page table.
  *
- * layout  NULL means the contiguous layouts (then identical to
- *         gqa_decode_typed). out stays a contiguous [batch, 32, 128] tensor.
+ * layout  NULL means the contiguous layouts with 32 and 8 heads (then
+ *         identical to gqa_decode_typed). out stays a contiguous
+ *         [batch, Hq, 128] tensor.
  * capacity  the largest position count of a sequence (lengths are clamped
  *         to it); for a paged cache at most max_pages * page_size.
  * chunk_len  as for gqa_decode_chunked; for a paged cache it is rounded up
  *         to a multiple of 16.
  * Limits (GQA_ERR_BAD_ARG): kv_stride_row must cover a row (256 B, or 128 B
  * for E4M3); kv_stride_row in bytes times capacity (paged: page_size) and
- * q_stride_head in bytes times 3 plus 256 must stay below 2^31 (32-bit
- * buffer offsets). The overlap check for out uses each tensor's address
- * range under its strides.
+ * q_stride_head in bytes times 7 plus 256 must stay below 2^31 (32-bit
+ * buffer offsets); head counts as above. The overlap check for out uses
+ * each tensor's address range under its strides.
  * Use: strided views (e.g. q as a slice of a packed projection output, or
  * an NHD cache [batch, capacity, 2, 8, 128] seen as [batch, 2, 8, capacity,
  * 128]) and paged caches, without copies.
@@ -225,8 +243,8 @@ void gqa_decode_release_workspace(void);
 /* How a decode call runs its combine step. */
 typedef enum gqa_launch_form {
   GQA_LAUNCH_AUTO = 0,    /* single launch when capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY
-                             and batch * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS, else two
-                             kernels (the default)                                           */
+                             and batch * KV heads * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS,
+                             else two kernels (the default)                                  */
   GQA_LAUNCH_SINGLE = 1,  /* one kernel: the last workgroup to finish a cut (sequence, KV
                              head) segment merges its partial results, found through a
                              per-segment atomic ticket                                       */
@@ -236,7 +254,7 @@ typedef enum gqa_launch_form {
 /* Bounds within which GQA_LAUNCH_AUTO picks the single launch (short
  * caches, where saving the second launch outweighs the ticket round trips). */
 #define GQA_SINGLE_LAUNCH_MAX_CAPACITY 512
-#define GQA_SINGLE_LAUNCH_MAX_ROWS 16384
+#define GQA_SINGLE_LAUNCH_MAX_ROWS 131072
 
 /*
  * gqa_decode_set_launch_form -- select the launch form of later calls (all

@@ -243,3 +243,20 @@ def test_layout_argument_errors(lib):
     assert _call_ex(lib, _layout(q_stride_batch=1 << 20), out=0x10000 + (1 << 20)) == ALIAS
     assert _call_ex(lib, _layout(block_table=0x40000 + 4096, max_pages=4, page_size=16,
                                  num_pages=9)) == ALIAS
+
+
+def test_head_count_argument_errors(lib):
+    expected = MISMATCH if _gpu_visible() else NO_DEVICE
+    for hq, hkv in [(64, 8), (28, 4), (16, 16), (8, 1), (1, 1), (0, 0)]:
+        lay = _layout(num_q_heads=hq, num_kv_heads=hkv, q_stride_batch=max(hq, 1) * 128)
+        assert _call_ex(lib, lay) == expected, (hq, hkv)
+    for hq, hkv in [(72, 8), (30, 4), (4, 8), (32, 0), (0, 8), (-32, -8), (9, 1), (2048, 2048)]:
+        lay = _layout(num_q_heads=hq, num_kv_heads=hkv)
+        assert _call_ex(lib, lay) == BAD_ARG, (hq, hkv)
+        assert "heads" in lib.gqa_decode_last_error().decode()
+    # batch * KV heads is bounded
+    lay = _layout(num_q_heads=256, num_kv_heads=256, q_stride_batch=256 * 128)
+    assert _call_ex(lib, lay, B=1 << 20) == BAD_SHAPE
+    # out extends over Hq rows per sequence: it must not reach kv
+    lay = _layout(num_q_heads=64, num_kv_heads=8, q_stride_batch=64 * 128)
+    assert _call_ex(lib, lay, out=0x20000000 - 2 * 64 * 128 * 2 + 256) == ALIAS

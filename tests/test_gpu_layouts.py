@@ -110,15 +110,15 @@ def test_packed_q_and_padded_rows_equal_contiguous_bitwise(elem):
 # ---------------------------------------------------------------- paged caches
 def _paginate(kv, lens, page_size, seed, spare=5, bad_tail=None):
     """Scatter each sequence's rows into pages of a shuffled pool. Returns
-    (kv_pages [num_pages, 2, 8, P, 128], block_table [B, max_pages])."""
+    (kv_pages [num_pages, 2, Hkv, P, 128], block_table [B, max_pages])."""
     torch = _torch()
-    B, _, _, C, D = kv.shape
+    B, _, H, C, D = kv.shape
     P = page_size
     max_pages = -(-C // P)
     num_pages = B * max_pages + spare
     rng = np.random.default_rng(seed)
     perm = rng.permutation(num_pages)
-    pages = _zeros_like_shape((num_pages, 2, 8, P, D), kv)
+    pages = _zeros_like_shape((num_pages, 2, H, P, D), kv)
     rp, rk = _raw(pages), _raw(kv)
     table = np.full((B, max_pages), -1 if bad_tail is None else bad_tail, dtype=np.int32)
     for b in range(B):

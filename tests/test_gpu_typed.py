@@ -60,6 +60,9 @@ class _Widened:
             def __getitem__(self, g):
                 return widen(arr[g])
 
+            def __len__(self):
+                return len(arr)
+
         return _Seq()
 
 
