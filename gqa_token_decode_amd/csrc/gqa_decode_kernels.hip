@@ -984,6 +984,11 @@ __device__ __forceinline__ void merge_waves(const WaveAcc& acc, int group, int p
   if constexpr (!kG4) lds_barrier();
 }
 
+// x / q for cost positions (both non-negative).
+__device__ __forceinline__ long long div_cost(const Params& P, long long x, long long q) {
+  return P.wave_planner ? (long long)((unsigned)x / (unsigned)q) : x / q;
+}
+
 // Partial slot of a segment in piece w: 2w for the piece's first segment,
 // 2w + 1 for a segment that starts strictly inside the piece (at most one of
 // those is cut by the piece's end).
@@ -1256,8 +1261,12 @@ void gqa_decode_pieces(Params P) {
     const int d = (tid & 63) * 2;
     const int seg_id = s.b * P.kv_heads + s.g;
 
+    // Pieces holding the segment's first and last rows: this one unless the
+    // segment starts before p0 (ends after p1); only then a division, in 32
+    // bits when every cost total fits them.
     const long long seg_end = s.off + s.len;
-    const long long first_w = s.off / Q, last_w = (seg_end - 1) / Q;
+    const long long first_w = s.off >= p0 ? w : div_cost(P, s.off, Q);
+    const long long last_w = seg_end <= p1 ? w : div_cost(P, seg_end - 1, Q);
     // 2 * (pieces holding rows of the segment) + (it starts inside its first
     // piece, whose second slot then holds its partial)
     const int n2 = (int)(2 * (last_w - first_w + 1)) + (s.off > first_w * Q ? 1 : 0);
