@@ -203,6 +203,9 @@ def main(argv=None):
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: read the cache as shuffled HND pages of this many positions "
                          "(gqa_decode_paged); 0: the contiguous cache")
+    ap.add_argument("--q-heads", type=int, default=32,
+                    help="query heads (with --kv-heads: other head counts, same lengths)")
+    ap.add_argument("--kv-heads", type=int, default=8, help="KV heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -229,7 +232,7 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.get(args.workload, args.elem)
+    w = workloads.get(args.workload, args.elem, q_heads=args.q_heads, kv_heads=args.kv_heads)
     kv_bytes = w.kv_bytes_read
     sum_len = int(w.valid_lengths.sum())
 
@@ -307,7 +310,9 @@ def main(argv=None):
     assert np.all(np.isfinite(res)), "non-finite decode output"
 
     achieved = kv_bytes / (pieces_us * 1e-6) / 1e9
-    traffic = traffic_from_profiles(args.workload) if args.elem == "f16" else None
+    default_heads = (args.q_heads, args.kv_heads) == (32, 8)
+    traffic = (traffic_from_profiles(args.workload)
+               if args.elem == "f16" and default_heads and args.page_size == 0 else None)
     line = {
         "metric": METRIC,
         "value": round(kv_bytes / (ms_per_step * 1e-3) / 1e9, 3),
@@ -326,7 +331,8 @@ def main(argv=None):
         "config": {
             "workload": args.workload,
             "description": workloads.describe(args.workload),
-            "batch": w.batch, "capacity": w.capacity, "q_heads": 32, "kv_heads": 8,
+            "batch": w.batch, "capacity": w.capacity, "q_heads": w.q_heads,
+            "kv_heads": w.kv_heads,
             "head_dim": 128, "sum_valid_len": sum_len, "kv_bytes_per_step": kv_bytes,
             "kv_copies_rotated": rot, "accumulate": "f32",
             "kv_layout": (f"paged, {args.page_size} positions per page, shuffled"

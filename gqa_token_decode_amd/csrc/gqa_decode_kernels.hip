@@ -99,6 +99,7 @@ template <int F> constexpr int row_bytes() { return F == kFmtE4m3 ? kDim : 2 * k
 constexpr unsigned kBufferFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
 constexpr int kHeadSlotFloats = 2 + kDim;   // one head of a partial: (max, den) + 128 sums
+constexpr int kCombinePerHeadBelow = 256;   // segments: below, the combine may split heads
 
 struct Params {
   const e16_t* q;
@@ -117,6 +118,7 @@ struct Params {
   int group;           // G = Hq / Hkv, 1 .. kMaxGroup
   int q_heads;         // Hq (rows of out per sequence)
   int wave_planner;    // 1: batch <= 64 and every cost total fits 32 bits
+  int combine_per_head;   // combine kernel: one workgroup per (segment, head)
   int pieces;          // automatic split: number of equal pieces
   int min_piece;       // automatic split: lower bound on the piece length
   int forced_piece;    // > 0: fixed piece length
@@ -1049,13 +1051,15 @@ struct CombineLds {
 };
 
 // Merge the n partials of segment (b, g), which kernel 1 cut into pieces
-// first_w .. first_w + n - 1, and write the group's G output rows. The 16 G
-// (head, 8-column group) pairs are spread over the 256 threads: thread t
-// takes pair t % 16G (head pair / 16, columns 8 (pair % 16) .. +7) and, as
-// subset t / 16G of S = 256 / 16G subsets (threads past S subsets idle),
-// every S-th partial: a running max over batches of independent loads. The
-// subsets are then merged through LDS, in a fixed order, so results do not
-// depend on timing or on which workgroup runs the merge.
+// first_w .. first_w + n - 1, and write output rows of heads head0 ..
+// head0 + nheads - 1 of the group (all G, or one). The 16 nheads (head,
+// 8-column group) pairs are spread over the 256 threads: thread t takes pair
+// t % 16 nheads (head head0 + pair / 16, columns 8 (pair % 16) .. +7) and,
+// as subset t / (16 nheads) of S = 256 / (16 nheads) subsets (threads past
+// S subsets idle), every S-th partial: a running max over batches of
+// independent loads. The subsets are then merged through LDS, in a fixed
+// order, so results do not depend on timing or on which workgroup runs the
+// merge.
 // Partial i lives in piece first_w + i: the first piece holds it in its
 // second slot if the segment starts inside that piece (bit), every later
 // piece holds it as its first segment.
@@ -1063,12 +1067,12 @@ struct CombineLds {
 // and are read with device-scope loads.
 template <bool kBf16, bool kCoherent, bool kG4>
 __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, int first_w, int n,
-                                                int bit, CombineLds& lds) {
+                                                int bit, int head0, int nheads, CombineLds& lds) {
   const int tid = threadIdx.x;
-  const int group = group_of<kG4>(P), npairs = 16 * group, nsub = kThreads / npairs;
+  const int group = group_of<kG4>(P), npairs = 16 * nheads, nsub = kThreads / npairs;
   const long long slot0 = 2LL * first_w + bit;
   const int pair = tid % npairs, sub = tid / npairs;
-  const int hh = pair >> 4, c8 = (pair & 15) * 8;
+  const int hh = head0 + (pair >> 4), c8 = (pair & 15) * 8;
   const float kNegInf = -__builtin_inff();
   float M = kNegInf, den = 0.f;
   float4_t na = {0.f, 0.f, 0.f, 0.f}, nb = {0.f, 0.f, 0.f, 0.f};
@@ -1338,26 +1342,43 @@ void gqa_decode_pieces(Params P) {
       const int seg = __builtin_amdgcn_readfirstlane(sh_cut[i][0]);
       const int fw = __builtin_amdgcn_readfirstlane(sh_cut[i][1]);
       const int n2 = __builtin_amdgcn_readfirstlane(sh_cut[i][2]);
-      combine_segment<kBf16, true, kG4>(P, seg / P.kv_heads, seg % P.kv_heads, fw, n2 >> 1,
-                                        n2 & 1, *reinterpret_cast<CombineLds*>(&stages[0][0][0]));
+      // the same subsets as the combine kernel: per head when it splits heads
+      CombineLds& clds = *reinterpret_cast<CombineLds*>(&stages[0][0][0]);
+      const int sb = seg / P.kv_heads, sg = seg % P.kv_heads;
+      if (P.combine_per_head) {
+        for (int h = 0; h < group_of<kG4>(P); ++h) {
+          if (h > 0) __syncthreads();              // the previous head's LDS reads are done
+          combine_segment<kBf16, true, kG4>(P, sb, sg, fw, n2 >> 1, n2 & 1, h, 1, clds);
+        }
+      } else {
+        combine_segment<kBf16, true, kG4>(P, sb, sg, fw, n2 >> 1, n2 & 1, 0, group_of<kG4>(P),
+                                          clds);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- kernel 2
-// Two-launch form: one workgroup per segment (b, g); if kernel 1 cut it into
-// several pieces, merge their partials, else exit. (One workgroup per
-// segment rather than per query head: 4x fewer waves to dispatch for large
-// batches, where most segments are not cut and their workgroups exit at
-// once.)
+// Two-launch form: one workgroup per segment (b, g), or per (segment, query
+// head) when segments are few (P.combine_per_head); if kernel 1 cut the
+// segment into several pieces, merge their partials, else exit. Per segment
+// for many segments: G x fewer waves to dispatch, and most exit at once.
+// Per head for few segments: G x more subsets share a segment's partials,
+// so each thread folds G x fewer of them in sequence.
 template <int F, bool kG4>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
   __shared__ __attribute__((aligned(16))) CombineLds lds;
-  const int seg = blockIdx.x, b = seg / P.kv_heads, g = seg - b * P.kv_heads;
+  const int group = group_of<kG4>(P);
+  const int seg = P.combine_per_head ? blockIdx.x / group : blockIdx.x;
+  const int b = seg / P.kv_heads, g = seg - b * P.kv_heads;
   const int2 desc = P.seg_desc[seg];
   const int n = desc.y >> 1;
   if (n <= 1) return;                  // empty (zero rows) or finished by kernel 1
-  combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1, lds);
+  if (P.combine_per_head)
+    combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1,
+                                               blockIdx.x - seg * group, 1, lds);
+  else
+    combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1, 0, group, lds);
 }
 
 }  // namespace
@@ -1409,7 +1430,8 @@ template <int F, bool kPaged, bool kG4>
 hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
                           hipEvent_t* events) {
   hipError_t err = hipSuccess;
-  const dim3 pieces_grid((unsigned)grid), combine_grid((unsigned)(batch * P.kv_heads)),
+  const dim3 pieces_grid((unsigned)grid),
+      combine_grid((unsigned)(batch * P.kv_heads * (P.combine_per_head ? P.group : 1))),
       block(kThreads);
   if (events) {
     // Start/stop events attached to the dispatches: they time each kernel's
@@ -1471,6 +1493,19 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
     const long long a = P.row_align;
     const long long seg_max = (capacity + a - 1) / a * a + P.seg_cost;
     P.wave_planner = batch <= 64 && (long long)batch * layout.kv_heads * seg_max < (1LL << 32);
+  }
+  // One combine workgroup per head when segments are few and are cut into
+  // more pieces than a whole-segment workgroup folds in one batch of loads
+  // (4 per subset, 256 / 16G subsets). Pieces per segment, estimated from
+  // the shape alone: the pieces shared by the segments, at most what one
+  // segment of full capacity spans.
+  {
+    const long long segs = (long long)batch * layout.kv_heads;
+    const long long piece_rows = cfg.forced_piece > 0 ? cfg.forced_piece : cfg.min_piece;
+    const long long span = (capacity + P.seg_cost) / (piece_rows > 0 ? piece_rows : 1) + 1;
+    const long long shared = cfg.forced_piece > 0 ? span : (grid + segs - 1) / segs;
+    const long long n_est = shared < span ? shared : span;
+    P.combine_per_head = segs < kCombinePerHeadBelow && n_est * group > 64 ? 1 : 0;
   }
 
   const bool paged = layout.block_table != nullptr;

@@ -221,43 +221,44 @@ def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
 WORKLOADS: Dict[str, tuple] = {
     "b1_c256_len200": (
         "batch 1, capacity 256, length 200, N(0,1), q_scale 1.0",
-        lambda e: build("b1_c256_len200", 1, 256, [200], elem=e),
+        lambda e, **kw: build("b1_c256_len200", 1, 256, [200], elem=e, **kw),
     ),
     "b8_c4096_nanfill": (
         "batch 8, capacity 4096, lengths U[1,4096], N(0,1), NaN beyond each length, q_scale 1.0",
-        lambda e: build("b8_c4096_nanfill", 2, 4096,
-                        lambda r: r.integers(1, 4096, 8, endpoint=True), fill="nan", elem=e),
+        lambda e, **kw: build("b8_c4096_nanfill", 2, 4096,
+                        lambda r: r.integers(1, 4096, 8, endpoint=True), fill="nan",
+                        elem=e, **kw),
     ),
     "b32_c8192_qs05": (
         "batch 32, capacity 8192, lengths U[1024,8192], N(0,1), q_scale 0.5",
-        lambda e: build("b32_c8192_qs05", 3, 8192,
+        lambda e, **kw: build("b32_c8192_qs05", 3, 8192,
                         lambda r: r.integers(1024, 8192, 32, endpoint=True), q_scale=0.5,
-                        elem=e),
+                        elem=e, **kw),
     ),
     "b64_c16384_skewed": (
         "batch 64, capacity 16384, 58 lengths U[16,512] + 6 lengths U[8192,16384] shuffled, "
         "q,V ~ N(0,1), K ~ N(0, std 2), q_scale 1.0",
-        lambda e: build("b64_c16384_skewed", 4, 16384, _cfg4_lengths, sigma_k=2.0, elem=e),
+        lambda e, **kw: build("b64_c16384_skewed", 4, 16384, _cfg4_lengths, sigma_k=2.0, elem=e, **kw),
     ),
     "b2_c131072_long": (
         "batch 2, capacity 131072, lengths [131072, 65537], N(0,1), q_scale 1.0",
-        lambda e: build("b2_c131072_long", 5, 131072, [131072, 65537], elem=e),
+        lambda e, **kw: build("b2_c131072_long", 5, 131072, [131072, 65537], elem=e, **kw),
     ),
     "page_b1_c64": (
         "page shape: batch 1, capacity 64, lengths [1]",
-        lambda e: build("page_b1_c64", 11, 64, [1], elem=e),
+        lambda e, **kw: build("page_b1_c64", 11, 64, [1], elem=e, **kw),
     ),
     "page_b4_c256": (
         "page shape: batch 4, capacity 256, lengths [64, 127, 191, 256]",
-        lambda e: build("page_b4_c256", 12, 256, [64, 127, 191, 256], elem=e),
+        lambda e, **kw: build("page_b4_c256", 12, 256, [64, 127, 191, 256], elem=e, **kw),
     ),
     "page_b1_c1024": (
         "page shape: batch 1, capacity 1024, lengths [1024]",
-        lambda e: build("page_b1_c1024", 13, 1024, [1024], elem=e),
+        lambda e, **kw: build("page_b1_c1024", 13, 1024, [1024], elem=e, **kw),
     ),
     "page_b1_c4096": (
         "page shape: batch 1, capacity 4096, lengths [3968]",
-        lambda e: build("page_b1_c4096", 14, 4096, [3968], elem=e),
+        lambda e, **kw: build("page_b1_c4096", 14, 4096, [3968], elem=e, **kw),
     ),
 }
 
@@ -267,10 +268,14 @@ SYNTHETIC = ["b1_c256_len200", "b8_c4096_nanfill", "b32_c8192_qs05",
 PAGE_SHAPES = ["page_b1_c64", "page_b4_c256", "page_b1_c1024", "page_b1_c4096"]
 
 
-def get(name: str, elem: str = "f16") -> Workload:
+def get(name: str, elem: str = "f16", q_heads: int = NUM_Q_HEADS,
+        kv_heads: int = NUM_KV_HEADS) -> Workload:
     """Named workload; elem="bf16" or "e4m3" draws it (same seed and recipe)
-    in that element type."""
-    return WORKLOADS[name][1](elem)
+    in that element type, and other head counts draw it with Hq query and
+    Hkv KV heads (same lengths)."""
+    if (q_heads, kv_heads) == (NUM_Q_HEADS, NUM_KV_HEADS):
+        return WORKLOADS[name][1](elem)
+    return WORKLOADS[name][1](elem, q_heads=q_heads, kv_heads=kv_heads)
 
 
 def describe(name: str) -> str:
