@@ -29,6 +29,8 @@ HIP_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the kernels' first 4 argument dwords arrive in scalar registers
+    "-mllvm", "-amdgpu-kernarg-preload-count=4",
 ]
 
 

@@ -276,17 +276,18 @@ __device__ __forceinline__ long long piece_len32(const Params& P, unsigned total
   return cost_len(P, Q);
 }
 
-// Small batches (<= 64): every wave finds the total and the batch entry of
+// Small batches (<= 64): raw_len is lane b's seq_lens[b] (loaded at kernel
+// entry). Every wave finds the total and the batch entry of
 // this workgroup's first cost position on its own (lane b holds sequence b),
 // with no workgroup barrier and no LDS traffic. The total fits 32 bits: at
 // most 64 * 8 * (2^22 + 16 + c0) units. Returns the total; *found_b = -1 if
 // the piece starts past it. *lens_v keeps the clamped lengths (lane b holds
 // sequence b's), so later segment steps read them with readlane instead of a
 // dependent memory load.
-__device__ long long wave_plan(const Params& P, long long* p_out, long long* q_out,
+__device__ long long wave_plan(const Params& P, int raw_len, long long* p_out, long long* q_out,
                                long long* found, int* found_b, int* lens_v) {
   const int lane = threadIdx.x & 63;
-  const long long len = lane < P.batch ? clamp_len(P.seq_lens[lane], P.capacity) : 0;
+  const long long len = lane < P.batch ? clamp_len(raw_len, P.capacity) : 0;
   *lens_v = (int)len;
   // 32-bit cost (the planner is only used when every total fits 32 bits)
   const unsigned cost =
@@ -1149,9 +1150,17 @@ __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, i
 }
 
 // ---------------------------------------------------------------- kernel 1
+// The leading scalar arguments repeat fields of P so that they arrive
+// preloaded in scalar registers (kernel-argument preloading, gfx950): the
+// lengths load is issued before the rest of the arguments have been read.
 template <int F, bool kPaged, bool kG4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gqa_decode_pieces(Params P) {
+void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Params P) {
+  int raw_len = 0;
+  if (wave_planner) {
+    const int ln = threadIdx.x & 63;
+    raw_len = ln < batch ? seq_lens[ln] : 0;
+  }
   constexpr bool kBf16 = F == kFmtBf16;
   constexpr int kRows = tile_rows<F>();
   __shared__ long long red[kWaves];
@@ -1175,7 +1184,7 @@ void gqa_decode_pieces(Params P) {
   int found_b, found_len = 0;
   int lens_v = 0;
   if (P.wave_planner) {
-    total = wave_plan(P, &p0, &Qw, &found, &found_b, &lens_v);
+    total = wave_plan(P, raw_len, &p0, &Qw, &found, &found_b, &lens_v);
   } else {
     long long part = 0;
     for (int b = tid; b < P.batch; b += kThreads)
@@ -1365,16 +1374,22 @@ void gqa_decode_pieces(Params P) {
 // for many segments: G x fewer waves to dispatch, and most exit at once.
 // Per head for few segments: G x more subsets share a segment's partials,
 // so each thread folds G x fewer of them in sequence.
+// The leading arguments repeat fields of P (preloaded, as for kernel 1).
 template <int F, bool kG4>
-__global__ __launch_bounds__(kThreads) void gqa_decode_combine(Params P) {
+__global__ __launch_bounds__(kThreads) void gqa_decode_combine(const int2* seg_desc, int per_head,
+                                                               int group_arg, Params P) {
   __shared__ __attribute__((aligned(16))) CombineLds lds;
-  const int group = group_of<kG4>(P);
-  const int seg = P.combine_per_head ? blockIdx.x / group : blockIdx.x;
+  const int group = kG4 ? 4 : group_arg;
+  const int seg = per_head ? blockIdx.x / group : blockIdx.x;
+  // A vector load (the index is hidden in a vector register): it is issued
+  // at once, without waiting for the scalar loads of the other arguments.
+  int vseg = seg;
+  asm volatile("" : "+v"(vseg));
+  const int2 desc = seg_desc[vseg];
   const int b = seg / P.kv_heads, g = seg - b * P.kv_heads;
-  const int2 desc = P.seg_desc[seg];
   const int n = desc.y >> 1;
   if (n <= 1) return;                  // empty (zero rows) or finished by kernel 1
-  if (P.combine_per_head)
+  if (per_head)
     combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1,
                                                blockIdx.x - seg * group, 1, lds);
   else
@@ -1437,15 +1452,17 @@ hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_
     // Start/stop events attached to the dispatches: they time each kernel's
     // execution without extra packets between the kernels.
     hipExtLaunchKernelGGL(gqa_decode_pieces<F, kPaged, kG4>, pieces_grid, block, 0, stream, events[0],
-                          events[1], 0, P);
+                          events[1], 0, P.seq_lens, P.batch, P.wave_planner, P);
     if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
     hipExtLaunchKernelGGL(gqa_decode_combine<F, kG4>, combine_grid, block, 0, stream, events[2],
-                          events[3], 0, P);
+                          events[3], 0, P.seg_desc, P.combine_per_head, P.group, P);
     return hipGetLastError();
   }
-  gqa_decode_pieces<F, kPaged, kG4><<<pieces_grid, block, 0, stream>>>(P);
+  gqa_decode_pieces<F, kPaged, kG4>
+      <<<pieces_grid, block, 0, stream>>>(P.seq_lens, P.batch, P.wave_planner, P);
   if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
-  gqa_decode_combine<F, kG4><<<combine_grid, block, 0, stream>>>(P);
+  gqa_decode_combine<F, kG4>
+      <<<combine_grid, block, 0, stream>>>(P.seg_desc, P.combine_per_head, P.group, P);
   return hipGetLastError();
 }
 
