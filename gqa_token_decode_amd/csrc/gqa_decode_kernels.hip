@@ -398,15 +398,6 @@ __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long
 // reads (rows r and r + 16 together) spread over the banks.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (((r >> 4) & 1) << 2); }
 
-// Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
-// an LDS stage (K, then V) and the segment's G query rows into the wave's q
-// slot, in this order: q (1 or 2 loads), 4 x K, 4 x V. Rows at or past s.hi
-// read as zeros. With live == false the buffers are empty: the same loads return zeros
-// without touching memory, so every pipeline step has the same shape. The q
-// load is live only for a wave's first tile of a segment (live_q); later
-// tiles reuse the q registers, and their empty q load leaves zeros in the
-// slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
-// rows of 128 B (E4M3).
 // Buffer resource over rows [row0, row0 + nrows) of one K or V block that
 // starts at `base` (row stride kv_sr bytes); rows past nrows read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, long long row0,
@@ -441,13 +432,13 @@ __device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, i
 }
 
 // Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
-// an LDS stage (K, then V) and the segment's 4 query rows into the wave's q
-// slot, in this order: q, 4 x K, 4 x V. Rows at or past s.hi read as zeros.
-// With live == false the buffers are empty: the same 9 loads return zeros
-// without touching memory, so every pipeline step has the same shape. The q
-// load is live only for a wave's first tile of a segment (live_q); later
-// tiles reuse the q registers, and their empty q load leaves zeros in the
-// slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
+// an LDS stage (K, then V) and the segment's G query rows into the wave's q
+// slot, in this order: q (1 load, or 2 in the general form), 4 x K, 4 x V.
+// Rows at or past s.hi read as zeros. With live == false the buffers are
+// empty: the same loads return zeros without touching memory, so every
+// pipeline step has the same shape. The q load is live only for a wave's
+// first tile of a segment (live_q); later tiles reuse the q registers, and
+// their empty q load leaves zeros in the slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
 // rows of 128 B (E4M3). In LDS the rows are dense whatever the strides.
 // Paged caches (page size a multiple of 16): each 16-row half of a tile
 // lies in one page, whose offset the caller passes in pb.

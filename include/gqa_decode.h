@@ -101,7 +101,10 @@ typedef enum gqa_status {
  * allocated on first need, so the first call on a new stream, or one needing
  * a larger workspace or batch, must not be under graph capture; later calls
  * allocate nothing and can be captured. Calls on one stream are ordered by
- * the stream; calls on different streams use different workspaces.
+ * the stream; calls on different streams use different workspaces. A call
+ * captured into a graph keeps the workspace of the stream it was captured
+ * on: replays must not overlap other calls on that stream (or other replays
+ * of graphs captured on it).
  *
  * Returns GQA_OK, or a negative gqa_status with nothing enqueued.
  */
