@@ -260,3 +260,20 @@ def test_head_count_argument_errors(lib):
     # out extends over Hq rows per sequence: it must not reach kv
     lay = _layout(num_q_heads=64, num_kv_heads=8, q_stride_batch=64 * 128)
     assert _call_ex(lib, lay, out=0x20000000 - 2 * 64 * 128 * 2 + 256) == ALIAS
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    # no fallback: a missing library is an error, never a silent CPU path
+    import torch
+
+    import gqa_token_decode_amd as g
+
+    monkeypatch.setattr(g, "_lib", None)
+    monkeypatch.setattr(g, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="build"):
+        g.load_library()
+    if not torch.cuda.is_available():
+        q = torch.zeros(1, 32, 128, dtype=torch.float16)
+        with pytest.raises((RuntimeError, ValueError)):
+            g.gqa_decode(q, torch.zeros(1, 2, 8, 4, 128, dtype=torch.float16),
+                         torch.ones(1, dtype=torch.int32))
