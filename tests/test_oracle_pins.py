@@ -462,6 +462,106 @@ def test_e4m3_cache_matches_sdpa_on_dequantised_tensors():
     assert np.abs(got - ref).max() <= 1e-12
 
 
+# ---------------------------------------------------------------- block-scaled FP4
+# The FP4 E2M1 element format as tabulated in the OCP Microscaling Formats
+# (MX) v1.0 specification (FP4 E2M1 section): the eight non-negative codes
+# and their values; codes 8..15 are their negatives.
+E2M1_TABLE = {0b0000: 0.0, 0b0001: 0.5, 0b0010: 1.0, 0b0011: 1.5,
+              0b0100: 2.0, 0b0101: 3.0, 0b0110: 4.0, 0b0111: 6.0}
+
+
+def _e2m1_from_table(code):
+    v = E2M1_TABLE[code & 7]
+    return -v if code & 8 else v
+
+
+def test_e2m1_decoding_matches_the_format_table():
+    from oracle.formats import e2m1_to_f64
+
+    got = e2m1_to_f64(np.arange(16))
+    for c in range(16):
+        assert got[c] == _e2m1_from_table(c), c
+    assert np.signbit(got[8]) and not np.signbit(got[0])
+
+
+def test_block_scaled_fp4_rows_match_element_by_element_brute_force():
+    # Each element decoded on its own from the table, its byte and nibble,
+    # and its block's scale (torch's E4M3 decoding): catches a swapped nibble
+    # order, a wrong block size or a scale applied to the wrong block.
+    import torch
+
+    from oracle.formats import nvfp4_to_f64
+
+    rng = np.random.default_rng(901)
+    packed = rng.integers(0, 256, (3, 5, 64), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (3, 5, 8), dtype=np.uint8)   # finite, positive codes
+    scales[0, 0] = [0x38, 0x40, 0x30, 0x48, 0x01, 0x7E, 0x39, 0x08]
+    got = nvfp4_to_f64(packed, scales)
+    sc = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for a in range(3):
+        for r in range(5):
+            for i in range(128):
+                byte = int(packed[a, r, i // 2])
+                code = byte & 15 if i % 2 == 0 else byte >> 4
+                want = _e2m1_from_table(code) * sc[a, r, i // 16]
+                assert got[a, r, i] == want, (a, r, i)
+    # one row written out: byte 0x21 holds elements (0.5, 1.0), byte 0xF7
+    # holds (6, -6); scales 2 and 0.5 for the first two blocks
+    row = np.zeros(64, np.uint8)
+    row[0], row[1], row[8] = 0x21, 0xF7, 0x93
+    scl = np.zeros(8, np.uint8)
+    scl[0], scl[1] = 0x40, 0x30
+    v = nvfp4_to_f64(row, scl)
+    assert list(v[:4]) == [1.0, 2.0, 12.0, -12.0]
+    assert list(v[16:18]) == [0.75, -0.25] and not v[4:16].any() and not v[18:].any()
+
+
+def test_block_scaled_fp4_encoding_keeps_representable_values():
+    # Input preparation check: a row whose blocks hold exact E2M1 multiples
+    # of an E4M3 scale, with the block maximum at 6 x scale, is encoded and
+    # decoded back unchanged.
+    from oracle.formats import nvfp4_to_f64
+
+    rng = np.random.default_rng(902)
+    mags = np.array(sorted(E2M1_TABLE.values()))
+    x = rng.choice(mags, (4, 128)) * rng.choice([-1.0, 1.0], (4, 128))
+    x[:, ::16] = 6.0
+    blk_scale = np.repeat(rng.choice([0.25, 0.5, 1.0, 1.5, 3.0], (4, 8)), 16, axis=1)
+    x = (x * blk_scale).astype(np.float32)
+    packed, scales = workloads.encode_nvfp4(x)
+    assert np.array_equal(nvfp4_to_f64(packed, scales), x.astype(np.float64))
+
+
+def test_block_scaled_fp4_cache_matches_sdpa_on_dequantised_tensors():
+    import torch
+    import torch.nn.functional as F
+
+    from oracle.formats import nvfp4_to_f64
+
+    w = workloads.build("nvfp4 pin", 58, 70, [70, 17, 1, 0], elem="nvfp4", fill="nan")
+    kv64 = nvfp4_to_f64(w.dense_kv(), w.dense_scales())
+    assert kv64.shape == (4, 2, 8, 70, 128)
+    got = decode(w.q, kv64, w.seq_lens, 1.0)
+    # SDPA on tensors dequantised with the table and torch's E4M3 decoding;
+    # NaN rows beyond the lengths are masked (and zeroed, as SDPA would still
+    # multiply them by a zero weight)
+    table = np.array([_e2m1_from_table(c) for c in range(16)])
+    raw = w.dense_kv().astype(np.int64)
+    codes = np.stack([raw & 15, raw >> 4], axis=-1).reshape(raw.shape[:-1] + (128,))
+    sc = torch.from_numpy(w.dense_scales()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    deq = table[codes] * np.repeat(sc, 16, axis=-1)
+    C = deq.shape[3]
+    valid = np.arange(C)[None, :] < w.seq_lens.astype(np.int64)[:, None]
+    deq = np.where(valid[:, None, None, :, None], deq, 0.0)
+    mask = torch.from_numpy(valid)[:, None, None, :]
+    ref = F.scaled_dot_product_attention(torch.from_numpy(w.q.astype(np.float64)).unsqueeze(2),
+                                         torch.from_numpy(deq[:, 0]), torch.from_numpy(deq[:, 1]),
+                                         attn_mask=mask, scale=effective_scale(1.0),
+                                         enable_gqa=True).squeeze(2).numpy()
+    ref[3] = 0.0                       # empty prefix: zeros (SDPA gives NaN for a fully masked row)
+    assert np.abs(got - ref).max() <= 1e-12
+
+
 # ---------------------------------------------------------------- other head counts
 # The page fixes 32 query and 8 KV heads; the library also takes other
 # counts (Hq a multiple of Hkv, Hq / Hkv <= 8), with query head h reading KV

@@ -29,6 +29,14 @@ k_scale (v_scale), a power of two, and rounded to OCP FP8 E4M3 (nearest
 even, by torch's float8_e4m3fn conversion), kept as uint8 codes. With
 k_scale = v_scale = 2^-4 a unit-variance draw is coded at variance 256:
 well inside the format's range (largest finite 448) and above its subnormals.
+Or "nvfp4": q as fp16, and K/V as block-scaled FP4: each block of 16
+consecutive elements of a row gets the scale amax / 6 rounded to E4M3
+(nearest even, torch's float8_e4m3fn), and each element the E2M1 code
+nearest to x / scale (ties to the even code, magnitudes above 6 saturate);
+two codes per byte, element 2m in the low nibble. The packed codes are kept
+as uint8 [Hkv, L, 64] and the scales as uint8 [Hkv, L, 8]; k_scale = v_scale
+= 1. Beyond the lengths the "nan" fill writes code bytes 0xFF and NaN scale
+codes 0x7F.
 """
 from __future__ import annotations
 
@@ -45,6 +53,12 @@ FP16_QNAN_BITS = 0x7E00
 BF16_QNAN_BITS = 0x7FC0
 E4M3_NAN_CODE = 0x7F
 E4M3_SCALE = 2.0 ** -4
+FP4_BLOCK = 16
+FP4_FILL_BYTE = 0xFF
+# E2M1 magnitudes in code order (code = 2 * exponent field + mantissa bit)
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+# midpoints between neighbouring magnitudes
+_E2M1_MID = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / 2
 
 
 @dataclasses.dataclass
@@ -66,9 +80,11 @@ class Workload:
     k_valid: List[np.ndarray]     # fp16 [Hkv, L_b, 128] per b
     v_valid: List[np.ndarray]     # fp16 [Hkv, L_b, 128] per b
     fill: str = "zero"            # "zero" or "nan": contents beyond L_b
-    elem: str = "f16"             # "f16", "bf16" or "e4m3" (kv only)
+    elem: str = "f16"             # "f16", "bf16", "e4m3" or "nvfp4" (kv only)
     k_scale: float = 1.0          # e4m3: the stored codes stand for K / k_scale
     v_scale: float = 1.0
+    k_scales: Optional[List[np.ndarray]] = None   # nvfp4: uint8 [Hkv, L_b, 8] E4M3 block scales
+    v_scales: Optional[List[np.ndarray]] = None
 
     @property
     def batch(self) -> int:
@@ -89,26 +105,40 @@ class Workload:
 
     @property
     def kv_bytes_read(self) -> int:
-        """K+V bytes of the valid prefixes: sum(L_b) * 2 * Hkv * 128 * (2 B,
-        or 1 B for e4m3)."""
-        return int(self.valid_lengths.sum()) * 2 * self.kv_heads * HEAD_DIM * self.kv_elem_bytes
+        """K+V bytes of the valid prefixes: sum(L_b) * 2 * Hkv * (bytes per
+        head row: 256 for 16-bit types, 128 for e4m3, 64 + 8 for nvfp4)."""
+        return int(self.valid_lengths.sum()) * 2 * self.kv_heads * self.kv_row_bytes
+
+    @property
+    def kv_row_bytes(self) -> int:
+        if self.elem == "nvfp4":
+            return HEAD_DIM // 2 + HEAD_DIM // FP4_BLOCK
+        return HEAD_DIM * self.kv_elem_bytes
 
     @property
     def kv_elem_bytes(self) -> int:
-        return 1 if self.elem == "e4m3" else 2
+        """Bytes per stored element of kv (nvfp4: the packed code bytes)."""
+        return 1 if self.elem in ("e4m3", "nvfp4") else 2
+
+    @property
+    def kv_row_elems(self) -> int:
+        """Stored elements per kv head row (nvfp4: 64 code bytes)."""
+        return HEAD_DIM // 2 if self.elem == "nvfp4" else HEAD_DIM
 
     def fill_value_bits(self) -> int:
         if self.fill != "nan":
             return 0
-        return {"bf16": BF16_QNAN_BITS, "e4m3": E4M3_NAN_CODE}.get(self.elem, FP16_QNAN_BITS)
+        return {"bf16": BF16_QNAN_BITS, "e4m3": E4M3_NAN_CODE,
+                "nvfp4": FP4_FILL_BYTE}.get(self.elem, FP16_QNAN_BITS)
 
     def _host_dtype(self):
-        return {"bf16": np.uint16, "e4m3": np.uint8}.get(self.elem, np.float16)
+        return {"bf16": np.uint16, "e4m3": np.uint8, "nvfp4": np.uint8}.get(self.elem, np.float16)
 
     def _torch_dtype(self):
         import torch
 
-        return {"bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}.get(self.elem, torch.float16)
+        return {"bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn,
+                "nvfp4": torch.uint8}.get(self.elem, torch.float16)
 
     def q_to_device(self, device):
         """q as a device tensor of the workload's element type."""
@@ -120,11 +150,15 @@ class Workload:
         return t.to(device)
 
     def dense_kv(self) -> np.ndarray:
-        """Host ``[B, 2, Hkv, C, 128]`` cache (fp16, or bf16 bit patterns)
-        with the fill beyond L_b."""
+        """Host ``[B, 2, Hkv, C, 128]`` cache (fp16, or bf16 bit patterns,
+        or codes; nvfp4: ``[B, 2, Hkv, C, 64]`` packed bytes) with the fill
+        beyond L_b."""
         B, C = self.batch, self.capacity
-        kv = np.empty((B, 2, self.kv_heads, C, HEAD_DIM), dtype=self._host_dtype())
-        kv.view(np.uint16)[...] = self.fill_value_bits()
+        kv = np.empty((B, 2, self.kv_heads, C, self.kv_row_elems), dtype=self._host_dtype())
+        if kv.dtype == np.uint8:
+            kv[...] = self.fill_value_bits()
+        else:
+            kv.view(np.uint16)[...] = self.fill_value_bits()
         for b in range(B):
             L = self.k_valid[b].shape[1]
             kv[b, 0, :, :L, :] = self.k_valid[b]
@@ -136,9 +170,9 @@ class Workload:
         import torch
 
         B, C = self.batch, self.capacity
-        kv = torch.empty((B, 2, self.kv_heads, C, HEAD_DIM), dtype=self._torch_dtype(),
+        kv = torch.empty((B, 2, self.kv_heads, C, self.kv_row_elems), dtype=self._torch_dtype(),
                          device=device)
-        if self.elem == "e4m3":
+        if self.elem in ("e4m3", "nvfp4"):
             raw, host_raw = kv.view(torch.uint8), np.uint8
             raw.fill_(self.fill_value_bits())
         else:
@@ -150,6 +184,74 @@ class Workload:
                 raw[b, 0, :, :L, :].copy_(torch.from_numpy(self.k_valid[b].view(host_raw)))
                 raw[b, 1, :, :L, :].copy_(torch.from_numpy(self.v_valid[b].view(host_raw)))
         return kv
+
+    def dense_scales(self) -> np.ndarray:
+        """nvfp4: host ``[B, 2, Hkv, C, 8]`` E4M3 block scales (NaN codes
+        beyond L_b for the "nan" fill, zeros otherwise)."""
+        assert self.elem == "nvfp4"
+        B, C = self.batch, self.capacity
+        sc = np.full((B, 2, self.kv_heads, C, HEAD_DIM // FP4_BLOCK),
+                     E4M3_NAN_CODE if self.fill == "nan" else 0, dtype=np.uint8)
+        for b in range(B):
+            L = self.k_scales[b].shape[1]
+            sc[b, 0, :, :L] = self.k_scales[b]
+            sc[b, 1, :, :L] = self.v_scales[b]
+        return sc
+
+    def scales_to_device(self, device):
+        """nvfp4: the block scales as a device uint8 tensor [B, 2, Hkv, C, 8]."""
+        import torch
+
+        assert self.elem == "nvfp4"
+        B, C = self.batch, self.capacity
+        sc = torch.empty((B, 2, self.kv_heads, C, HEAD_DIM // FP4_BLOCK), dtype=torch.uint8,
+                         device=device)
+        sc.fill_(E4M3_NAN_CODE if self.fill == "nan" else 0)
+        for b in range(B):
+            L = self.k_scales[b].shape[1]
+            if L:
+                sc[b, 0, :, :L].copy_(torch.from_numpy(self.k_scales[b]))
+                sc[b, 1, :, :L].copy_(torch.from_numpy(self.v_scales[b]))
+        return sc
+
+
+def encode_nvfp4(x: np.ndarray):
+    """float32 [..., 128] -> (packed uint8 [..., 64], scales uint8 [..., 8]).
+
+    Input preparation only (the decode never encodes): per block of 16, the
+    scale amax / 6 rounded to E4M3, then each element's nearest E2M1 code
+    for x / scale. Works one leading slice at a time to bound host memory.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim > 2:
+        parts = [encode_nvfp4(x[i]) for i in range(x.shape[0])]
+        shp = x.shape[:-1]
+        if not parts:
+            return (np.zeros(shp + (x.shape[-1] // 2,), np.uint8),
+                    np.zeros(shp + (x.shape[-1] // FP4_BLOCK,), np.uint8))
+        return np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])
+    import torch
+
+    blocks = x.reshape(x.shape[:-1] + (x.shape[-1] // FP4_BLOCK, FP4_BLOCK))
+    amax = np.abs(blocks).max(axis=-1, initial=0.0)
+    sc_codes = torch.from_numpy((amax / np.float32(6.0)).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sc_vals = torch.from_numpy(sc_codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    den = np.where(sc_vals > 0, sc_vals, 1.0)[..., None]
+    y = np.where(sc_vals[..., None] > 0, blocks.astype(np.float64) / den, 0.0)
+    mag = np.abs(y)
+    # index into the sorted magnitudes (= the code without its sign): the
+    # number of midpoints below |y|, plus one at the midpoints whose upper
+    # neighbour is the even code (ties go to the even code)
+    code = np.zeros(mag.shape, dtype=np.uint8)
+    for k, mid in enumerate(_E2M1_MID):
+        code += mag > mid
+        if k % 2 == 1:
+            code += mag == mid
+    code |= (y < 0).astype(np.uint8) << 3
+    code = code.reshape(x.shape)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.astype(np.uint8), sc_codes.astype(np.uint8)
 
 
 def _normal(rng: np.random.Generator, shape, sigma: float, elem: str,
@@ -196,16 +298,27 @@ def build(
     else:
         lens = np.asarray(lengths, dtype=np.int64)
     B = int(lens.shape[0])
-    assert elem in ("f16", "bf16", "e4m3"), elem
+    assert elem in ("f16", "bf16", "e4m3", "nvfp4"), elem
     kv_scale = E4M3_SCALE if elem == "e4m3" else 1.0
-    q = _normal(rng, (B, q_heads, HEAD_DIM), sigma_q, "f16" if elem == "e4m3" else elem)
+    q = _normal(rng, (B, q_heads, HEAD_DIM), sigma_q,
+                "f16" if elem in ("e4m3", "nvfp4") else elem)
     k_valid, v_valid = [], []
+    k_scales, v_scales = ([], []) if elem == "nvfp4" else (None, None)
     for b in range(B):
         L = int(min(max(lens[b], 0), capacity))
+        if elem == "nvfp4":
+            for sigma, vals, scs in ((sigma_k, k_valid, k_scales), (sigma_v, v_valid, v_scales)):
+                x = rng.standard_normal((kv_heads, L, HEAD_DIM), dtype=np.float32)
+                if sigma != 1.0:
+                    x = x * np.float32(sigma)
+                packed, sc = encode_nvfp4(x)
+                vals.append(packed)
+                scs.append(sc)
+            continue
         k_valid.append(_normal(rng, (kv_heads, L, HEAD_DIM), sigma_k, elem, kv_scale))
         v_valid.append(_normal(rng, (kv_heads, L, HEAD_DIM), sigma_v, elem, kv_scale))
     return Workload(name, q, lens.astype(np.int32), int(capacity), float(q_scale),
-                    k_valid, v_valid, fill, elem, kv_scale, kv_scale)
+                    k_valid, v_valid, fill, elem, kv_scale, kv_scale, k_scales, v_scales)
 
 
 def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
