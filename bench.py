@@ -80,7 +80,7 @@ def traffic_from_profiles(workload: str):
 def cpu_baseline(w, min_seconds: float):
     import numpy as np
 
-    from oracle.formats import bf16_to_f64, e4m3_to_f64
+    from oracle.formats import bf16_to_f64, e4m3_to_f64, nvfp4_to_f64
     from oracle.reference import decode_ragged
 
     # the oracle takes the element values widened exactly
@@ -92,6 +92,10 @@ def cpu_baseline(w, min_seconds: float):
         q = w.q
         kval = [e4m3_to_f64(k) for k in w.k_valid]
         vval = [e4m3_to_f64(v) for v in w.v_valid]
+    elif w.elem == "nvfp4":
+        q = w.q
+        kval = [nvfp4_to_f64(k, s) for k, s in zip(w.k_valid, w.k_scales)]
+        vval = [nvfp4_to_f64(v, s) for v, s in zip(w.v_valid, w.v_scales)]
     else:
         q, kval, vval = w.q, w.k_valid, w.v_valid
     try:
@@ -196,10 +200,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--elem", default="f16", choices=["f16", "bf16", "e4m3"],
-                    help="element type: f16 (default), bf16 (q, kv, out), or e4m3 (fp16 q and "
-                         "out, FP8 E4M3 kv with per-tensor scales); non-f16 types use the typed "
-                         "entry point")
+    ap.add_argument("--elem", default="f16", choices=["f16", "bf16", "e4m3", "nvfp4"],
+                    help="element type: f16 (default), bf16 (q, kv, out), e4m3 (fp16 q and "
+                         "out, FP8 E4M3 kv with per-tensor scales), or nvfp4 (fp16 q and out, "
+                         "block-scaled FP4 kv: gqa_decode_fp4); non-f16 types use the typed "
+                         "entry points")
     ap.add_argument("--page-size", type=int, default=0,
                     help="> 0: read the cache as shuffled HND pages of this many positions "
                          "(gqa_decode_paged); 0: the contiguous cache")
@@ -239,17 +244,27 @@ def main(argv=None):
     q = w.q_to_device(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
     kv0 = w.kv_to_device(dev)
+    fp4 = args.elem == "nvfp4"
+    sc0 = w.scales_to_device(dev) if fp4 else None
+    alloc = kv0.numel() * kv0.element_size() + (sc0.numel() if fp4 else 0)
     rot = max(1, math.ceil(ROTATE_TARGET_BYTES / max(kv_bytes, 1)))
-    rot = min(rot, ROTATE_MAX_COPIES, max(1, int(40e9 // (kv0.numel() * kv0.element_size()))))
+    rot = min(rot, ROTATE_MAX_COPIES, max(1, int(40e9 // alloc)))
     kvs = [kv0] + [kv0.clone() for _ in range(rot - 1)]
+    scs = ([sc0] + [sc0.clone() for _ in range(rot - 1)]) if fp4 else None
     out = torch.empty_like(q)
     tables = None
     if args.page_size > 0:
         kvs, tables = zip(*[_paginate(kv, args.page_size, seed=i) for i, kv in enumerate(kvs)])
+        if fp4:   # the same pages (same seed): the scale pages share the block table
+            scs = [_paginate(sc, args.page_size, seed=i)[0] for i, sc in enumerate(scs)]
     torch.cuda.synchronize()
 
     def step(i):
-        if tables is not None:
+        if fp4:
+            g.gqa_decode_fp4(q, kvs[i % rot], scs[i % rot], lens, out=out,
+                             block_table=None if tables is None else tables[i % rot],
+                             q_scale=w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
+        elif tables is not None:
             g.gqa_decode_paged(q, kvs[i % rot], tables[i % rot], lens, out=out,
                                q_scale=w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
         else:

@@ -15,6 +15,7 @@ library's extension):
     gqa_decode(q, kv, sequence_lengths, *, out=None, q_scale=1.0, chunk_len=0,
                k_scale=1.0, v_scale=1.0)
     gqa_decode_paged(q, kv_pages, block_table, sequence_lengths, *, ...)
+    gqa_decode_fp4(q, kv_codes, kv_scales, sequence_lengths, *, block_table=None, ...)
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ from typing import Optional
 
 import torch  # must load before the library so both share one HIP runtime
 
-__all__ = ["gqa_decode", "gqa_decode_paged", "workspace_bytes", "release_workspace", "library_path",
+__all__ = ["gqa_decode", "gqa_decode_paged", "gqa_decode_fp4", "workspace_bytes", "release_workspace", "library_path",
            "load_library", "KernelTimer", "GqaDecodeError",
            "NUM_Q_HEADS", "NUM_KV_HEADS", "HEAD_DIM"]
 
@@ -71,6 +72,9 @@ def load_library():
     lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(_Layout), f32, f32, f32,
                                   i32, i32, i32, vp]
     lib.gqa_decode_ex.restype = i32
+    lib.gqa_decode_fp4.argtypes = [vp, vp, ctypes.POINTER(_BlockScales), vp, vp,
+                                   ctypes.POINTER(_Layout), f32, f32, f32, i32, i32, i32, vp]
+    lib.gqa_decode_fp4.restype = i32
     lib.gqa_decode_workspace_bytes.argtypes = [i32, i32]
     lib.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.gqa_decode_release_workspace.argtypes = []
@@ -125,6 +129,17 @@ class _Layout(ctypes.Structure):
                 ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int),
                 ("page_size", ctypes.c_int), ("num_pages", ctypes.c_int),
                 ("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int)]
+
+
+class _BlockScales(ctypes.Structure):
+    """struct gqa_block_scales of the C ABI (strides in bytes)."""
+
+    _fields_ = [("scales", ctypes.c_void_p), ("stride_batch", ctypes.c_int64),
+                ("stride_kind", ctypes.c_int64), ("stride_head", ctypes.c_int64),
+                ("stride_row", ctypes.c_int64)]
+
+
+FP4_SCALES_PER_ROW = 8      # E4M3 block scales per head row (one per 16 elements)
 
 
 def _check_view(name, t, dtype, shape_len):
@@ -281,6 +296,76 @@ def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch
                            out.data_ptr(), code, ctypes.byref(lay), float(q_scale),
                            float(k_scale), float(v_scale), B, max_pages * page_size, chunk_len,
                            _stream_of(q.device))
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def gqa_decode_fp4(q: torch.Tensor, kv_codes: torch.Tensor, kv_scales: torch.Tensor,
+                   sequence_lengths: torch.Tensor, *, block_table: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, q_scale: float = 1.0, chunk_len: int = 0,
+                   k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Decode one token of GQA from a block-scaled FP4 cache.
+
+    q: fp16 [batch, Hq, 128]. kv_codes: uint8 [batch, 2, Hkv, capacity, 64]
+    (or pages [num_pages, 2, Hkv, page_size, 64] with ``block_table``): per
+    head row, 64 bytes of E2M1 codes, element 2m in the low nibble of byte
+    m. kv_scales: uint8 (or torch.float8_e4m3fn) with kv_codes' leading
+    shape and a last axis of 8: the E4M3 scale of each block of 16
+    elements. Element value = E2M1 value x its block's scale; k_scale and
+    v_scale are per-tensor scales on top. Paged caches: page_size a power of
+    two >= 32, block_table int32 [batch, max_pages] as for gqa_decode_paged.
+    Strided views with contiguous last axes are taken without copies. Other
+    arguments as for gqa_decode; fp16 output.
+    """
+    paged = block_table is not None
+    if not isinstance(kv_scales, torch.Tensor):
+        raise TypeError(f"kv_scales must be a torch.Tensor, got {type(kv_scales).__name__}")
+    sc_dtype = kv_scales.dtype if kv_scales.dtype in _FP8_KV_DTYPES else torch.uint8
+
+    def kv_shape(B):
+        ks = kv_codes.shape
+        if (not paged and ks[0] != B) or ks[1] != 2 or ks[4] != HEAD_DIM // 2:
+            lead = "num_pages" if paged else str(B)
+            raise ValueError(f"kv_codes must have shape [{lead}, 2, kv_heads, "
+                             f"{'page_size' if paged else 'capacity'}, 64], got {tuple(ks)}")
+        _check_view("kv_scales", kv_scales, sc_dtype, 5)
+        if tuple(kv_scales.shape) != tuple(ks[:4]) + (FP4_SCALES_PER_ROW,):
+            raise ValueError(f"kv_scales must have shape {tuple(ks[:4]) + (FP4_SCALES_PER_ROW,)}, "
+                             f"got {tuple(kv_scales.shape)}")
+        if paged:
+            _check_tensor("block_table", block_table, torch.int32, 2)
+            if block_table.shape[0] != B:
+                raise ValueError(f"block_table must have {B} rows, got {tuple(block_table.shape)}")
+
+    if not isinstance(kv_codes, torch.Tensor) or kv_codes.dtype != torch.uint8:
+        raise TypeError("kv_codes must be a uint8 torch.Tensor of packed E2M1 codes")
+    if not isinstance(q, torch.Tensor) or q.dtype != torch.float16:
+        raise TypeError("q must be a float16 torch.Tensor")
+    _, _, out = _prepare(q, kv_codes, sequence_lengths, out, kv_shape)
+    for name, t in (("kv_scales", kv_scales),) + ((("block_table", block_table),) if paged else ()):
+        if t.device != q.device:
+            _check_device(name, t)
+            raise ValueError(f"{name} must be on q's device")
+    _check_chunk(chunk_len)
+    B, Hq, Hkv = q.shape[0], q.shape[1], kv_codes.shape[2]
+    if paged:
+        num_pages, page_size, max_pages = kv_codes.shape[0], kv_codes.shape[3], block_table.shape[1]
+        capacity = max_pages * page_size
+        lay = _Layout(q.stride(0), q.stride(1), kv_codes.stride(0), kv_codes.stride(1),
+                      kv_codes.stride(2), kv_codes.stride(3), block_table.data_ptr(), max_pages,
+                      page_size, num_pages, Hq, Hkv)
+    else:
+        capacity = kv_codes.shape[3]
+        lay = _Layout(q.stride(0), q.stride(1), kv_codes.stride(0), kv_codes.stride(1),
+                      kv_codes.stride(2), kv_codes.stride(3), None, 0, 0, 0, Hq, Hkv)
+    scl = _BlockScales(kv_scales.data_ptr(), kv_scales.stride(0), kv_scales.stride(1),
+                       kv_scales.stride(2), kv_scales.stride(3))
+    lib = _lib if _lib is not None else load_library()
+    st = lib.gqa_decode_fp4(q.data_ptr(), kv_codes.data_ptr(), ctypes.byref(scl),
+                            sequence_lengths.data_ptr(), out.data_ptr(), ctypes.byref(lay),
+                            float(q_scale), float(k_scale), float(v_scale), B, capacity,
+                            chunk_len, _stream_of(q.device))
     if st != 0:
         _raise(lib, st)
     return out

@@ -49,7 +49,8 @@ struct DeviceInfo {
   bool ready = false;
   int status = GQA_OK;
   int cus = 0;
-  int resident = 0;   // decode workgroups per CU
+  int resident = 0;       // decode workgroups per CU
+  int resident_fp4 = 0;   // the same for the FP4-cache kernels
   std::string arch;
 };
 
@@ -108,8 +109,10 @@ const DeviceInfo& device_info(int dev) {
                     ? GQA_OK
                     : GQA_ERR_UNSUPPORTED_ARCH;
     if (di.status == GQA_OK) {
-      di.resident = gqa::resident_workgroups_per_cu();
+      di.resident = gqa::resident_workgroups_per_cu(false);
       if (di.resident <= 0) di.resident = 1;
+      di.resident_fp4 = gqa::resident_workgroups_per_cu(true);
+      if (di.resident_fp4 <= 0) di.resident_fp4 = 1;
     }
   }
   di.ready = true;
@@ -118,12 +121,13 @@ const DeviceInfo& device_info(int dev) {
 
 // One equal piece per workgroup that can be resident at once (times an
 // optional factor), so the whole decode runs in a single round.
-// row_align (1, or 16 for paged caches) rounds the piece and cost sizes up.
-gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align = 1) {
+// row_align (1, or 16 / 32 for paged caches) rounds the piece and cost sizes up.
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, bool fp4) {
   gqa::SplitConfig cfg;
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
   auto up = [row_align](int v) { return (v + row_align - 1) / row_align * row_align; };
-  cfg.pieces = (di.cus > 0 ? di.cus : 256) * (di.resident > 0 ? di.resident : 1) * per_slot;
+  const int resident = fp4 ? di.resident_fp4 : di.resident;
+  cfg.pieces = (di.cus > 0 ? di.cus : 256) * (resident > 0 ? resident : 1) * per_slot;
   cfg.min_piece = up(env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30));
   cfg.seg_cost = up(env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20));
   cfg.forced_piece = forced_piece > 0 ? up(forced_piece) : 0;
@@ -225,15 +229,20 @@ int* get_tickets(int dev, hipStream_t stream, size_t count, int* status) {
   return ws->tickets;
 }
 
-// Strides resolved to bytes, with the address range each of q and kv spans.
+// Strides resolved to bytes, with the address range each of q, kv (and the
+// FP4 block scales) spans.
 struct Resolved {
   gqa::Layout lay;
-  size_t q_extent = 0, kv_extent = 0, table_bytes = 0;
+  size_t q_extent = 0, kv_extent = 0, table_bytes = 0, scale_extent = 0;
   int row_align = 1;
 };
 
-int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, Resolved* r) {
+// kv_eb: bytes per kv element (2, or 1 for E4M3 and the FP4 code bytes);
+// fp4: kv rows are 64 code bytes (element pairs) instead of 128 elements.
+int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, bool fp4,
+                   Resolved* r) {
   const long long C = capacity;
+  const long long row_elems = fp4 ? GQA_HEAD_DIM / 2 : GQA_HEAD_DIM;
   gqa_layout L;
   if (in) {
     L = *in;
@@ -241,9 +250,9 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
     L = gqa_layout{};
     L.q_stride_batch = (long long)GQA_NUM_Q_HEADS * GQA_HEAD_DIM;
     L.q_stride_head = GQA_HEAD_DIM;
-    L.kv_stride_row = GQA_HEAD_DIM;
-    L.kv_stride_head = C * GQA_HEAD_DIM;
-    L.kv_stride_kind = GQA_NUM_KV_HEADS * C * GQA_HEAD_DIM;
+    L.kv_stride_row = row_elems;
+    L.kv_stride_head = C * row_elems;
+    L.kv_stride_kind = GQA_NUM_KV_HEADS * C * row_elems;
     L.kv_stride_batch = 2 * L.kv_stride_kind;
   }
   if (L.num_q_heads == 0 && L.num_kv_heads == 0) {
@@ -267,7 +276,7 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
   for (long long v : ks)
     if (v < 0 || v > kLimit || (v * (long long)kv_eb) % 16 != 0)
       return fail(GQA_ERR_BAD_ARG, "gqa_decode: kv strides must be >= 0 and keep rows 16-byte aligned");
-  const long long row_bytes = GQA_HEAD_DIM * (long long)kv_eb;
+  const long long row_bytes = row_elems * (long long)kv_eb;
   const long long sr = L.kv_stride_row * (long long)kv_eb;
   if (sr < row_bytes)
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: kv_stride_row must cover a %lld-byte row", row_bytes);
@@ -277,8 +286,10 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
   long long rows_per_block = C;
   if (paged) {
     const int P = L.page_size;
-    if (P < 16 || (P & (P - 1)) != 0)
-      return fail(GQA_ERR_BAD_ARG, "gqa_decode: page_size must be a power of two >= 16, got %d", P);
+    const int min_page = fp4 ? 32 : 16;
+    if (P < min_page || (P & (P - 1)) != 0)
+      return fail(GQA_ERR_BAD_ARG, "gqa_decode: page_size must be a power of two >= %d, got %d",
+                  min_page, P);
     if (L.max_pages <= 0 || L.num_pages <= 0)
       return fail(GQA_ERR_BAD_ARG, "gqa_decode: max_pages and num_pages must be positive");
     if ((long long)L.max_pages * P < C)
@@ -296,7 +307,7 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
                           (long long)(Hq - 1) * L.q_stride_head + GQA_HEAD_DIM) * 2);
   r->kv_extent = (size_t)(((blocks - 1) * L.kv_stride_batch + L.kv_stride_kind +
                            (long long)(Hkv - 1) * L.kv_stride_head +
-                           (rows_per_block - 1) * L.kv_stride_row + GQA_HEAD_DIM) * (long long)kv_eb);
+                           (rows_per_block - 1) * L.kv_stride_row + row_elems) * (long long)kv_eb);
   r->table_bytes = paged ? (size_t)batch * (size_t)L.max_pages * 4 : 0;
   r->lay.q_sb = L.q_stride_batch * 2;
   r->lay.q_sh = L.q_stride_head * 2;
@@ -310,9 +321,50 @@ int resolve_layout(const gqa_layout* in, int batch, int capacity, size_t kv_eb, 
   int shift = 0;
   while (paged && (1 << shift) < L.page_size) ++shift;
   r->lay.page_shift = shift;
-  r->row_align = paged ? 16 : 1;
+  r->row_align = paged ? (fp4 ? 32 : 16) : 1;
   r->lay.q_heads = Hq;
   r->lay.kv_heads = Hkv;
+  return GQA_OK;
+}
+
+// FP4 block scales: strides (bytes), 4-byte alignment for the 4-byte loads,
+// 32-bit offsets, and the address range. All-zero strides select the
+// contiguous [blocks][2][Hkv][rows][8] layout (blocks = batch, or pages).
+int resolve_scales(const gqa_block_scales* sc, int batch, int capacity, Resolved* r) {
+  if (!sc || !sc->scales)
+    return fail(GQA_ERR_NULL, "gqa_decode_fp4: the block scales must be non-NULL");
+  const bool paged = r->lay.block_table != nullptr;
+  const long long rows = paged ? (1LL << r->lay.page_shift) : capacity;
+  const long long Hkv = r->lay.kv_heads;
+  long long sb = sc->stride_batch, sk = sc->stride_kind, sh = sc->stride_head,
+            sr = sc->stride_row;
+  if (sb == 0 && sk == 0 && sh == 0 && sr == 0) {
+    sr = GQA_FP4_SCALES_PER_ROW;
+    sh = rows * sr;
+    sk = Hkv * sh;
+    sb = 2 * sk;
+  }
+  const long long st[4] = {sb, sk, sh, sr};
+  for (long long v : st)
+    if (v < 0 || v > (1LL << 40) || v % 4 != 0)
+      return fail(GQA_ERR_BAD_ARG,
+                  "gqa_decode_fp4: block-scale strides must be >= 0 and multiples of 4 bytes");
+  if (sr < GQA_FP4_SCALES_PER_ROW)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode_fp4: the block-scale row stride must cover 8 bytes");
+  if (sr * rows >= (1LL << 31))
+    return fail(GQA_ERR_BAD_ARG,
+                "gqa_decode_fp4: block-scale row stride times %s is too large for 32-bit offsets",
+                paged ? "page_size" : "capacity");
+  if ((uintptr_t)sc->scales & 3u)
+    return fail(GQA_ERR_MISALIGNED, "gqa_decode_fp4: the block scales must be 4-byte aligned");
+  const long long blocks = paged ? r->lay.num_pages : batch;
+  r->scale_extent = (size_t)((blocks - 1) * sb + sk + (Hkv - 1) * sh + (rows - 1) * sr +
+                             GQA_FP4_SCALES_PER_ROW);
+  r->lay.kv_scales = sc->scales;
+  r->lay.sc_sb = sb;
+  r->lay.sc_sk = sk;
+  r->lay.sc_sh = sh;
+  r->lay.sc_sr = sr;
   return GQA_OK;
 }
 
@@ -342,21 +394,35 @@ int check_alias(const void* q, const void* kv, const int32_t* seq_lens, const vo
   const size_t ob = (size_t)batch * r.lay.q_heads * GQA_HEAD_DIM * 2;
   if (overlaps(out, ob, q, r.q_extent) || overlaps(out, ob, kv, r.kv_extent) ||
       overlaps(out, ob, seq_lens, (size_t)batch * 4) ||
-      (r.table_bytes && overlaps(out, ob, r.lay.block_table, r.table_bytes)))
-    return fail(GQA_ERR_ALIAS, "gqa_decode: out must not overlap q, kv, seq_lens or block_table");
+      (r.table_bytes && overlaps(out, ob, r.lay.block_table, r.table_bytes)) ||
+      (r.scale_extent && overlaps(out, ob, r.lay.kv_scales, r.scale_extent)))
+    return fail(GQA_ERR_ALIAS,
+                "gqa_decode: out must not overlap q, kv, seq_lens, block_table or the block scales");
   return GQA_OK;
 }
 
-int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
-                const gqa_layout* layout, float q_scale, float k_scale, float v_scale, int batch,
-                int capacity, int chunk_len, hipStream_t stream) {
+int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
+                const int32_t* seq_lens, void* out, int dtype, const gqa_layout* layout,
+                float q_scale, float k_scale, float v_scale, int batch, int capacity,
+                int chunk_len, hipStream_t stream) {
   int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len);
   if (st != GQA_OK) return st;
-  if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16 && dtype != GQA_DTYPE_E4M3_KV)
+  if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16 && dtype != GQA_DTYPE_E4M3_KV &&
+      dtype != GQA_DTYPE_FP4_KV)
     return fail(GQA_ERR_BAD_ARG, "gqa_decode: unknown dtype %d", dtype);
+  const bool fp4 = dtype == GQA_DTYPE_FP4_KV;
+  if (fp4 != (scales != nullptr))
+    return fail(fp4 ? GQA_ERR_NULL : GQA_ERR_BAD_ARG,
+                fp4 ? "gqa_decode_fp4: the block scales must be non-NULL"
+                    : "gqa_decode: an FP4 cache goes through gqa_decode_fp4");
   Resolved res;
-  st = resolve_layout(layout, batch, capacity, dtype == GQA_DTYPE_E4M3_KV ? 1 : 2, &res);
+  st = resolve_layout(layout, batch, capacity, dtype == GQA_DTYPE_E4M3_KV || fp4 ? 1 : 2, fp4,
+                      &res);
   if (st != GQA_OK) return st;
+  if (fp4) {
+    st = resolve_scales(scales, batch, capacity, &res);
+    if (st != GQA_OK) return st;
+  }
   st = check_alias(q, kv, seq_lens, out, batch, res);
   if (st != GQA_OK) return st;
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
@@ -370,10 +436,11 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
   const int dev = pointer_device(q);
   if (dev < 0) return fail(GQA_ERR_DEVICE_MISMATCH, "gqa_decode: q is not device memory");
   if (pointer_device(kv) != dev || pointer_device(out) != dev || pointer_device(seq_lens) != dev ||
-      (res.lay.block_table && pointer_device(res.lay.block_table) != dev))
+      (res.lay.block_table && pointer_device(res.lay.block_table) != dev) ||
+      (res.lay.kv_scales && pointer_device(res.lay.kv_scales) != dev))
     return fail(GQA_ERR_DEVICE_MISMATCH,
-                "gqa_decode: q, kv, seq_lens, out (and block_table) must be device memory on one "
-                "device");
+                "gqa_decode: q, kv, seq_lens, out (and block_table, block scales) must be device "
+                "memory on one device");
 
   int prev = -1;
   if (hipGetDevice(&prev) != hipSuccess) prev = -1;
@@ -388,7 +455,7 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
       st = fail(di.status, "gqa_decode: device %d is %s; this library is built for gfx950", dev,
                 di.arch.c_str());
     } else {
-      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align);
+      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align, fp4);
       const int Hkv = res.lay.kv_heads, group = res.lay.q_heads / res.lay.kv_heads;
       const long long grid = gqa::grid_for(batch, capacity, Hkv, cfg);
       const size_t pbytes =
@@ -435,6 +502,7 @@ int decode_impl(const void* q, const void* kv, const int32_t* seq_lens, void* ou
           }
           const gqa::ElemType elem = dtype == GQA_DTYPE_BF16      ? gqa::ElemType::kBf16
                                      : dtype == GQA_DTYPE_E4M3_KV ? gqa::ElemType::kE4m3Kv
+                                     : fp4                        ? gqa::ElemType::kFp4Kv
                                                                   : gqa::ElemType::kF16;
           const hipError_t e = gqa::launch_decode(q, kv, seq_lens, out, elem, res.lay,
                                                   (float)scale, v_scale, batch, capacity, cfg,
@@ -455,28 +523,40 @@ extern "C" {
 
 int gqa_decode(const void* q, const void* kv, const int32_t* seq_lens, void* out, float q_scale,
                int batch, int capacity, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, nullptr, q_scale, 1.0f, 1.0f, batch,
+  return decode_impl(q, kv, nullptr, seq_lens, out, GQA_DTYPE_F16, nullptr, q_scale, 1.0f, 1.0f, batch,
                      capacity, 0, stream);
 }
 
 int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, void* out,
                        float q_scale, int batch, int capacity, int chunk_len, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, GQA_DTYPE_F16, nullptr, q_scale, 1.0f, 1.0f, batch,
+  return decode_impl(q, kv, nullptr, seq_lens, out, GQA_DTYPE_F16, nullptr, q_scale, 1.0f, 1.0f, batch,
                      capacity, chunk_len, stream);
 }
 
 int gqa_decode_typed(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
                      float q_scale, float k_scale, float v_scale, int batch, int capacity,
                      int chunk_len, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, dtype, nullptr, q_scale, k_scale, v_scale, batch,
+  if (dtype == GQA_DTYPE_FP4_KV)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode_typed: an FP4 cache goes through gqa_decode_fp4");
+  return decode_impl(q, kv, nullptr, seq_lens, out, dtype, nullptr, q_scale, k_scale, v_scale, batch,
                      capacity, chunk_len, stream);
 }
 
 int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
                   const gqa_layout* layout, float q_scale, float k_scale, float v_scale,
                   int batch, int capacity, int chunk_len, hipStream_t stream) {
-  return decode_impl(q, kv, seq_lens, out, dtype, layout, q_scale, k_scale, v_scale, batch,
-                     capacity, chunk_len, stream);
+  if (dtype == GQA_DTYPE_FP4_KV)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode_ex: an FP4 cache goes through gqa_decode_fp4");
+  return decode_impl(q, kv, nullptr, seq_lens, out, dtype, layout, q_scale, k_scale, v_scale,
+                     batch, capacity, chunk_len, stream);
+}
+
+int gqa_decode_fp4(const void* q, const void* kv, const gqa_block_scales* scales,
+                   const int32_t* seq_lens, void* out, const gqa_layout* layout, float q_scale,
+                   float k_scale, float v_scale, int batch, int capacity, int chunk_len,
+                   hipStream_t stream) {
+  return decode_impl(q, kv, scales, seq_lens, out, GQA_DTYPE_FP4_KV, layout,
+                     q_scale, k_scale, v_scale, batch, capacity, chunk_len, stream);
 }
 
 size_t gqa_decode_workspace_bytes(int batch, int capacity) {
@@ -489,7 +569,7 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   std::lock_guard<std::mutex> lock(g_mu);
   const DeviceInfo& di = device_info(dev);
   if (di.status != GQA_OK) return 0;
-  const long long grid = gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0));
+  const long long grid = gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0, 1, false));
   return gqa::segment_bytes_for_batch(batch, GQA_NUM_KV_HEADS) +
          gqa::partial_bytes_for_grid(grid, GQA_NUM_Q_HEADS / GQA_NUM_KV_HEADS);
 }

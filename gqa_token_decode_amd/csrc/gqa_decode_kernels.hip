@@ -78,24 +78,39 @@ constexpr int kMaxGroup = 8;                 // query heads per KV head, at most
 constexpr int kDim = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTileRows = 16;                // rows per wave per step
-constexpr int kStepRows = kWaves * kTileRows;     // rows per workgroup step
-constexpr int kTileHalves = kTileRows * kDim;     // one K or V tile in LDS (4 KiB)
-constexpr int kStageHalves = 2 * kTileHalves;     // one pipeline stage: K then V
 // Kernels come in two forms: kG4 for exactly 4 query heads per KV head (the
 // page's 32/8 case: group size, q loads and merge layout fixed at compile
 // time) and a general form for any group of 1..8 heads.
 template <bool kG4> constexpr int q_halves() { return (kG4 ? 4 : kMaxGroup) * kDim; }
-// Loads per tile and lane: 1 or 2 q loads (1 KiB each), 4 x K, 4 x V.
-template <bool kG4> constexpr int loads_per_tile() { return kG4 ? 9 : 10; }
-
 
 // Element formats: q, K, V and out in fp16 or bf16 (16-row tiles of 256-byte
 // rows), or fp16 q and out with OCP FP8 E4M3 K and V (32-row tiles of
-// 128-byte rows; one stage holds the same 8 KiB).
-constexpr int kFmtF16 = 0, kFmtBf16 = 1, kFmtE4m3 = 2;
-template <int F> constexpr int tile_rows() { return F == kFmtE4m3 ? 32 : 16; }
-template <int F> constexpr int row_bytes() { return F == kFmtE4m3 ? kDim : 2 * kDim; }
+// 128-byte rows; one stage holds the same 8 KiB), or fp16 q and out with
+// block-scaled FP4 K and V (32-row tiles of 64-byte rows of E2M1 codes, plus
+// 8 bytes of E4M3 block scales per row; a stage holds 4.5 KiB).
+constexpr int kFmtF16 = 0, kFmtBf16 = 1, kFmtE4m3 = 2, kFmtFp4 = 3;
+template <int F> constexpr int tile_rows() { return F == kFmtE4m3 || F == kFmtFp4 ? 32 : 16; }
+template <int F> constexpr int row_bytes() {
+  return F == kFmtFp4 ? kDim / 2 : F == kFmtE4m3 ? kDim : 2 * kDim;
+}
+constexpr int kFp4ScaleBytes = 8;            // E4M3 block scales per FP4 row (16 elements each)
+// LDS pipeline stage of one wave: K rows, then V rows (kind_bytes each); FP4
+// stages then hold the K and V block scales (32 rows x 8 B each).
+template <int F> constexpr int kind_bytes() { return tile_rows<F>() * row_bytes<F>(); }
+template <int F> constexpr int scale_offset() { return 2 * kind_bytes<F>(); }
+template <int F> constexpr int stage_bytes() {
+  return 2 * kind_bytes<F>() + (F == kFmtFp4 ? 2 * 32 * kFp4ScaleBytes : 0);
+}
+template <int F> constexpr int stage_halves() { return stage_bytes<F>() / 2; }
+// Loads per tile and lane: 1 or 2 q loads (1 KiB each), then 4 x K and 4 x V
+// (1 KiB each); FP4: 2 x K codes, 1 x K scales (256 B), 2 x V codes, 1 x V
+// scales.
+template <int F, bool kG4> constexpr int loads_per_tile() {
+  return (kG4 ? 1 : 2) + (F == kFmtFp4 ? 6 : 8);
+}
+// Workgroups per CU the pieces kernel is built for (waves per SIMD): the
+// FP4 stages are small enough for three.
+template <int F> constexpr int waves_per_simd() { return F == kFmtFp4 ? 3 : 2; }
 constexpr unsigned kBufferFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
 constexpr int kHeadSlotFloats = 2 + kDim;   // one head of a partial: (max, den) + 128 sums
@@ -104,6 +119,7 @@ constexpr int kCombinePerHeadBelow = 256;   // segments: below, the combine may 
 struct Params {
   const e16_t* q;
   const e16_t* kv;
+  const uint8_t* kv_scales;   // FP4: E4M3 block scales, 8 per K or V row
   const int32_t* seq_lens;
   e16_t* out;
   float2* ws_ml;       // [2 * grid][G] (max, denominator) per partial and head
@@ -130,6 +146,7 @@ struct Params {
   // i*kv_sr. Paged caches replace b*kv_sb by page*kv_sb, page =
   // block_table[b*max_pages + i/page_size], and i by i % page_size.
   long long q_sb, q_sh, kv_sb, kv_sk, kv_sh, kv_sr;
+  long long sc_sb, sc_sk, sc_sh, sc_sr;   // FP4 block scales, addressed like kv
   const int32_t* block_table;   // paged: [batch][max_pages] page ids
   int max_pages, page_shift, num_pages;
   int row_align;                // 1, or 16 for paged caches: segments and pieces
@@ -398,6 +415,11 @@ __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long
 // reads (rows r and r + 16 together) spread over the banks.
 __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (((r >> 4) & 1) << 2); }
 
+// 16-byte chunk c of row r of an FP4 tile (64-byte rows) sits at chunk
+// c ^ sw4(r): 8 consecutive rows read at one logical chunk (the K reads)
+// then hit 8 different 16-byte bank groups of a 128-byte line.
+__device__ __forceinline__ int sw4(int r) { return (r >> 1) & 3; }
+
 // Buffer resource over rows [row0, row0 + nrows) of one K or V block that
 // starts at `base` (row stride kv_sr bytes); rows past nrows read as zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, long long row0,
@@ -406,28 +428,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, lo
                                            nrows > 0 ? (int)(nrows * sr) : 0, kBufferFlags);
 }
 
-// Page holding row i of sequence b (paged caches): the page's byte offset,
-// or -1 if the page id is outside [0, num_pages) (its rows then read as
-// zeros instead of faulting). Uniform: one scalar load.
-__device__ __forceinline__ long long page_base(const Params& P, int b, int i) {
+// Page holding row i of sequence b (paged caches): the page id, or -1 if it
+// is outside [0, num_pages) (its rows then read as zeros instead of
+// faulting). Uniform: one scalar load.
+__device__ __forceinline__ int page_id(const Params& P, int b, int i) {
   const __attribute__((address_space(4))) int32_t* bt =
       (const __attribute__((address_space(4))) int32_t*)P.block_table;
   const int page = bt[(size_t)b * P.max_pages + (i >> P.page_shift)];
-  return (page >= 0 && page < P.num_pages) ? (long long)page * P.kv_sb : -1;
+  return (page >= 0 && page < P.num_pages) ? page : -1;
 }
 
 // Byte offsets of the pages holding rows t and t + 16 of a tile of segment
-// s (-1: no rows there, or an invalid page id). Unused for contiguous caches.
+// s (-1: no rows there, or an invalid page id), and for FP4 caches the
+// offset of the scale page of row t (FP4 tiles lie in one page: pages and
+// pieces are multiples of 32 rows). Unused for contiguous caches.
 struct PageBases {
-  long long p0 = -1, p1 = -1;
+  long long p0 = -1, p1 = -1, s0 = -1;
 };
 
-template <int kRows>
+template <int F>
 __device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, int t, bool live) {
   PageBases pb;
   const int nrows = live ? s.hi - t : 0;
-  if (nrows > 0) pb.p0 = page_base(P, s.b, t);
-  if (kRows == 32 && nrows > 16) pb.p1 = page_base(P, s.b, t + 16);
+  if (nrows > 0) {
+    const int id = page_id(P, s.b, t);
+    if (id >= 0) {
+      pb.p0 = (long long)id * P.kv_sb;
+      if constexpr (F == kFmtFp4) pb.s0 = (long long)id * P.sc_sb;
+    }
+  }
+  if constexpr (F == kFmtE4m3) {
+    if (nrows > 16) {
+      const int id = page_id(P, s.b, t + 16);
+      if (id >= 0) pb.p1 = (long long)id * P.kv_sb;
+    }
+  }
   return pb;
 }
 
@@ -468,6 +503,42 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
   // holding logical chunk (l%8) ^ swz8(row). Both swizzles are their own
   // inverse.
   char* st = reinterpret_cast<char*>(stage);
+  if constexpr (F == kFmtFp4) {
+    // Codes: load u gives lane l row 16u + l/4, physical 16-byte chunk l%4,
+    // which holds logical chunk (l%4) ^ sw4(row). Scales: one 4-byte load
+    // per lane, lane l taking bytes 4(l%2) .. +3 of row l/2, so the tile's
+    // 32 x 8 scale bytes land densely, row by row.
+#pragma unroll
+    for (int kind = 0; kind < 2; ++kind) {
+      __amdgpu_buffer_rsrc_t rc, rs;
+      if constexpr (kPaged) {
+        const int psz_mask = (1 << P.page_shift) - 1;
+        const char* blk = reinterpret_cast<const char*>(P.kv) + kind * P.kv_sk + s.g * P.kv_sh;
+        const char* sblk = reinterpret_cast<const char*>(P.kv_scales) + kind * P.sc_sk +
+                           s.g * P.sc_sh;
+        const int n = pb.p0 < 0 ? 0 : (nrows < 32 ? nrows : 32);   // the tile's rows, one page
+        rc = rows_rsrc(blk + (pb.p0 < 0 ? 0 : pb.p0), t & psz_mask, n, P.kv_sr);
+        rs = rows_rsrc(sblk + (pb.s0 < 0 ? 0 : pb.s0), t & psz_mask, n, P.sc_sr);
+      } else {
+        rc = rows_rsrc(reinterpret_cast<const char*>(P.kv) + s.b * P.kv_sb + kind * P.kv_sk +
+                           s.g * P.kv_sh, t, nrows, P.kv_sr);
+        rs = rows_rsrc(reinterpret_cast<const char*>(P.kv_scales) + s.b * P.sc_sb +
+                           kind * P.sc_sk + s.g * P.sc_sh, t, nrows, P.sc_sr);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = 16 * u + (lane >> 2);
+        const int c = (lane & 3) ^ sw4(r);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rc, (lds_void_t*)(st + kind * kind_bytes<F>() + u * 1024), 16,
+            (int)(r * P.kv_sr) + 16 * c, 0, 0, kNonTemporal);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void_t*)(st + scale_offset<F>() + kind * 32 * kFp4ScaleBytes), 4,
+          (int)((lane >> 1) * P.sc_sr) + 4 * (lane & 1), 0, 0, kNonTemporal);
+    }
+    return;
+  }
   // Paged: pb holds the byte offsets of the pages of rows t and t + 16.
   const long long pb0 = pb.p0, pb1 = pb.p1;
 #pragma unroll
@@ -520,22 +591,25 @@ struct WaveAcc {
 };
 
 // q^T as the QK B operand, read from the wave's q slot: lane (G4, j) takes
-// head j, depth 32kk + 8 G4 .. +7; columns j >= G are zero.
-template <bool kG4>
+// head j, depth 32kk + 8 G4 .. +7 (FP4 caches: depth 32 G4 + 8kk .. +7, the
+// order in which a lane's FP4 K bytes hold the depth; a dot product does
+// not depend on the order of its terms); columns j >= G are zero.
+template <bool kG4, int F>
 __device__ __forceinline__ void read_q(const e16_t* qslot, int group, uint4_t (&qb)[4]) {
   const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
   int row = j & (kG4 ? 3 : 7);
   asm volatile("" : "+v"(row));
-  const unsigned base = lds_addr(qslot) + 2 * (row * kDim + 8 * G);
+  constexpr bool kFp4 = F == kFmtFp4;
+  const unsigned base = lds_addr(qslot) + 2 * (row * kDim + (kFp4 ? 32 : 8) * G);
   uint4_t x0, x1, x2, x3;
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:64\n\t"
-      "ds_read_b128 %2, %4 offset:128\n\t"
-      "ds_read_b128 %3, %4 offset:192\n\t"
+      "ds_read_b128 %1, %4 offset:%5\n\t"
+      "ds_read_b128 %2, %4 offset:%6\n\t"
+      "ds_read_b128 %3, %4 offset:%7\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
-      : "v"(base)
+      : "v"(base), "n"(kFp4 ? 16 : 64), "n"(kFp4 ? 32 : 128), "n"(kFp4 ? 48 : 192)
       : "memory");
   const uint4_t zero = {0u, 0u, 0u, 0u};
   qb[0] = j < group ? x0 : zero;
@@ -545,12 +619,17 @@ __device__ __forceinline__ void read_q(const e16_t* qslot, int group, uint4_t (&
 }
 
 // LDS addresses of this lane's operand reads in stage 0 of its wave; stage 1
-// lies kStageHalves halves higher (an immediate offset of the reads).
+// lies stage_bytes<F>() higher (an immediate offset of the reads).
 //   16-bit formats: k[kk] = row j, logical chunk 4kk + G (16 B); v[db] =
 //   transposed read of row 4G + j/4, columns 16db + 4(j%4) .. +3.
 //   E4M3: k[4h + kk] = row 16h + j, bytes 32kk + 8G .. +7; v[db] =
 //   transposed read of row rowE(G, j/2), bytes 16db + 8(j%2) .. +7, where
 //   rowE(G, e) = 4G + e for e < 4 and 16 + 4G + e - 4 for e >= 4.
+//   FP4: k[h] = row 16h + j, logical chunk G (16 B: depth 32G .. 32G + 31);
+//   k[2 + h] = the 2 scale bytes of that row for depth blocks 2G, 2G + 1;
+//   v[rd] = transposed 4-bit read: lane (G, i) addresses row rowE(G, i % 8),
+//   half i / 8 of logical chunk rd (columns 32rd + 16(i/8) .. +15);
+//   v[4] = the V scales of rows 4G .. 4G + 3 (16 + 4G .. at +128).
 struct LdsReads {
   unsigned k[8];
   unsigned v[8];
@@ -560,9 +639,35 @@ template <int F>
 __device__ __forceinline__ LdsReads lds_reads(const e16_t* stage0) {
   const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
   const unsigned kbase = lds_addr(stage0);
-  const unsigned vbase = kbase + 4096;
+  const unsigned vbase = kbase + kind_bytes<F>();
   LdsReads r;
-  if constexpr (F == kFmtE4m3) {
+  if constexpr (F == kFmtFp4) {
+    const unsigned sbase = kbase + scale_offset<F>();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 16 * h + j;
+      r.k[h] = kbase + row * (kDim / 2) + 16 * (G ^ sw4(row));
+      r.k[2 + h] = sbase + row * kFp4ScaleBytes + 2 * G;
+    }
+    // Transposed 4-bit reads (lane mapping measured on the hardware): within
+    // each 16-lane group, output lane i receives, as its nibble e (e = 0..15,
+    // low nibbles first), nibble i of the 8-byte chunk addressed by lane e.
+    // Lanes e < 8 address row rowE(G, e), columns 32rd .. +15; lanes e >= 8
+    // the same rows, columns 32rd + 16 .. +31. So lane (G, i) receives
+    // column 32rd + i of rows rowE(G, 0..7) in its first dword and column
+    // 32rd + 16 + i of the same rows in its second: the A operands (V^T) of
+    // two K = 32 MFMAs.
+    const int e = j & 7;
+    const int row = e < 4 ? 4 * G + e : 16 + 4 * G + (e - 4);
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd)
+      r.v[rd] = vbase + row * (kDim / 2) + 16 * (rd ^ sw4(row)) + 8 * (j >> 3);
+    r.v[4] = sbase + 32 * kFp4ScaleBytes + 4 * G * kFp4ScaleBytes;
+#pragma unroll
+    for (int i = 5; i < 8; ++i) r.v[i] = 0;
+#pragma unroll
+    for (int i = 4; i < 8; ++i) r.k[i] = 0;
+  } else if constexpr (F == kFmtE4m3) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -705,6 +810,148 @@ __device__ __forceinline__ e16_t to_elem(float x) {
     return __builtin_bit_cast(e16_t, (_Float16)x);
 }
 
+// Read the FP4 operands of one stage (byte offset OFF from stage 0): K codes
+// (2 x 16 B), K scales (2 x 2 B), V codes transposed (4 x 8 B) and V scales
+// (4 x 16 B: the 8 scale bytes of rows rowE(G, 0..7), two rows per read).
+template <int OFF>
+__device__ __forceinline__ void read_stage_fp4(const LdsReads& a, uint4_t (&k)[2],
+                                               unsigned (&ks)[2], uint2 (&v)[4],
+                                               uint4_t (&vs)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %12 offset:%19\n\t"
+      "ds_read_b128 %1, %13 offset:%19\n\t"
+      "ds_read_u16 %2, %14 offset:%19\n\t"
+      "ds_read_u16 %3, %15 offset:%19\n\t"
+      "ds_read_b64_tr_b4 %4, %16 offset:%19\n\t"
+      "ds_read_b64_tr_b4 %5, %17 offset:%19\n\t"
+      "ds_read_b64_tr_b4 %6, %18 offset:%19\n\t"
+      "ds_read_b64_tr_b4 %7, %20 offset:%19\n\t"
+      "ds_read_b128 %8, %21 offset:%19\n\t"
+      "ds_read_b128 %9, %21 offset:%22\n\t"
+      "ds_read_b128 %10, %21 offset:%23\n\t"
+      "ds_read_b128 %11, %21 offset:%24\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(ks[0]), "=&v"(ks[1]), "=&v"(v[0]), "=&v"(v[1]),
+        "=&v"(v[2]), "=&v"(v[3]), "=&v"(vs[0]), "=&v"(vs[1]), "=&v"(vs[2]), "=&v"(vs[3])
+      : "v"(a.k[0]), "v"(a.k[1]), "v"(a.k[2]), "v"(a.k[3]), "v"(a.v[0]), "v"(a.v[1]),
+        "v"(a.v[2]), "n"(OFF), "v"(a.v[3]), "v"(a.v[4]), "n"(OFF + 16), "n"(OFF + 128),
+        "n"(OFF + 144)
+      : "memory");
+}
+
+// Two E4M3 codes (bytes 0, 1 of the low or high half of x) as an fp16 pair,
+// exactly (every E4M3 value is an fp16 value).
+template <bool kHigh>
+__device__ __forceinline__ half2_t e4m3x2_to_f16(unsigned x) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, kHigh);
+}
+
+// Eight FP4 E2M1 codes (one dword, element 2m in the low nibble of byte m) as
+// fp16 values, elements 2m and 2m + 1 multiplied by the pair s[m]. The
+// conversion runs at scale 1 (the conversion's own scale operand takes only
+// a power of two: measured on the hardware); each product of an E2M1 value
+// (at most 2 significant bits, |x| <= 6) and an E4M3 scale (at most 4 bits,
+// 2^-9 <= |s| <= 448, or 0) is an fp16 value, so the multiply is exact.
+__device__ __forceinline__ half8_t fp4x8_to_f16(unsigned x, half2_t s0, half2_t s1, half2_t s2,
+                                                half2_t s3) {
+  const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s0;
+  const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s1;
+  const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2;
+  const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s3;
+  return (half8_t){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Fold tile rows [t, t + 32) of an FP4 tile held in LDS stage `par` into
+// acc. K: lane (G, j) holds depth 32G .. 32G + 31 of row 16h + j (q is read
+// in the same depth order); each depth block of 16 has its own scale. QK
+// runs as two 16-row halves, so lane (G, j) ends with the scores of rows
+// rowE(G, 0..7) for head j, the B layout of a K = 32 PV MFMA. V: the
+// transposed reads give lane (G, i) column c of rows rowE(G, 0..7); each of
+// those rows has its own scale for c's block, applied per element pair.
+__device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
+                                                 const uint4_t (&qb)[4], int t, int hi,
+                                                 float scale_log2, WaveAcc& acc) {
+  const int lane = threadIdx.x & 63, G = lane >> 4;
+  const float kNegInf = -__builtin_inff();
+  uint4_t kd[2];
+  unsigned ks[2];
+  uint2 vt[4];
+  uint4_t vsc[4];
+  if (par)
+    read_stage_fp4<stage_bytes<kFmtFp4>()>(la, kd, ks, vt, vsc);
+  else
+    read_stage_fp4<0>(la, kd, ks, vt, vsc);
+
+  float4_t sc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const half2_t s2 = e4m3x2_to_f16<false>(ks[h]);   // blocks 2G, 2G + 1 of row 16h + j
+    const half2_t sa = {s2.x, s2.x}, sb = {s2.y, s2.y};
+    sc[h] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const half2_t sp = kk < 2 ? sa : sb;
+      sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fp4x8_to_f16(kd[h][kk], sp, sp, sp, sp),
+                                                     __builtin_bit_cast(half8_t, qb[kk]), sc[h],
+                                                     0, 0, 0);
+    }
+  }
+
+  float sv[8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int row = (e < 4 ? 0 : 16) + 4 * G + (e & 3);
+    const float x = (t + row) < hi ? sc[e >> 2][e & 3] * scale_log2 : kNegInf;
+    sv[e] = x;
+    mx = fmaxf(mx, x);
+  }
+  mx = max_over_row_groups(mx);
+  const float m_new = fmaxf(acc.m, mx);
+  const float alpha = exp2_hw(acc.m - m_new);
+  acc.m = m_new;
+
+  half8_t ph, pl;
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = (sv[e] == kNegInf) ? 0.f : exp2_hw(sv[e] - m_new);
+    psum += p;
+    short hs, ls;
+    split_weight<false>(p, hs, ls);
+    ph[e] = __builtin_bit_cast(_Float16, hs);
+    pl[e] = __builtin_bit_cast(_Float16, ls);
+  }
+  acc.l = acc.l * alpha + psum;
+
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+  // V scales: rows rowE(G, 2m) and rowE(G, 2m + 1) are consecutive rows;
+  // dword 2e + (db / 4) of vsc (e = local row) holds row e's scales of
+  // blocks 4 (db / 4) .. +3. For each row pair and block pair (db, db + 1)
+  // one byte permute gathers the four scale bytes, two conversions give the
+  // fp16 pairs.
+  const unsigned* vw = reinterpret_cast<const unsigned*>(vsc);
+#pragma unroll
+  for (int rd = 0; rd < 4; ++rd) {
+    const int db = 2 * rd, hw = db >> 2, c = db & 3;
+    const unsigned sel = (unsigned)c | ((4u + c) << 8) | ((c + 1u) << 16) | ((5u + c) << 24);
+    half2_t p0[4], p1[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const unsigned w = __builtin_amdgcn_perm(vw[2 * (2 * m + 1) + hw], vw[2 * (2 * m) + hw], sel);
+      p0[m] = e4m3x2_to_f16<false>(w);
+      p1[m] = e4m3x2_to_f16<true>(w);
+    }
+    const half8_t va0 = fp4x8_to_f16(vt[rd].x, p0[0], p0[1], p0[2], p0[3]);
+    const half8_t va1 = fp4x8_to_f16(vt[rd].y, p1[0], p1[1], p1[2], p1[3]);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0, ph, acc.O[db], 0, 0, 0);
+    acc.O[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0, pl, acc.O[db], 0, 0, 0);
+    acc.O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1, ph, acc.O[db + 1], 0, 0, 0);
+    acc.O[db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1, pl, acc.O[db + 1], 0, 0, 0);
+  }
+}
+
 // Fold tile rows [t, t + 32) of an E4M3 tile held in LDS stage `par` into
 // acc. QK runs as two 16-row halves on the fp16 MFMA (K converted exactly);
 // lane (G, j) then holds the scores of rows 4G .. 4G+3 and 16 + 4G .. +3
@@ -716,7 +963,7 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   const float kNegInf = -__builtin_inff();
   uint2 kr[8], vr[8];
   if (par)
-    read_stage8<kStageHalves * 2>(la, kr, vr);
+    read_stage8<stage_bytes<kFmtE4m3>()>(la, kr, vr);
   else
     read_stage8<0>(la, kr, vr);
 
@@ -780,7 +1027,7 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   uint4_t kr[4];
   short4_t vr[8];
   if (par)
-    read_stage<kStageHalves * 2>(la, kr, vr);
+    read_stage<stage_bytes<kFmtF16>()>(la, kr, vr);
   else
     read_stage<0>(la, kr, vr);
   const uint4_t k0 = kr[0], k1 = kr[1], k2 = kr[2], k3 = kr[3];
@@ -846,12 +1093,15 @@ __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, i
                                           uint4_t (&qb)[4], WaveAcc& acc) {
   if (first) {
     // the q loads (the first 1 or 2 of the group) landed
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<kG4>() - (kG4 ? 1 : 2)) : "memory");
-    read_q<kG4>(qslot, group_of<kG4>(P), qb);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<F, kG4>() - (kG4 ? 1 : 2))
+                 : "memory");
+    read_q<kG4, F>(qslot, group_of<kG4>(P), qb);
   }
   issue_tile<F, kPaged, kG4>(P, nseg, nt, has_next, next_new_seg, nxt, qslot, npb);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<kG4>()) : "memory");   // K, V landed
-  if constexpr (F == kFmtE4m3)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<F, kG4>()) : "memory");   // K, V landed
+  if constexpr (F == kFmtFp4)
+    compute_tile_fp4(la, par, qb, t, hi, P.scale_log2, acc);
+  else if constexpr (F == kFmtE4m3)
     compute_tile8(la, par, qb, t, hi, P.scale_log2, acc);
   else
     compute_tile<F == kFmtBf16>(la, par, qb, t, hi, P.scale_log2, acc);
@@ -897,9 +1147,9 @@ template <bool kG4> constexpr int heads_per_thread() { return kG4 ? 1 : kMaxGrou
 // before the waves' next loads into them. kG4 form: rows4 is reused from
 // segment to segment, so the first barrier orders the previous merge's
 // reads before this merge's writes.
-template <bool kG4>
+template <bool kG4, int kSH>
 __device__ __forceinline__ void merge_waves(const WaveAcc& acc, int group, int par, MergeLds& sm,
-                                            e16_t (*stages)[2][kStageHalves], MergeRows4* rows4,
+                                            e16_t (*stages)[2][kSH], MergeRows4* rows4,
                                             float (&M)[heads_per_thread<kG4>()],
                                             float (&den)[heads_per_thread<kG4>()],
                                             float (&n0)[heads_per_thread<kG4>()],
@@ -1145,7 +1395,8 @@ __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, i
 // preloaded in scalar registers (kernel-argument preloading, gfx950): the
 // lengths load is issued before the rest of the arguments have been read.
 template <int F, bool kPaged, bool kG4>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<F>(), waves_per_simd<F>())))
 void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Params P) {
   int raw_len = 0;
   if (wave_planner) {
@@ -1157,7 +1408,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   __shared__ long long red[kWaves];
   __shared__ long long sh_found;
   __shared__ int sh_found_b, sh_found_len;
-  __shared__ __attribute__((aligned(16))) e16_t stages[kWaves][2][kStageHalves];
+  __shared__ __attribute__((aligned(16))) e16_t stages[kWaves][2][stage_halves<F>()];
   __shared__ __attribute__((aligned(16))) e16_t qslots[kWaves][q_halves<kG4>()];
   __shared__ MergeLds sm;
   __shared__ __attribute__((aligned(16))) typename MergeRowsOf<kG4>::type rows4_lds;
@@ -1230,7 +1481,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   int pt = s.lo + kRows * wv;
   const bool pf_ok = tile_first<kRows>(P, pf, pt, p1, wv, lens_v);
   PageBases pbs;                                    // paged: pages of the issued tile
-  if constexpr (kPaged) pbs = page_bases<kRows>(P, pf, pt, pf_ok);
+  if constexpr (kPaged) pbs = page_bases<F>(P, pf, pt, pf_ok);
   issue_tile<F, kPaged, kG4>(P, pf, pt, pf_ok, true, st0, qslot, pbs);
   zero_empty_sequences(P, lens_v, w);               // overlaps the first tile's loads
   int par = 0;
@@ -1250,7 +1501,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
       Seg nf = pf;
       int nt = pt;
       const bool n_ok = tile_next<kRows>(P, nf, nt, p1, wv, lens_v);
-      if constexpr (kPaged) pbs = page_bases<kRows>(P, nf, nt, n_ok);
+      if constexpr (kPaged) pbs = page_bases<F>(P, nf, nt, n_ok);
       tile_step<F, kPaged, kG4>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
                 nf.off != s.off, pbs, t, s.hi, qb, acc);
       pf = nf;
@@ -1261,7 +1512,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
     constexpr int kHeads = heads_per_thread<kG4>();
     const int group = group_of<kG4>(P);
     float M[kHeads], den[kHeads], n0[kHeads], n1[kHeads];
-    merge_waves<kG4>(acc, group, par, sm, stages, rows4, M, den, n0, n1);
+    merge_waves<kG4, stage_halves<F>()>(acc, group, par, sm, stages, rows4, M, den, n0, n1);
     const int d = (tid & 63) * 2;
     const int seg_id = s.b * P.kv_heads + s.g;
 
@@ -1389,7 +1640,23 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(const int2* seg_d
 
 }  // namespace
 
-int resident_workgroups_per_cu() {
+int resident_workgroups_per_cu(bool fp4) {
+  if (fp4) {
+    const void* kernels[4] = {(const void*)gqa_decode_pieces<kFmtFp4, false, true>,
+                              (const void*)gqa_decode_pieces<kFmtFp4, true, true>,
+                              (const void*)gqa_decode_pieces<kFmtFp4, false, false>,
+                              (const void*)gqa_decode_pieces<kFmtFp4, true, false>};
+    int m = 1 << 30;
+    for (const void* k : kernels) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+      }
+      m = n < m ? n : m;
+    }
+    return m;
+  }
   const void* kernels[12] = {
       (const void*)gqa_decode_pieces<kFmtF16, false, true>,
       (const void*)gqa_decode_pieces<kFmtBf16, false, true>,
@@ -1435,6 +1702,8 @@ size_t segment_bytes_for_batch(int batch, int kv_heads) {
 template <int F, bool kPaged, bool kG4>
 hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
                           hipEvent_t* events) {
+  // The combine only depends on the output type: fp16 for every format but bf16.
+  constexpr int kCombineF = F == kFmtBf16 ? kFmtBf16 : kFmtF16;
   hipError_t err = hipSuccess;
   const dim3 pieces_grid((unsigned)grid),
       combine_grid((unsigned)(batch * P.kv_heads * (P.combine_per_head ? P.group : 1))),
@@ -1445,14 +1714,14 @@ hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_
     hipExtLaunchKernelGGL(gqa_decode_pieces<F, kPaged, kG4>, pieces_grid, block, 0, stream, events[0],
                           events[1], 0, P.seq_lens, P.batch, P.wave_planner, P);
     if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
-    hipExtLaunchKernelGGL(gqa_decode_combine<F, kG4>, combine_grid, block, 0, stream, events[2],
+    hipExtLaunchKernelGGL(gqa_decode_combine<kCombineF, kG4>, combine_grid, block, 0, stream, events[2],
                           events[3], 0, P.seg_desc, P.combine_per_head, P.group, P);
     return hipGetLastError();
   }
   gqa_decode_pieces<F, kPaged, kG4>
       <<<pieces_grid, block, 0, stream>>>(P.seq_lens, P.batch, P.wave_planner, P);
   if ((err = hipGetLastError()) != hipSuccess || P.fused) return err;
-  gqa_decode_combine<F, kG4>
+  gqa_decode_combine<kCombineF, kG4>
       <<<combine_grid, block, 0, stream>>>(P.seg_desc, P.combine_per_head, P.group, P);
   return hipGetLastError();
 }
@@ -1467,6 +1736,11 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.fused = tickets != nullptr ? 1 : 0;
   P.q = static_cast<const e16_t*>(q);
   P.kv = static_cast<const e16_t*>(kv);
+  P.kv_scales = static_cast<const uint8_t*>(layout.kv_scales);
+  P.sc_sb = layout.sc_sb;
+  P.sc_sk = layout.sc_sk;
+  P.sc_sh = layout.sc_sh;
+  P.sc_sr = layout.sc_sr;
   P.seq_lens = seq_lens;
   P.out = static_cast<e16_t*>(out);
   const int group = layout.q_heads / layout.kv_heads;
@@ -1528,6 +1802,8 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
       return GQA_LAUNCH(kFmtBf16);
     case ElemType::kE4m3Kv:
       return GQA_LAUNCH(kFmtE4m3);
+    case ElemType::kFp4Kv:
+      return GQA_LAUNCH(kFmtFp4);
     default:
       return GQA_LAUNCH(kFmtF16);
   }

@@ -10,8 +10,8 @@
 namespace gqa {
 
 // Element types: q, kv and out all fp16 or all bf16; or fp16 q and out with
-// OCP FP8 E4M3 kv.
-enum class ElemType { kF16, kBf16, kE4m3Kv };
+// OCP FP8 E4M3 kv, or with block-scaled FP4 kv (E2M1 codes and E4M3 scales).
+enum class ElemType { kF16, kBf16, kE4m3Kv, kFp4Kv };
 
 // Addressing of q and kv, in bytes (see the kernel's Params). A non-null
 // block_table selects the paged kernels: kv_sb is then the page stride, and
@@ -21,6 +21,10 @@ struct Layout {
   const int32_t* block_table;
   int max_pages, page_shift, num_pages;
   int q_heads, kv_heads;   // q_heads a multiple of kv_heads, at most 8 times it
+  // FP4 kv: the block scales (8 bytes per K or V row), addressed like kv
+  // (kv_scales + b*sc_sb + kind*sc_sk + g*sc_sh + i*sc_sr; paged: page*sc_sb).
+  const void* kv_scales;
+  long long sc_sb, sc_sk, sc_sh, sc_sr;
 };
 
 // How the device-side planner cuts the valid rows into pieces.
@@ -32,8 +36,9 @@ struct SplitConfig {
   int row_align;      // 1, or 16 for paged caches (pieces and segments 16-row aligned)
 };
 
-// Workgroups of the pieces kernel that fit on one CU at once (0 on error).
-int resident_workgroups_per_cu();
+// Workgroups of the pieces kernel that fit on one CU at once (0 on error),
+// for the FP4 kernels or for the others.
+int resident_workgroups_per_cu(bool fp4);
 
 // Number of workgroups launched for this shape and split (forced pieces must
 // already be a multiple of cfg.row_align).

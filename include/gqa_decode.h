@@ -132,9 +132,11 @@ int gqa_decode_chunked(const void* q, const void* kv, const int32_t* seq_lens, v
 typedef enum gqa_dtype {
   GQA_DTYPE_F16 = 0,     /* q, kv and out are IEEE binary16 (the page-4 operation)      */
   GQA_DTYPE_BF16 = 1,    /* q, kv and out are bfloat16 (8-bit exponent, 7-bit fraction)  */
-  GQA_DTYPE_E4M3_KV = 2  /* q and out binary16; kv holds OCP FP8 E4M3 bytes (1 sign,
+  GQA_DTYPE_E4M3_KV = 2, /* q and out binary16; kv holds OCP FP8 E4M3 bytes (1 sign,
                             4 exponent bits with bias 7, 3 fraction bits; no
                             infinities; S.1111.111 is NaN), one byte per element  */
+  GQA_DTYPE_FP4_KV = 3   /* q and out binary16; kv holds block-scaled FP4: only
+                            through gqa_decode_fp4 (declared below)               */
 } gqa_dtype;
 
 /*
@@ -227,6 +229,58 @@ typedef struct gqa_layout {
 int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* out, int dtype,
                   const gqa_layout* layout, float q_scale, float k_scale, float v_scale,
                   int batch, int capacity, int chunk_len, hipStream_t stream);
+
+/* E4M3 block scales per 128-element FP4 head row (one per 16 elements). */
+#define GQA_FP4_SCALES_PER_ROW 8
+
+/*
+ * Block scales of an FP4 cache. Strides are in bytes (the scales are one
+ * byte each) and follow kv's: scales + b*stride_batch + kind*stride_kind +
+ * g*stride_head + i*stride_row is the first of the 8 scales of K (kind 0) or
+ * V (kind 1) row i of KV head g of sequence b; for a paged cache b is the
+ * page id and i the row within the page, and stride_batch the page stride.
+ * All four strides 0 select the contiguous layout [blocks][2][Hkv][rows][8]
+ * (blocks = batch and rows = capacity, or num_pages and page_size). Strides
+ * must be multiples of 4, stride_row at least 8, and stride_row times
+ * capacity (paged: page_size) below 2^31; scales must be 4-byte aligned
+ * device memory on the decode's device.
+ */
+typedef struct gqa_block_scales {
+  const void* scales;      /* device uint8 E4M3 codes                  */
+  int64_t stride_batch;    /* [2*Hkv*C*8]                             */
+  int64_t stride_kind;     /* [Hkv*C*8]                               */
+  int64_t stride_head;     /* [C*8]                                   */
+  int64_t stride_row;      /* [8]                                     */
+} gqa_block_scales;
+
+/*
+ * gqa_decode_fp4 -- gqa_decode_ex for a block-scaled FP4 cache (the K/V page
+ * format named on the FlashInfer NVFP4 paged-context attention page: E2M1
+ * values with E4M3 block scales, dequantised in on-chip memory).
+ *
+ * kv holds, per K or V head row, 64 bytes of E2M1 codes: element 2m in the
+ * low nibble of byte m, element 2m + 1 in the high nibble; a code is 1 sign
+ * bit, 2 exponent bits with bias 1 and 1 fraction bit (magnitudes 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6). `scales` gives each row 8 E4M3 codes (format as for
+ * GQA_DTYPE_E4M3_KV), code k scaling elements 16k .. 16k + 15. Element value
+ * = E2M1 value x block scale; k_scale and v_scale are per-tensor scales on
+ * top (as in gqa_decode_typed), q and out are binary16. The decode is then
+ * that of gqa_decode_typed on the element values, in fp32 (each element
+ * value is an fp16 value, so it enters the arithmetic exactly).
+ * layout: as for gqa_decode_ex, with kv strides counted in bytes (the code
+ * bytes are kv's elements): the contiguous layout is [batch, 2, Hkv,
+ * capacity, 64] (kv_stride_row 64). Paged caches need page_size >= 32
+ * (FP4 tiles are 32 rows); chunk_len is then rounded up to a multiple of
+ * 32. Scales of rows inside [0, L) that are NaN are outside the contract;
+ * rows at or beyond L (codes and scales) are never read.
+ * Returns GQA_ERR_NULL if scales (or scales->scales) is NULL, and the
+ * errors of gqa_decode_ex; gqa_decode_typed and gqa_decode_ex reject
+ * GQA_DTYPE_FP4_KV with GQA_ERR_BAD_ARG.
+ */
+int gqa_decode_fp4(const void* q, const void* kv, const gqa_block_scales* scales,
+                   const int32_t* seq_lens, void* out, const gqa_layout* layout, float q_scale,
+                   float k_scale, float v_scale, int batch, int capacity, int chunk_len,
+                   hipStream_t stream);
 
 /*
  * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace

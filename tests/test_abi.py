@@ -52,7 +52,7 @@ def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     assert names == sorted([
         "gqa_decode", "gqa_decode_chunked", "gqa_decode_typed", "gqa_decode_ex",
-        "gqa_decode_workspace_bytes", "gqa_decode_set_launch_form",
+        "gqa_decode_fp4", "gqa_decode_workspace_bytes", "gqa_decode_set_launch_form",
         "gqa_decode_release_workspace", "gqa_decode_status_string", "gqa_decode_last_error",
         "gqa_decode_profile_begin", "gqa_decode_profile_end"])
 
@@ -260,6 +260,75 @@ def test_head_count_argument_errors(lib):
     # out extends over Hq rows per sequence: it must not reach kv
     lay = _layout(num_q_heads=64, num_kv_heads=8, q_stride_batch=64 * 128)
     assert _call_ex(lib, lay, out=0x20000000 - 2 * 64 * 128 * 2 + 256) == ALIAS
+
+
+def _fp4_layout(**kw):
+    C = kw.pop("C", 64)
+    d = dict(kv_stride_batch=2 * 8 * C * 64, kv_stride_kind=8 * C * 64, kv_stride_head=C * 64,
+             kv_stride_row=64)
+    d.update(kw)
+    return _layout(C=C, **d)
+
+
+def _call_fp4(lib, lay="default", scales=0x60000, strides=(0, 0, 0, 0), B=2, C=64, chunk=0,
+              out=0x40000, ks=1.0):
+    from gqa_token_decode_amd import _BlockScales
+
+    lay = _fp4_layout(C=C) if lay == "default" else lay
+    sc = None if scales is None else _BlockScales(scales, *strides)
+    return lib.gqa_decode_fp4(0x10000, 0x20000000, ctypes.byref(sc) if sc else None, 0x30000, out,
+                              ctypes.byref(lay) if lay else None, 1.0, ks, 1.0, B, C, chunk, None)
+
+
+def test_fp4_entry_point_argument_errors(lib):
+    expected = MISMATCH if _gpu_visible() else NO_DEVICE
+    assert _call_fp4(lib) == expected                        # contiguous codes and scales
+    assert _call_fp4(lib, lay=None) == expected              # layout NULL: 64-byte rows
+    assert _call_fp4(lib, strides=(2 * 8 * 64 * 8, 8 * 64 * 8, 64 * 8, 8)) == expected
+    assert _call_fp4(lib, scales=None) == NULL
+    assert _call_fp4(lib, scales=0) == NULL
+    assert _call_fp4(lib, scales=0x60002) == MISALIGNED
+    assert _call_fp4(lib, strides=(2 * 8 * 64 * 8, 8 * 64 * 8, 64 * 8, 6)) == BAD_ARG   # not a multiple of 4
+    assert _call_fp4(lib, strides=(2 * 8 * 64 * 4, 8 * 64 * 4, 64 * 4, 4)) == BAD_ARG   # under 8 bytes
+    assert "8 bytes" in lib.gqa_decode_last_error().decode()
+    assert _call_fp4(lib, strides=(0, 0, 0, 1 << 26), C=64) == BAD_ARG                  # 32-bit offsets
+    assert _call_fp4(lib, lay=_fp4_layout(kv_stride_row=48)) == BAD_ARG                 # does not cover 64 B
+    assert _call_fp4(lib, lay=_fp4_layout(kv_stride_row=80)) == expected
+    assert _call_fp4(lib, ks=float("inf")) == BAD_ARG
+    # out overlapping the scales
+    assert _call_fp4(lib, scales=0x40000 + 1024) == ALIAS
+    # paged: pages of at least 32 rows
+    bt = 0x50000
+    paged = dict(block_table=bt, max_pages=4, num_pages=9)
+    assert _call_fp4(lib, lay=_fp4_layout(page_size=32, C=32, **paged), C=128) == expected
+    assert _call_fp4(lib, lay=_fp4_layout(page_size=16, C=16, **paged), C=64) == BAD_ARG
+    assert ">= 32" in lib.gqa_decode_last_error().decode()
+    # the other entry points take no FP4 cache
+    assert _call_typed(lib, dtype=3) == BAD_ARG
+    assert "gqa_decode_fp4" in lib.gqa_decode_last_error().decode()
+    assert _call_ex(lib, _layout(), dtype=3) == BAD_ARG
+
+
+def test_fp4_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    import gqa_token_decode_amd as g
+
+    q = torch.zeros((2, 32, 128), dtype=torch.float16)
+    codes = torch.zeros((2, 2, 8, 64, 64), dtype=torch.uint8)
+    scales = torch.zeros((2, 2, 8, 64, 8), dtype=torch.uint8)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        g.gqa_decode_fp4(q, codes.to(torch.int8), scales, lens)
+    with pytest.raises(TypeError):
+        g.gqa_decode_fp4(q.to(torch.bfloat16), codes, scales, lens)
+    with pytest.raises(ValueError, match="kv_codes must have shape"):
+        g.gqa_decode_fp4(q, torch.zeros((2, 2, 8, 64, 128), dtype=torch.uint8), scales, lens)
+    with pytest.raises(ValueError, match="kv_scales must have shape"):
+        g.gqa_decode_fp4(q, codes, torch.zeros((2, 2, 8, 64, 16), dtype=torch.uint8), lens)
+    with pytest.raises(TypeError):
+        g.gqa_decode_fp4(q, codes, scales.to(torch.int32), lens)
+    with pytest.raises(ValueError, match="GPU"):                  # CPU tensors
+        g.gqa_decode_fp4(q, codes, scales, lens)
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
