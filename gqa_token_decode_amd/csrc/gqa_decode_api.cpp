@@ -232,7 +232,7 @@ int* get_tickets(int dev, hipStream_t stream, size_t count, int* status) {
 // Strides resolved to bytes, with the address range each of q, kv (and the
 // FP4 block scales) spans.
 struct Resolved {
-  gqa::Layout lay;
+  gqa::Layout lay{};          // value-initialised: kv_scales stays null unless set
   size_t q_extent = 0, kv_extent = 0, table_bytes = 0, scale_extent = 0;
   int row_align = 1;
 };

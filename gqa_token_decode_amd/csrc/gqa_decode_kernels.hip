@@ -898,15 +898,22 @@ __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
   }
 
   float sv[8];
+  if (t + 32 <= hi) {                    // the whole tile is in range (wave-uniform)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = sc[e >> 2][e & 3] * scale_log2;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = (e < 4 ? 0 : 16) + 4 * G + (e & 3);
+      sv[e] = (t + row) < hi ? sc[e >> 2][e & 3] * scale_log2 : kNegInf;
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = (e < 4 ? 0 : 16) + 4 * G + (e & 3);
-    const float x = (t + row) < hi ? sc[e >> 2][e & 3] * scale_log2 : kNegInf;
-    sv[e] = x;
-    mx = fmaxf(mx, x);
-  }
+  for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = max_over_row_groups(mx);
+  // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
+  // tile, where acc.m is still -inf.
   const float m_new = fmaxf(acc.m, mx);
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
@@ -915,7 +922,7 @@ __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = (sv[e] == kNegInf) ? 0.f : exp2_hw(sv[e] - m_new);
+    const float p = exp2_hw(sv[e] - m_new);      // 0 for rows out of range (score -inf)
     psum += p;
     short hs, ls;
     split_weight<false>(p, hs, ls);
@@ -924,8 +931,12 @@ __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
   }
   acc.l = acc.l * alpha + psum;
 
+  // alpha is exactly 1 in every lane once no running maximum grows; the
+  // rescale is then an identity and is skipped (a wave-uniform test).
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+    for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+  }
   // V scales: rows rowE(G, 2m) and rowE(G, 2m + 1) are consecutive rows;
   // dword 2e + (db / 4) of vsc (e = local row) holds row e's scales of
   // blocks 4 (db / 4) .. +3. For each row pair and block pair (db, db + 1)
@@ -979,14 +990,19 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   }
 
   float sv[8];
+  if (t + 32 <= hi) {                    // the whole tile is in range (wave-uniform)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] = sc[e >> 2][e & 3] * scale_log2;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = (e < 4 ? 0 : 16) + 4 * G + (e & 3);
+      sv[e] = (t + row) < hi ? sc[e >> 2][e & 3] * scale_log2 : kNegInf;
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int row = (e < 4 ? 0 : 16) + 4 * G + (e & 3);
-    const float x = (t + row) < hi ? sc[e >> 2][e & 3] * scale_log2 : kNegInf;
-    sv[e] = x;
-    mx = fmaxf(mx, x);
-  }
+  for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = max_over_row_groups(mx);
   // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
   // tile, where acc.m is still -inf.
@@ -998,7 +1014,7 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = (sv[e] == kNegInf) ? 0.f : exp2_hw(sv[e] - m_new);
+    const float p = exp2_hw(sv[e] - m_new);      // 0 for rows out of range (score -inf)
     psum += p;
     short hs, ls;
     split_weight<false>(p, hs, ls);
@@ -1008,8 +1024,12 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   acc.l = acc.l * alpha + psum;
 
   // O^T = V^T P^T: every accumulator of this lane belongs to head j.
+  // alpha is exactly 1 in every lane once no running maximum grows; the
+  // rescale is then an identity and is skipped (a wave-uniform test).
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+    for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+  }
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     const half8_t va = e4m3x8_to_f16(vr[db]);
@@ -1041,13 +1061,16 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   sc = mfma_qk<kBf16>(k3, qb[3], sc);
 
   float sv[4];
+  if (t + 16 <= hi) {                    // the whole tile is in range (wave-uniform)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = sc[r] * scale_log2;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (t + 4 * G + r) < hi ? sc[r] * scale_log2 : kNegInf;
+  }
   float mx = kNegInf;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float x = (t + 4 * G + r) < hi ? sc[r] * scale_log2 : kNegInf;
-    sv[r] = x;
-    mx = fmaxf(mx, x);
-  }
+  for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[r]);
   mx = max_over_row_groups(mx);
   // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
   // tile, where acc.m is still -inf.
@@ -1059,7 +1082,7 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float p = (sv[r] == kNegInf) ? 0.f : exp2_hw(sv[r] - m_new);
+    const float p = exp2_hw(sv[r] - m_new);      // 0 for rows out of range (score -inf)
     psum += p;
     short h, l;
     split_weight<kBf16>(p, h, l);
@@ -1069,8 +1092,12 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   acc.l = acc.l * alpha + psum;
 
   // O^T = V^T P^T: every accumulator of this lane belongs to head j.
+  // alpha is exactly 1 in every lane once no running maximum grows; the
+  // rescale is then an identity and is skipped (a wave-uniform test).
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+    for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
+  }
 
   const short4_t vv[8] = {v0, v1, v2, v3, v4, v5, v6, v7};
 #pragma unroll
