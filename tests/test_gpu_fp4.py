@@ -214,3 +214,30 @@ def test_fp4_launch_forms_agree_bitwise(spec, chunk):
     assert np.array_equal(res[0], res[1])
     if cap <= 3000:
         check(torch.from_numpy(res[1].view(np.float16)), oracle_fp4(w), f"fp4 forms {cap}")
+
+
+def test_fp4_paged_table_entries_beyond_lengths_and_invalid_ids():
+    # Entries past a sequence's pages are never read (any value gives the
+    # same bits); an out-of-range id inside a length reads zero codes and
+    # scales (zero K and V rows) without a fault, other sequences unchanged.
+    torch = _torch()
+    print("case fp4 paged table", flush=True)
+    w = workloads.build("fp4 paged table", 89, 256, [256, 200, 64], elem="nvfp4")
+    codes, scales = w.kv_to_device(DEV), w.scales_to_device(DEV)
+    cp, sp, table = _paginate_fp4(codes, scales, w.valid_lengths, 32, seed=9)
+    base = bits(run(w, cp, sp, block_table=table))
+    tail = table.clone()
+    tail[tail < 0] = 1 << 30
+    assert np.array_equal(bits(run(w, cp, sp, block_table=tail)), base)
+    bad = table.clone()
+    bad[1, 2] = cp.shape[0] + 7
+    bad[1, 3] = -5
+    got = run(w, cp, sp, block_table=bad)
+    assert np.all(np.isfinite(got.float().cpu().numpy()))
+    assert np.array_equal(bits(got)[[0, 2]], base[[0, 2]])
+    # equal to the cache with sequence 1's rows 64..127 zeroed (codes and scales)
+    codes0, scales0 = codes.clone(), scales.clone()
+    codes0[1, :, :, 64:128] = 0
+    scales0[1, :, :, 64:128] = 0
+    cp0, sp0, table0 = _paginate_fp4(codes0, scales0, w.valid_lengths, 32, seed=9)
+    assert np.array_equal(bits(got)[1], bits(run(w, cp0, sp0, block_table=table0))[1])
