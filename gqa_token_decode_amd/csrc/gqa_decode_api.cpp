@@ -49,8 +49,7 @@ struct DeviceInfo {
   bool ready = false;
   int status = GQA_OK;
   int cus = 0;
-  int resident = 0;       // decode workgroups per CU
-  int resident_fp4 = 0;   // the same for the FP4-cache kernels
+  int resident = 0;   // decode workgroups per CU
   std::string arch;
 };
 
@@ -109,10 +108,8 @@ const DeviceInfo& device_info(int dev) {
                     ? GQA_OK
                     : GQA_ERR_UNSUPPORTED_ARCH;
     if (di.status == GQA_OK) {
-      di.resident = gqa::resident_workgroups_per_cu(false);
+      di.resident = gqa::resident_workgroups_per_cu();
       if (di.resident <= 0) di.resident = 1;
-      di.resident_fp4 = gqa::resident_workgroups_per_cu(true);
-      if (di.resident_fp4 <= 0) di.resident_fp4 = 1;
     }
   }
   di.ready = true;
@@ -122,12 +119,11 @@ const DeviceInfo& device_info(int dev) {
 // One equal piece per workgroup that can be resident at once (times an
 // optional factor), so the whole decode runs in a single round.
 // row_align (1, or 16 / 32 for paged caches) rounds the piece and cost sizes up.
-gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, bool fp4) {
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align) {
   gqa::SplitConfig cfg;
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
   auto up = [row_align](int v) { return (v + row_align - 1) / row_align * row_align; };
-  const int resident = fp4 ? di.resident_fp4 : di.resident;
-  cfg.pieces = (di.cus > 0 ? di.cus : 256) * (resident > 0 ? resident : 1) * per_slot;
+  cfg.pieces = (di.cus > 0 ? di.cus : 256) * (di.resident > 0 ? di.resident : 1) * per_slot;
   cfg.min_piece = up(env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30));
   cfg.seg_cost = up(env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20));
   cfg.forced_piece = forced_piece > 0 ? up(forced_piece) : 0;
@@ -455,7 +451,7 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
       st = fail(di.status, "gqa_decode: device %d is %s; this library is built for gfx950", dev,
                 di.arch.c_str());
     } else {
-      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align, fp4);
+      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align);
       const int Hkv = res.lay.kv_heads, group = res.lay.q_heads / res.lay.kv_heads;
       const long long grid = gqa::grid_for(batch, capacity, Hkv, cfg);
       const size_t pbytes =
@@ -569,7 +565,7 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   std::lock_guard<std::mutex> lock(g_mu);
   const DeviceInfo& di = device_info(dev);
   if (di.status != GQA_OK) return 0;
-  const long long grid = gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0, 1, false));
+  const long long grid = gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0, 1));
   return gqa::segment_bytes_for_batch(batch, GQA_NUM_KV_HEADS) +
          gqa::partial_bytes_for_grid(grid, GQA_NUM_Q_HEADS / GQA_NUM_KV_HEADS);
 }

@@ -108,9 +108,6 @@ template <int F> constexpr int stage_halves() { return stage_bytes<F>() / 2; }
 template <int F, bool kG4> constexpr int loads_per_tile() {
   return (kG4 ? 1 : 2) + (F == kFmtFp4 ? 6 : 8);
 }
-// Workgroups per CU the pieces kernel is built for (waves per SIMD): the
-// FP4 stages are small enough for three.
-template <int F> constexpr int waves_per_simd() { return F == kFmtFp4 ? 3 : 2; }
 constexpr unsigned kBufferFlags = 0x00020000;     // raw buffer resource word 3 (gfx9 family)
 constexpr int kNonTemporal = 2;              // buffer load cache policy: nt
 constexpr int kHeadSlotFloats = 2 + kDim;   // one head of a partial: (max, den) + 128 sums
@@ -1422,8 +1419,7 @@ __device__ __forceinline__ void combine_segment(const Params& P, int b, int g, i
 // preloaded in scalar registers (kernel-argument preloading, gfx950): the
 // lengths load is issued before the rest of the arguments have been read.
 template <int F, bool kPaged, bool kG4>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd<F>(), waves_per_simd<F>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Params P) {
   int raw_len = 0;
   if (wave_planner) {
@@ -1667,24 +1663,8 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(const int2* seg_d
 
 }  // namespace
 
-int resident_workgroups_per_cu(bool fp4) {
-  if (fp4) {
-    const void* kernels[4] = {(const void*)gqa_decode_pieces<kFmtFp4, false, true>,
-                              (const void*)gqa_decode_pieces<kFmtFp4, true, true>,
-                              (const void*)gqa_decode_pieces<kFmtFp4, false, false>,
-                              (const void*)gqa_decode_pieces<kFmtFp4, true, false>};
-    int m = 1 << 30;
-    for (const void* k : kernels) {
-      int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess) {
-        (void)hipGetLastError();
-        return 0;
-      }
-      m = n < m ? n : m;
-    }
-    return m;
-  }
-  const void* kernels[12] = {
+int resident_workgroups_per_cu() {
+  const void* kernels[16] = {
       (const void*)gqa_decode_pieces<kFmtF16, false, true>,
       (const void*)gqa_decode_pieces<kFmtBf16, false, true>,
       (const void*)gqa_decode_pieces<kFmtE4m3, false, true>,
@@ -1696,7 +1676,11 @@ int resident_workgroups_per_cu(bool fp4) {
       (const void*)gqa_decode_pieces<kFmtE4m3, false, false>,
       (const void*)gqa_decode_pieces<kFmtF16, true, false>,
       (const void*)gqa_decode_pieces<kFmtBf16, true, false>,
-      (const void*)gqa_decode_pieces<kFmtE4m3, true, false>};
+      (const void*)gqa_decode_pieces<kFmtE4m3, true, false>,
+      (const void*)gqa_decode_pieces<kFmtFp4, false, true>,
+      (const void*)gqa_decode_pieces<kFmtFp4, true, true>,
+      (const void*)gqa_decode_pieces<kFmtFp4, false, false>,
+      (const void*)gqa_decode_pieces<kFmtFp4, true, false>};
   int m = 1 << 30;
   for (const void* k : kernels) {
     int n = 0;

@@ -36,9 +36,9 @@ struct SplitConfig {
   int row_align;      // 1, or 16 for paged caches (pieces and segments 16-row aligned)
 };
 
-// Workgroups of the pieces kernel that fit on one CU at once (0 on error),
-// for the FP4 kernels or for the others.
-int resident_workgroups_per_cu(bool fp4);
+// Workgroups of the pieces kernel that fit on one CU at once (the fewest
+// over its instantiations; 0 on error).
+int resident_workgroups_per_cu();
 
 // Number of workgroups launched for this shape and split (forced pieces must
 // already be a multiple of cfg.row_align).

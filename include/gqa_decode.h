@@ -286,9 +286,9 @@ int gqa_decode_fp4(const void* q, const void* kv, const gqa_block_scales* scales
  * gqa_decode_workspace_bytes -- size of the fp32 partial-result workspace
  * the automatic split of gqa_decode (fp16, 32 query and 8 KV heads) needs
  * for (batch, capacity) on the current device (a per-segment descriptor
- * table plus two partial slots per workgroup). Other element types, head
- * counts and forced splits may need more (the FP4 kernels run more
- * workgroups per CU); the library grows its cached workspace as needed.
+ * table plus two partial slots per workgroup). Other head counts and
+ * forced splits may need more; the library grows its cached workspace as
+ * needed.
  * Returns 0 for invalid sizes or when no device is available.
  */
 size_t gqa_decode_workspace_bytes(int batch, int capacity);
