@@ -241,3 +241,51 @@ def test_fp4_paged_table_entries_beyond_lengths_and_invalid_ids():
     scales0[1, :, :, 64:128] = 0
     cp0, sp0, table0 = _paginate_fp4(codes0, scales0, w.valid_lengths, 32, seed=9)
     assert np.array_equal(bits(got)[1], bits(run(w, cp0, sp0, block_table=table0))[1])
+
+
+def test_fp4_graph_replays_match_eager_bitwise():
+    # Captured calls hold only kernel nodes: every replay reproduces the eager
+    # bits, with unrelated eager work between replays and with lengths
+    # changed on the device.
+    torch = _torch()
+    g = _g()
+    print("case fp4 graph", flush=True)
+    ws = [workloads.build(f"fp4 graph {i}", 95 + i, 2048, lens, elem="nvfp4")
+          for i, lens in enumerate([[2048, 5, 700], [1, 1500, 33], [0, 64, 2048]])]
+    qs = [w.q_to_device(DEV) for w in ws]
+    codes = [w.kv_to_device(DEV) for w in ws]
+    scales = [w.scales_to_device(DEV) for w in ws]
+    lens = [torch.from_numpy(w.seq_lens).to(DEV) for w in ws]
+    outs = [torch.empty_like(q) for q in qs]
+
+    def calls():
+        for q, c, sc, ln, o in zip(qs, codes, scales, lens, outs):
+            g.gqa_decode_fp4(q, c, sc, ln, out=o)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    s.synchronize()
+    eager = [bits(o) for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for i, o in enumerate(outs):
+            assert np.array_equal(bits(o), eager[i]), f"replay {rep}, call {i}"
+    lens[0].copy_(torch.tensor([3, 2048, 0], dtype=torch.int32))
+    graph.replay()
+    torch.cuda.synchronize()
+    ref = g.gqa_decode_fp4(qs[0], codes[0], scales[0],
+                           torch.tensor([3, 2048, 0], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(outs[0]), bits(ref))
