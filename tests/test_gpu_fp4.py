@@ -186,6 +186,16 @@ def test_fp4_paged_cache(page_size, chunk):
     check(out, oracle_fp4(w), f"fp4 paged {page_size} chunk {chunk}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (28, 4), (8, 1)])
+def test_fp4_head_counts_paged(hq, hkv):
+    print(f"case fp4 heads {hq}/{hkv} paged", flush=True)
+    w = workloads.build("fp4 heads paged", 91 + hq, 300, [300, 1, 0, 97, 64], fill="nan",
+                        elem="nvfp4", q_heads=hq, kv_heads=hkv)
+    cp, sp, table = _paginate_fp4(w.kv_to_device(DEV), w.scales_to_device(DEV),
+                                  w.valid_lengths, 32, seed=hq)
+    check(run(w, cp, sp, block_table=table), oracle_fp4(w), f"fp4 heads {hq}/{hkv} paged")
+
+
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (28, 4), (16, 16), (8, 1), (6, 2)])
 def test_fp4_head_counts(hq, hkv):
     print(f"case fp4 heads {hq}/{hkv}", flush=True)

@@ -112,16 +112,19 @@ def test_head_counts_large_batch_block_planner(hq, hkv):
 
 
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (28, 4), (16, 16)])
-def test_head_counts_paged(hq, hkv):
+@pytest.mark.parametrize("elem", ["f16", "bf16", "e4m3"])
+def test_head_counts_paged(hq, hkv, elem):
+    print(f"case heads {hq}/{hkv} paged {elem}", flush=True)
     w = workloads.build("heads paged", 80 + hq, 512, [512, 1, 0, 300, 17], fill="nan",
-                        q_heads=hq, kv_heads=hkv)
+                        q_heads=hq, kv_heads=hkv, elem=elem)
     kv = w.kv_to_device(DEV)
     pages, table = _paginate(kv, w.valid_lengths, 32, seed=hq)
     torch = _torch()
     lens = torch.from_numpy(w.seq_lens).to(DEV)
-    out = _g().gqa_decode_paged(w.q_to_device(DEV), pages, table, lens, q_scale=w.q_scale)
+    out = _g().gqa_decode_paged(w.q_to_device(DEV), pages, table, lens, q_scale=w.q_scale,
+                                k_scale=w.k_scale, v_scale=w.v_scale)
     torch.cuda.synchronize()
-    _check(w, out, f"heads {hq}/{hkv} paged")
+    _check(w, out, f"heads {hq}/{hkv} paged {elem}")
 
 
 def test_head_counts_strided_q_equals_contiguous_bitwise():
