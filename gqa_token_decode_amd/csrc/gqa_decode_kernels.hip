@@ -465,15 +465,18 @@ __device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, i
 
 // Issue the loads of this wave's tile of segment s (rows [t, t + rows)) into
 // an LDS stage (K, then V) and the segment's G query rows into the wave's q
-// slot, in this order: q (1 load, or 2 in the general form), 4 x K, 4 x V.
+// slot, in this order: q (1 load, or 2 in the general form), 4 x K, 4 x V
+// (FP4: 2 x K codes, K scales, 2 x V codes, V scales).
 // Rows at or past s.hi read as zeros. With live == false the buffers are
 // empty: the same loads return zeros without touching memory, so every
 // pipeline step has the same shape. The q load is live only for a wave's
 // first tile of a segment (live_q); later tiles reuse the q registers, and
-// their empty q load leaves zeros in the slot. Each K/V load moves 1 KiB: 4 rows of 256 B (16-bit formats) or 8
-// rows of 128 B (E4M3). In LDS the rows are dense whatever the strides.
+// their empty q load leaves zeros in the slot. Each K/V load moves 1 KiB:
+// 4 rows of 256 B (16-bit formats), 8 rows of 128 B (E4M3) or 16 rows of
+// 64 B (FP4 codes). In LDS the rows are dense whatever the strides.
 // Paged caches (page size a multiple of 16): each 16-row half of a tile
-// lies in one page, whose offset the caller passes in pb.
+// lies in one page, whose offset the caller passes in pb (FP4: the whole
+// 32-row tile, pages and pieces being multiples of 32 rows).
 template <int F, bool kPaged, bool kG4>
 __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t, bool live,
                                            bool live_q, e16_t* stage, e16_t* qslot,
