@@ -1,7 +1,8 @@
 """Benchmark of the FP16 GQA single-token decode on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                [--no-cpu-baseline] [--graph] [--copy-calibration-mib N]
+                [--elem f16|bf16|e4m3|nvfp4] [--page-size P] [--q-heads H --kv-heads H]
+                [--no-cpu-baseline] [--copy-calibration-mib N]
 python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--workload NAME]
 
 One step = one gqa_decode call (split-KV pieces kernel + combine kernel)
