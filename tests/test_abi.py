@@ -346,3 +346,26 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
         with pytest.raises((RuntimeError, ValueError)):
             g.gqa_decode(q, torch.zeros(1, 2, 8, 4, 128, dtype=torch.float16),
                          torch.ones(1, dtype=torch.int32))
+
+
+def _c_abi_helper():
+    import importlib.util
+
+    path = os.path.join(ROOT, "tests", "c_abi", "build.py")
+    spec = importlib.util.spec_from_file_location("gqa_c_abi_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_c_program_reaches_the_abi_without_python(lib, tmp_path):
+    # A plain C11 program built against include/gqa_decode.h alone links to
+    # the library and gets its argument errors back (no device needed).
+    prog = _c_abi_helper().ensure_c_program()
+    res = subprocess.run([prog, "--bad-shape"], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert f"status {BAD_SHAPE}" in res.stdout and "batch" in res.stdout
+    missing = str(tmp_path / "nothing.bin")
+    res = subprocess.run([prog, missing, missing, missing, missing, "1", "16", "1.0"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 2 and "could not read" in res.stderr
