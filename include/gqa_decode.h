@@ -22,6 +22,14 @@
  * Arithmetic: fp16 inputs, fp32 accumulation for the dot products, the
  * softmax and the weighted sum, one round-to-nearest-even to fp16 at the end.
  *
+ * Entry points: gqa_decode (the page's call); gqa_decode_chunked (a fixed
+ * split length); gqa_decode_typed (bfloat16 tensors or an FP8 E4M3 cache,
+ * with per-tensor K/V scales); gqa_decode_ex (the same with explicit
+ * strides, other head counts and paged caches); gqa_decode_fp4 (a
+ * block-scaled FP4 cache); and helpers for the workspace, the launch form,
+ * kernel timing and error text. This library's extensions beyond the page
+ * are marked as such where they are declared.
+ *
  * All entry points are thread-safe. Compute entry points only enqueue work
  * on `stream` (no host synchronisation); a device-side fault surfaces at the
  * caller's next synchronisation. Every call reports its outcome as a
