@@ -246,6 +246,43 @@ def test_workspace_reuse_after_a_larger_call():
     check(run(small), oracle_of(small), "after large call")
 
 
+@pytest.mark.parametrize("form", ["two", "single"])
+def test_poisoned_partials_do_not_leak_into_the_next_call(form):
+    # The library's cached workspace cannot be written from outside, so it
+    # is poisoned through the API: a call whose valid rows hold NaN fills
+    # every partial slot it uses with NaN. The next call on the same stream
+    # (same workspace, same split) must return exactly the bits of the same
+    # call on a fresh stream (another workspace).
+    torch = _torch()
+    g = _g()
+    print(f"case poisoned partials {form}", flush=True)
+    g.set_launch_form(form)
+    try:
+        w = workloads.build("poison", 43, 600, [600, 421, 2, 599], fill="nan")
+        q, kv, lens = _device_inputs(w)
+        bad = kv.clone()
+        bad.view(torch.int16).fill_(0x7E00)                  # NaN everywhere
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        outs = []
+        for chunk in (0, 37):
+            with torch.cuda.stream(s1):
+                poisoned = g.gqa_decode(q, bad, lens, chunk_len=chunk)
+                after = g.gqa_decode(q, kv, lens, chunk_len=chunk)
+            with torch.cuda.stream(s2):
+                fresh = g.gqa_decode(q, kv, lens, chunk_len=chunk)
+            torch.cuda.synchronize()
+            assert np.isnan(poisoned.float().cpu().numpy()).all()
+            a = after.view(torch.int16).cpu().numpy()
+            f = fresh.view(torch.int16).cpu().numpy()
+            assert np.array_equal(a, f), f"chunk {chunk}"
+            outs.append(after.cpu().numpy())
+        check(outs[0], oracle_of(w), f"after poisoned partials ({form})")
+    finally:
+        g.set_launch_form("auto")
+
+
 def test_errors_are_raised_on_gpu():
     torch = _torch()
     g = _g()

@@ -631,3 +631,21 @@ def test_one_query_head_per_kv_head_is_per_head_attention():
         p = np.exp(s - s.max())
         p /= p.sum()
         assert np.abs(got[0, h] - p @ V).max() <= 1e-13
+
+
+def test_workload_inputs_match_recorded_fingerprints():
+    # The seeded inputs are byte-for-byte those recorded when the fixture
+    # was written (tests/golden/make_workload_hashes.py): a change of the
+    # input recipe, or of the random streams under it, shows up here.
+    import importlib.util
+
+    path = os.path.join(HERE, "golden", "make_workload_hashes.py")
+    spec = importlib.util.spec_from_file_location("make_workload_hashes", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    with open(os.path.join(HERE, "golden", "workload_sha256.json")) as f:
+        gold = json.load(f)
+    for name in workloads.WORKLOADS:
+        assert mod.fingerprint(name) == gold["f16"][name], name
+    for name, elem in mod.TYPED:
+        assert mod.fingerprint(name, elem) == gold["typed"][f"{name}/{elem}"], (name, elem)

@@ -285,12 +285,15 @@ def build(
     elem: str = "f16",
     q_heads: int = NUM_Q_HEADS,
     kv_heads: int = NUM_KV_HEADS,
+    with_kv: bool = True,
 ) -> Workload:
     """Draw a workload. ``lengths`` is a list or a callable taking the rng.
 
     Lengths may lie outside [0, capacity] (tests of clamping); only
     ``clip(L_b, 0, capacity)`` rows are drawn. Draw order: lengths, q, then
     per sequence K and V (the same order for any head counts).
+    ``with_kv=False`` stops after q (lengths and q are the same; the K/V
+    lists hold empty arrays): for checks of the first draws only.
     """
     rng = np.random.default_rng(seed)
     if callable(lengths):
@@ -305,7 +308,7 @@ def build(
     k_valid, v_valid = [], []
     k_scales, v_scales = ([], []) if elem == "nvfp4" else (None, None)
     for b in range(B):
-        L = int(min(max(lens[b], 0), capacity))
+        L = int(min(max(lens[b], 0), capacity)) if with_kv else 0
         if elem == "nvfp4":
             for sigma, vals, scs in ((sigma_k, k_valid, k_scales), (sigma_v, v_valid, v_scales)):
                 x = rng.standard_normal((kv_heads, L, HEAD_DIM), dtype=np.float32)
@@ -382,13 +385,15 @@ PAGE_SHAPES = ["page_b1_c64", "page_b4_c256", "page_b1_c1024", "page_b1_c4096"]
 
 
 def get(name: str, elem: str = "f16", q_heads: int = NUM_Q_HEADS,
-        kv_heads: int = NUM_KV_HEADS) -> Workload:
-    """Named workload; elem="bf16" or "e4m3" draws it (same seed and recipe)
-    in that element type, and other head counts draw it with Hq query and
-    Hkv KV heads (same lengths)."""
-    if (q_heads, kv_heads) == (NUM_Q_HEADS, NUM_KV_HEADS):
-        return WORKLOADS[name][1](elem)
-    return WORKLOADS[name][1](elem, q_heads=q_heads, kv_heads=kv_heads)
+        kv_heads: int = NUM_KV_HEADS, with_kv: bool = True) -> Workload:
+    """Named workload; elem="bf16", "e4m3" or "nvfp4" draws it (same seed and
+    recipe) in that element type, and other head counts draw it with Hq
+    query and Hkv KV heads (same lengths). with_kv=False: lengths and q only
+    (see build)."""
+    kw = {} if with_kv else {"with_kv": False}
+    if (q_heads, kv_heads) != (NUM_Q_HEADS, NUM_KV_HEADS):
+        kw.update(q_heads=q_heads, kv_heads=kv_heads)
+    return WORKLOADS[name][1](elem, **kw)
 
 
 def describe(name: str) -> str:
