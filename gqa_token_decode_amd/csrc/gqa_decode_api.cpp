@@ -154,6 +154,16 @@ void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
   for (Workspace& w : g_workspaces)
     if (w.device == dev && w.stream == stream) ws = &w;
   if (ws && ws->bytes >= bytes) return ws->ptr;
+  // Optional cap on the library's device memory (bytes; unset or 0: none).
+  if (const char* e = getenv("GQA_DECODE_WORKSPACE_LIMIT")) {
+    const unsigned long long cap = strtoull(e, nullptr, 10);
+    if (cap > 0 && bytes > cap) {
+      *status = fail(GQA_ERR_ALLOC,
+                     "gqa_decode: a workspace of %zu bytes exceeds GQA_DECODE_WORKSPACE_LIMIT=%llu",
+                     bytes, cap);
+      return nullptr;
+    }
+  }
   if (!ws) {
     g_workspaces.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0});
     ws = &g_workspaces.back();

@@ -302,6 +302,14 @@ int gqa_decode_fp4(const void* q, const void* kv, const gqa_block_scales* scales
 size_t gqa_decode_workspace_bytes(int batch, int capacity);
 
 /*
+ * Environment: GQA_DECODE_WORKSPACE_LIMIT=<bytes> caps the workspace the
+ * library allocates; a call that would need a larger one on its (device,
+ * stream) fails with GQA_ERR_ALLOC and enqueues nothing (workspaces already
+ * large enough are reused). GQA_DECODE_LAUNCH_FORM sets the initial launch
+ * form (see gqa_decode_set_launch_form).
+ */
+
+/*
  * gqa_decode_release_workspace -- free every cached workspace (all devices
  * and streams). Synchronises each device that held one. Safe to call at any
  * time no decode is in flight on another host thread.

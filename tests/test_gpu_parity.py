@@ -283,6 +283,32 @@ def test_poisoned_partials_do_not_leak_into_the_next_call(form):
         g.set_launch_form("auto")
 
 
+def test_workspace_limit_reports_allocation_failure(monkeypatch):
+    # A call that needs a new workspace larger than GQA_DECODE_WORKSPACE_LIMIT
+    # fails with GQA_ERR_ALLOC and enqueues nothing; without the limit the
+    # same call on the same stream then succeeds.
+    torch = _torch()
+    g = _g()
+    print("case workspace limit", flush=True)
+    w = workloads.build("ws limit", 44, 2048, [2048, 1500])
+    q, kv, lens = _device_inputs(w)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    monkeypatch.setenv("GQA_DECODE_WORKSPACE_LIMIT", "4096")
+    with torch.cuda.stream(s):
+        with pytest.raises(g.GqaDecodeError) as err:
+            g.gqa_decode(q, kv, lens, out=out)
+    assert err.value.status == -7 and "GQA_DECODE_WORKSPACE_LIMIT" in str(err.value)
+    torch.cuda.synchronize()
+    assert np.isnan(out.float().cpu().numpy()).all()          # nothing was enqueued
+    monkeypatch.delenv("GQA_DECODE_WORKSPACE_LIMIT")
+    with torch.cuda.stream(s):
+        g.gqa_decode(q, kv, lens, out=out)
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), oracle_of(w), "after the workspace limit is lifted")
+
+
 def test_errors_are_raised_on_gpu():
     torch = _torch()
     g = _g()
