@@ -79,7 +79,7 @@ def traffic_from_profiles(workload: str):
     return None
 
 
-def cpu_baseline(w, min_seconds: float):
+def cpu_baseline(w, min_seconds: float, gpu_out=None):
     import numpy as np
 
     from oracle.formats import bf16_to_f64, e4m3_to_f64, nvfp4_to_f64
@@ -106,18 +106,34 @@ def cpu_baseline(w, min_seconds: float):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     reps, t0 = 0, time.perf_counter()
+    ref = None
     while True:
-        decode_ragged(q, kval, vval, w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
+        ref = decode_ragged(q, kval, vval, w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
     gbs = w.kv_bytes_read * reps / el / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    parity = None
+    if gpu_out is not None:
+        # the benchmarked output against the oracle's, rounded once to the
+        # output type (fp16; bf16 for bf16 runs)
+        if w.elem == "bf16":
+            from oracle.formats import round_bf16
+            ref_t = bf16_to_f64(round_bf16(ref))
+        else:
+            from oracle.reference import round_fp16
+            ref_t = round_fp16(ref).astype(np.float64)
+        d = np.abs(gpu_out - ref_t)
+        parity = {"max_abs_diff": float(d.max()), "mean_abs_diff": float(d.mean()),
+                  "bar": ("within about 1 bf16 ulp of the rounded oracle" if w.elem == "bf16"
+                          else "max <= 2e-3, mean <= 2e-4")}
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"whole workload {w.name}, {reps} pass(es) in {el:.1f} s "
                       f"(float64 numpy, {threads} BLAS threads, "
                       f"{len(os.sched_getaffinity(0))} host cores visible)",
             "seconds_per_step": round(el / reps, 4)}
+    return res, parity
 
 
 def _counter_rows(d: str):
@@ -375,7 +391,14 @@ def main(argv=None):
         },
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # the last eager step's output (every KV copy holds the same values)
+        if out.dtype == torch.bfloat16:
+            from oracle.formats import bf16_to_f64
+            got = bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        else:
+            got = out.cpu().numpy().astype(np.float64)
+        line["cpu_baseline"], parity = cpu_baseline(w, args.cpu_seconds, got)
+        line["parity_vs_oracle"] = parity
     print(json.dumps(line), flush=True)
     return 0
 
