@@ -20,6 +20,13 @@ call after another sees per step), then once more with the library's
 start/stop HIP events attached to each kernel dispatch on the launch stream
 (kernel_us: the kernels' execution time, without launch gaps).
 
+Single calls, cold and warm (latency_us): before each cold sample a 1 GiB
+scratch buffer is overwritten, which evicts the L2 caches and the Infinity
+Cache, then one eager call is timed between two events on its stream
+(median, p10, p90); warm samples repeat one call on the same KV copy behind
+a short spin kernel, so the KV bytes may be cache-resident when they fit.
+Both kinds of sample wait behind GPU work, so host launch time stays out.
+
 Prints ONE JSON line:
   value       KV-read throughput: sum(L_b) * 4096 B / step time (GB/s)
   roofline    the pieces kernel's algorithmic KV bytes per launch divided
@@ -28,6 +35,8 @@ Prints ONE JSON line:
               from rocprofv3 counters when a committed summary matches the
               current kernel source, else null
   cpu_baseline  the float64 CPU oracle on the host cores, same workload
+  parity_vs_oracle  max/mean |d| of the benchmarked output against the
+              oracle's result from the CPU leg, rounded to the output type
 """
 from __future__ import annotations
 
@@ -136,6 +145,43 @@ def cpu_baseline(w, min_seconds: float, gpu_out=None):
     return res, parity
 
 
+def single_call_latency(step, dev, samples: int):
+    """Median/p10/p90 (us) of one eager call timed between two events on the
+    current stream: cold (a 1 GiB write before each call evicts the L2s and
+    the Infinity Cache) and warm (the same KV copy again). Each sample is
+    queued behind GPU work (the write, or a short spin kernel for warm
+    samples), so the host's launch time is not inside the events."""
+    import numpy as np
+    import torch
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(i, cold):
+        if cold:
+            flush.fill_(i & 0xFF)
+        else:
+            torch.cuda._sleep(200000)     # a spin kernel, tens of microseconds
+        a.record(stream)
+        step(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+    res = {}
+    for name, cold in (("cold", True), ("warm", False)):
+        timed(0, cold)                                   # untimed first call
+        t = np.array([timed(i if cold else 0, cold) for i in range(samples)])
+        res[name] = {"p10": round(float(np.percentile(t, 10)), 3),
+                     "p50": round(float(np.percentile(t, 50)), 3),
+                     "p90": round(float(np.percentile(t, 90)), 3)}
+    res["samples"] = samples
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def _counter_rows(d: str):
     import csv
     import glob
@@ -230,6 +276,8 @@ def main(argv=None):
                     help="query heads (with --kv-heads: other head counts, same lengths)")
     ap.add_argument("--kv-heads", type=int, default=8, help="KV heads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--latency-samples", type=int, default=100,
+                    help="single-call samples, cold and warm each (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (counter calibration)")
@@ -333,6 +381,10 @@ def main(argv=None):
     pieces_us = kt.pieces_ms / kt.calls * 1e3
     combine_us = kt.combine_ms / kt.calls * 1e3
 
+    latency = None
+    if args.latency_samples > 0:
+        latency = single_call_latency(step, dev, args.latency_samples)
+
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1048576
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -375,6 +427,7 @@ def main(argv=None):
             "kv_layout": (f"paged, {args.page_size} positions per page, shuffled"
                           if args.page_size > 0 else "contiguous"),
         },
+        "latency_us": latency,
         "kernel_us": {"pieces": round(pieces_us, 3), "combine": round(combine_us, 3),
                       "sum": round(pieces_us + combine_us, 3)},
         "hbm_frac_of_step": round(kv_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
