@@ -4,7 +4,8 @@ Bar (element-wise over every output, rows of empty sequences included):
 max |gpu - fp16(oracle)| <= 2e-3 and mean |gpu - fp16(oracle)| <= 2e-4,
 where fp16(oracle) is one nearest-even rounding of the float64 result.
 Exact properties of the method (length-1 rows, contents beyond a length,
-power-of-two scaling of V, fixed-split reproducibility) are checked bitwise.
+power-of-two scaling of V, fixed-split reproducibility, independence of
+batch entries and heads) are checked bitwise.
 """
 import numpy as np
 import pytest
@@ -176,6 +177,41 @@ def test_batch_entries_are_independent(chunk_len):
         one = workloads.Workload("one", w.q[b:b + 1], w.seq_lens[b:b + 1], w.capacity, w.q_scale,
                                  w.k_valid[b:b + 1], w.v_valid[b:b + 1])
         check(run(one, chunk_len=chunk_len), oracle_of(one), f"batch entry {b} alone")
+
+
+@pytest.mark.parametrize("chunk_len", [0, 300])
+def test_heads_are_independent_bitwise(chunk_len):
+    # The split depends on the lengths only, and each query head is its own
+    # MFMA column with its own softmax state: replacing the other KV heads'
+    # K/V and the other groups' q must leave a group's outputs bit-identical,
+    # and so must replacing one q head inside the group for its neighbours.
+    lens = [1500, 700, 3, 1]
+    w = workloads.build("heads indep", 41, 1500, lens)
+    full = run(w, chunk_len=chunk_len)
+    other = workloads.build("heads indep 2", 42, 1500, lens, sigma_k=3.0)
+    for g in (0, 5):
+        hs = slice(4 * g, 4 * g + 4)
+        mix_q = other.q.copy()
+        mix_q[:, hs] = w.q[:, hs]
+        mix_k, mix_v = [], []
+        for b in range(w.batch):
+            k, v = other.k_valid[b].copy(), other.v_valid[b].copy()
+            k[g], v[g] = w.k_valid[b][g], w.v_valid[b][g]
+            mix_k.append(k)
+            mix_v.append(v)
+        mixed = workloads.Workload("heads mixed", mix_q, w.seq_lens, w.capacity, w.q_scale,
+                                   mix_k, mix_v)
+        got = run(mixed, chunk_len=chunk_len)
+        assert np.array_equal(got[:, hs].view(np.uint16), full[:, hs].view(np.uint16)), g
+        # one q head of the group replaced: its three neighbours are unchanged
+        q1 = w.q.copy()
+        q1[:, 4 * g + 1] = other.q[:, 4 * g + 1]
+        one = workloads.Workload("one head", q1, w.seq_lens, w.capacity, w.q_scale,
+                                 w.k_valid, w.v_valid)
+        got1 = run(one, chunk_len=chunk_len)
+        for h in (4 * g, 4 * g + 2, 4 * g + 3):
+            assert np.array_equal(got1[:, h].view(np.uint16), full[:, h].view(np.uint16)), h
+        check(got1, oracle_of(one), f"one q head replaced, group {g}")
 
 
 def test_doubling_v_doubles_output_bitwise():
