@@ -427,6 +427,19 @@ def main(argv=None):
             "kv_layout": (f"paged, {args.page_size} positions per page, shuffled"
                           if args.page_size > 0 else "contiguous"),
         },
+        "bytes_per_step": {
+            "kv": kv_bytes,
+            "q": q.numel() * q.element_size(),
+            "out": out.numel() * out.element_size(),
+            "seq_lens": lens.numel() * lens.element_size(),
+            "algorithmic_total": kv_bytes + q.numel() * q.element_size()
+                                 + out.numel() * out.element_size()
+                                 + lens.numel() * lens.element_size(),
+            # device memory the library holds for this shape (partials,
+            # segment table), allocated once and reused
+            "workspace_allocated": (g.workspace_bytes(w.batch, w.capacity)
+                                    if default_heads else None),
+        },
         "latency_us": latency,
         "kernel_us": {"pieces": round(pieces_us, 3), "combine": round(combine_us, 3),
                       "sum": round(pieces_us + combine_us, 3)},
