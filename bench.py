@@ -4,6 +4,7 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                 [--elem f16|bf16|e4m3|nvfp4] [--page-size P] [--q-heads H --kv-heads H]
                 [--no-cpu-baseline] [--copy-calibration-mib N]
 python bench.py --summarize-pmc FETCH_DIR WRITE_DIR [--workload NAME]
+python bench.py --summarize-sq DIR [--workload NAME] [--elem E]
 
 One step = one gqa_decode call (split-KV pieces kernel + combine kernel)
 over one batch of the named synthetic workload, inputs resident in HBM.
@@ -204,6 +205,44 @@ def _per_dispatch(rows, counter, match):
     return sorted(vals.items())
 
 
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+               "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "GRBM_GUI_ACTIVE")
+
+
+def summarize_sq(d: str, workload: str, elem: str) -> str:
+    """Mean per pieces-kernel dispatch of one rocprofv3 --pmc run of the
+    SQ_COUNTERS, with utilisations normalised to the chip's cycles:
+    GRBM_GUI_ACTIVE is read as summed over the 8 XCDs, so one XCD's active
+    cycles are GRBM/8, and the chip has 1024 SIMDs and 256 CUs in them.
+    VALU busy = 4 * SQ_ACTIVE_INST_VALU (counted in 4-cycle units) / SIMD
+    cycles; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD cycles; LDS bank
+    conflicts = SQ_LDS_BANK_CONFLICT / CU cycles."""
+    rows = _counter_rows(d)
+    is_ours = lambda n: "gqa_decode_pieces" in n
+    mean = {}
+    n = 0
+    for c in SQ_COUNTERS:
+        vals = [v for _, v in _per_dispatch(rows, c, is_ours)]
+        if not vals:
+            raise SystemExit(f"{c}: no decode dispatches in {d}")
+        mean[c] = sum(vals) / len(vals)
+        n = len(vals)
+    xcd_cycles = mean["GRBM_GUI_ACTIVE"] / 8
+    simd_cycles, cu_cycles = xcd_cycles * 1024, xcd_cycles * 256
+    lines = [f"# SQ counters of gqa_decode_pieces ({elem}) on {workload}", "",
+             f"kernel_source_sha256: {kernel_source_hash()}",
+             f"dispatches: {n}", "", "Mean per dispatch:", "", "```"]
+    lines += [f"{c:26s} {mean[c]:16.1f}" for c in SQ_COUNTERS]
+    lines += ["```", "",
+              f"VALU busy: {100 * 4 * mean['SQ_ACTIVE_INST_VALU'] / simd_cycles:.1f}% of SIMD cycles",
+              f"MFMA busy: {100 * mean['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.1f}% of SIMD cycles",
+              f"LDS bank conflicts: {100 * mean['SQ_LDS_BANK_CONFLICT'] / cu_cycles:.1f}% of CU cycles",
+              f"VALU instructions per MFMA: {mean['SQ_INSTS_VALU'] / max(mean['SQ_INSTS_MFMA'], 1):.1f}",
+              ""]
+    return "\n".join(lines)
+
+
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, copy_mib: int) -> str:
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, both of
     `bench.py --copy-calibration-mib N`) into HBM bytes per pieces-kernel
@@ -282,8 +321,12 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run plain device copies of this size (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-sq", metavar="DIR")
     args = ap.parse_args(argv)
 
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq, args.workload, args.elem))
+        return 0
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc, args.workload, args.copy_calibration_mib or 256))
         return 0
