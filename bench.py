@@ -332,9 +332,9 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the decode shards by batch or KV head with no communication, "
-              "but multi-GPU runs are not part of it).", file=sys.stderr)
+              "but no multi-GPU path is implemented).", file=sys.stderr)
         return 2
 
     import numpy as np
