@@ -118,6 +118,48 @@ def test_scale_variants(q_scale):
     check(run(w, q_scale=q_scale), oracle_of(w, q_scale), f"q_scale={q_scale}")
 
 
+def test_extreme_magnitudes_stay_finite_within_the_fp32_error_bound():
+    # V near the fp16 maximum and K scaled by 40: no overflow in the fp32
+    # accumulators or the output conversion. Neither the absolute bar nor a
+    # one-ulp bar applies here. Two near-equal weights on V values of opposite
+    # sign leave an output far below the terms it sums (109 against 52000),
+    # and the fp32 scores carry an absolute error that scales with their
+    # terms' magnitude A = scale * max_i sum_d |q_d k_id| (about 360 here).
+    # A weight is then off by that error relative to itself, and an output by
+    # that much of mag = sum_i p_i |v_i| / sum_i p_i. The bound, with
+    # sixteen fp32 roundings' worth of slack on the scores (measured: under
+    # half of it): one fp16 ulp of the output plus 2^-20 (1 + A) mag, here
+    # 3.4e-4 mag; a 1% error in a weight would exceed it about 30-fold.
+    rng = np.random.default_rng(77)
+    w = workloads.build("extreme", 77, 900, [900, 17, 1])
+    k = [(kk.astype(np.float32) * 40).astype(np.float16) for kk in w.k_valid]
+    v = [(np.sign(vv.astype(np.float32)) * 65504 * rng.uniform(0.5, 1.0, vv.shape))
+         .astype(np.float16) for vv in w.v_valid]
+    big = workloads.Workload("extreme big", w.q, w.seq_lens, w.capacity, w.q_scale, k, v)
+    ref16 = round_fp16(oracle_of(big)).astype(np.float16)
+    mag = decode_ragged(w.q, k, [np.abs(x) for x in v], w.q_scale)
+    scale = w.q_scale / np.sqrt(128.0)
+    A = np.zeros(mag.shape[:2])
+    for b in range(w.batch):
+        for h in range(32):
+            A[b, h] = scale * np.max(np.abs(k[b][h // 4].astype(np.float64))
+                                     @ np.abs(w.q[b, h].astype(np.float64)))
+    # fp16 ulp of each reference value from its binade (np.spacing would
+    # step past 65504 to infinity)
+    r = np.abs(ref16.astype(np.float64))
+    _, ex = np.frexp(r)
+    ulp = np.where(r > 0, np.ldexp(1.0, np.maximum(ex - 1, -14) - 10), 2.0 ** -24)
+    bound = ulp + 2.0 ** -20 * (1.0 + A[:, :, None]) * mag
+    for chunk in (0, 64):
+        got = run(big, chunk_len=chunk).astype(np.float64)
+        assert np.all(np.isfinite(got))
+        d = np.abs(got - ref16.astype(np.float64))
+        print(f"extreme chunk {chunk}: max|d|={d.max():.3f}, max|d|/bound={np.max(d / bound):.3f}, "
+              f"max|out|={np.abs(got).max():.0f}", flush=True)
+        assert np.all(d <= bound), np.unravel_index(np.argmax(d / bound), d.shape)
+        assert np.abs(got).max() > 30000                 # the case reaches the top binade
+
+
 # ---------------------------------------------------------------- exact properties
 def test_length_one_returns_v_row_bitwise():
     w = workloads.build("len1", 35, 96, [1, 1, 1], fill="nan")
