@@ -169,8 +169,9 @@ typedef enum gqa_dtype {
  * Range: the scores and the unnormalised sums (sum_i p_i v_i with every
  * p_i <= 1, plus sum_i p_i) are fp32, so the result is finite only while
  * scale * sum_d |q_d k_d| and L * max|v| stay below the fp32 maximum
- * (3.4e38). Every fp16 and E4M3 input meets this; bfloat16 values above
- * about 1e32 may not, and then the output may be infinite or NaN.
+ * (3.4e38), where scale includes q_scale and k_scale. fp16 and E4M3 inputs
+ * meet this for any scales below about 1e25; bfloat16 values above about
+ * 1e32 may not, and then the output may be infinite or NaN.
  * chunk_len  as for gqa_decode_chunked (0 = automatic split).
  * Returns GQA_ERR_BAD_ARG for an unknown dtype or a non-finite scale.
  */
