@@ -156,14 +156,15 @@ def single_call_latency(step, dev, samples: int):
     import torch
 
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    spin = getattr(torch.cuda, "_sleep", None)    # torch's spin kernel (a private helper)
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def timed(i, cold):
         if cold:
             flush.fill_(i & 0xFF)
-        else:
-            torch.cuda._sleep(200000)     # a spin kernel, tens of microseconds
+        elif spin is not None:
+            spin(200000)                  # tens of microseconds of GPU work
         a.record(stream)
         step(i)
         b.record(stream)
@@ -178,6 +179,7 @@ def single_call_latency(step, dev, samples: int):
                      "p50": round(float(np.percentile(t, 50)), 3),
                      "p90": round(float(np.percentile(t, 90)), 3)}
     res["samples"] = samples
+    res["warm_queued_behind_spin"] = spin is not None   # else host launch time is included
     del flush
     torch.cuda.empty_cache()
     return res
