@@ -16,7 +16,7 @@ def pytest_configure(config):
 def pytest_collection_modifyitems(config, items):
     # GPU tests that are collected where no GPU is visible are skipped with a
     # reason rather than failing, so `-m "not gpu"` and plain runs stay green
-    # on build hosts; on the GPU machine they run.
+    # on hosts without a GPU; where an MI355X is visible they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
