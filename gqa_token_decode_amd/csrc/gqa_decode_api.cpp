@@ -30,6 +30,7 @@ namespace {
 constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
 constexpr int kMinPieceDefault = 128;      // cost units: two 64-row steps of a workgroup
 constexpr int kSegCostDefault = 128;       // fixed cost of a segment, in row units
+constexpr int kCombineMaxGrid = 1 << 16;   // combine workgroups, at most
 // Forced chunk lengths may not make the workspace exceed this.
 constexpr size_t kMaxForcedWorkspace = (size_t)4 << 30;
 
@@ -55,7 +56,9 @@ struct DeviceInfo {
 
 // fp32 partial results, cached per (device, stream), and the single-launch
 // form's per-segment tickets (zeroed once when allocated; every call leaves
-// them zero).
+// them zero). A buffer that a call under graph capture used may be read and
+// written by every replay of that graph, so it is never freed before
+// gqa_decode_release_workspace: when it is outgrown it moves to g_retired.
 struct Workspace {
   int device;
   hipStream_t stream;
@@ -63,6 +66,13 @@ struct Workspace {
   size_t bytes;
   int* tickets;
   size_t ticket_bytes;
+  bool ptr_captured;       // a captured call holds ptr
+  bool tickets_captured;   // a captured call holds tickets
+};
+
+struct Retired {
+  int device;
+  void* ptr;
 };
 
 struct ProfileRecord {
@@ -75,6 +85,7 @@ std::mutex g_mu;
 int g_launch_form = -1;   // -1: not yet read from the environment
 std::vector<DeviceInfo> g_devices;
 std::vector<Workspace> g_workspaces;
+std::vector<Retired> g_retired;   // outgrown buffers that captured graphs may still use
 bool g_profiling = false;
 // Event triples reused across profiling sessions; the first g_profile_used
 // belong to the current session.
@@ -128,6 +139,7 @@ gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_al
   cfg.seg_cost = up(env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20));
   cfg.forced_piece = forced_piece > 0 ? up(forced_piece) : 0;
   cfg.row_align = row_align;
+  cfg.combine_max_grid = env_int("GQA_DECODE_COMBINE_MAX_GRID", kCombineMaxGrid, 1, kCombineMaxGrid);
   return cfg;
 }
 
@@ -147,45 +159,89 @@ int pointer_device(const void* p) {
   return attr.device;
 }
 
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;   // unknown: treat as capturing (no allocation, no synchronisation)
+  }
+  return cap != hipStreamCaptureStatusNone;
+}
+
+// Drop an outgrown buffer of (dev, stream): kept until release if a captured
+// call holds it, else freed once the stream's earlier calls are done with it.
+bool drop_buffer(int dev, hipStream_t stream, void* p, bool captured) {
+  if (!p) return true;
+  if (captured) {
+    g_retired.push_back(Retired{dev, p});
+    return true;
+  }
+  const bool ok = hipStreamSynchronize(stream) == hipSuccess && hipFree(p) == hipSuccess;
+  if (!ok) (void)hipGetLastError();
+  return ok;
+}
+
+// Size to allocate when `need` bytes outgrow `have`: at least double, so that
+// buffers retired under graph capture add up to less than the live one.
+size_t grown_size(size_t have, size_t need, size_t cap) {
+  size_t n = have * 2 > need ? have * 2 : need;
+  if (cap > 0 && n > cap) n = need;
+  return (n + 255) & ~(size_t)255;
+}
+
+size_t workspace_cap() {
+  const char* e = getenv("GQA_DECODE_WORKSPACE_LIMIT");
+  return e ? (size_t)strtoull(e, nullptr, 10) : 0;
+}
+
 // Workspace of at least `bytes` for (dev, stream). Caller holds g_mu and
-// has made `dev` current. Sets *status on error.
+// has made `dev` current. Sets *status on error. Growing is refused under
+// graph capture (no allocation or synchronisation may be captured).
 void* get_workspace(int dev, hipStream_t stream, size_t bytes, int* status) {
   Workspace* ws = nullptr;
   for (Workspace& w : g_workspaces)
     if (w.device == dev && w.stream == stream) ws = &w;
-  if (ws && ws->bytes >= bytes) return ws->ptr;
+  const bool capturing = stream_capturing(stream);
+  if (ws && ws->bytes >= bytes) {
+    ws->ptr_captured = ws->ptr_captured || capturing;
+    return ws->ptr;
+  }
   // Optional cap on the library's device memory (bytes; unset or 0: none).
-  if (const char* e = getenv("GQA_DECODE_WORKSPACE_LIMIT")) {
-    const unsigned long long cap = strtoull(e, nullptr, 10);
-    if (cap > 0 && bytes > cap) {
-      *status = fail(GQA_ERR_ALLOC,
-                     "gqa_decode: a workspace of %zu bytes exceeds GQA_DECODE_WORKSPACE_LIMIT=%llu",
-                     bytes, cap);
-      return nullptr;
-    }
+  const size_t cap = workspace_cap();
+  if (cap > 0 && bytes > cap) {
+    *status = fail(GQA_ERR_ALLOC,
+                   "gqa_decode: a workspace of %zu bytes exceeds GQA_DECODE_WORKSPACE_LIMIT=%zu",
+                   bytes, cap);
+    return nullptr;
+  }
+  if (capturing) {
+    *status = fail(GQA_ERR_ALLOC,
+                   "gqa_decode: this call needs a larger workspace on its stream; make a call "
+                   "of this size (or larger) on the stream outside graph capture first");
+    return nullptr;
   }
   if (!ws) {
-    g_workspaces.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0});
+    g_workspaces.push_back(Workspace{dev, stream, nullptr, 0, nullptr, 0, false, false});
     ws = &g_workspaces.back();
   }
+  const size_t n = grown_size(ws->bytes, bytes, cap);
   if (ws->ptr) {
-    // Earlier calls on this stream may still use the old buffer.
-    const bool ok = hipStreamSynchronize(stream) == hipSuccess && hipFree(ws->ptr) == hipSuccess;
+    const bool ok = drop_buffer(dev, stream, ws->ptr, ws->ptr_captured);
     ws->ptr = nullptr;
     ws->bytes = 0;
+    ws->ptr_captured = false;
     if (!ok) {
-      (void)hipGetLastError();
       *status = fail(GQA_ERR_LAUNCH, "gqa_decode: could not release the old workspace");
       return nullptr;
     }
   }
-  if (hipMalloc(&ws->ptr, bytes) != hipSuccess) {
+  if (hipMalloc(&ws->ptr, n) != hipSuccess) {
     (void)hipGetLastError();
     ws->ptr = nullptr;
-    *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu workspace bytes failed", bytes);
+    *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu workspace bytes failed", n);
     return nullptr;
   }
-  ws->bytes = bytes;
+  ws->bytes = n;
   return ws->ptr;
 }
 
@@ -198,40 +254,42 @@ int* get_tickets(int dev, hipStream_t stream, size_t count, int* status) {
   for (Workspace& w : g_workspaces)
     if (w.device == dev && w.stream == stream) ws = &w;
   const size_t bytes = (count * sizeof(int) + 255) & ~(size_t)255;
-  if (ws && ws->ticket_bytes >= bytes) return ws->tickets;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (!ws || hipStreamIsCapturing(stream, &cap) != hipSuccess ||
-      cap != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();
+  const bool capturing = stream_capturing(stream);
+  if (ws && ws->ticket_bytes >= bytes) {
+    ws->tickets_captured = ws->tickets_captured || capturing;
+    return ws->tickets;
+  }
+  if (!ws || capturing) {
     *status = fail(GQA_ERR_ALLOC,
                    "gqa_decode: the first call with this batch size on a stream must run "
                    "outside graph capture");
     return nullptr;
   }
+  const size_t n = grown_size(ws->ticket_bytes, bytes, 0);
   if (ws->tickets) {
-    const bool ok = hipStreamSynchronize(stream) == hipSuccess && hipFree(ws->tickets) == hipSuccess;
+    const bool ok = drop_buffer(dev, stream, ws->tickets, ws->tickets_captured);
     ws->tickets = nullptr;
     ws->ticket_bytes = 0;
+    ws->tickets_captured = false;
     if (!ok) {
-      (void)hipGetLastError();
       *status = fail(GQA_ERR_LAUNCH, "gqa_decode: could not release the old ticket array");
       return nullptr;
     }
   }
   void* p = nullptr;
-  if (hipMalloc(&p, bytes) != hipSuccess) {
+  if (hipMalloc(&p, n) != hipSuccess) {
     (void)hipGetLastError();
-    *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu ticket bytes failed", bytes);
+    *status = fail(GQA_ERR_ALLOC, "gqa_decode: hipMalloc of %zu ticket bytes failed", n);
     return nullptr;
   }
-  if (hipMemsetAsync(p, 0, bytes, stream) != hipSuccess) {
+  if (hipMemsetAsync(p, 0, n, stream) != hipSuccess) {
     (void)hipGetLastError();
     (void)hipFree(p);
     *status = fail(GQA_ERR_LAUNCH, "gqa_decode: clearing the ticket array failed");
     return nullptr;
   }
   ws->tickets = static_cast<int*>(p);
-  ws->ticket_bytes = bytes;
+  ws->ticket_bytes = n;
   return ws->tickets;
 }
 
@@ -468,8 +526,9 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
           grid > 0 ? gqa::segment_bytes_for_batch(batch, Hkv) +
                          gqa::partial_bytes_for_grid(grid, group)
                    : 0;
-      if (grid <= 0 || grid > 0x7fffffffLL) {
-        st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs more than 2^31 workgroups");
+      if (grid <= 0 || grid >= (1LL << 24)) {
+        // a dispatch holds below 2^32 work items: 2^24 workgroups of 256
+        st = fail(GQA_ERR_BAD_ARG, "gqa_decode: the split needs 2^24 or more workgroups");
       } else if (chunk_len > 0 && pbytes > kMaxForcedWorkspace) {
         st = fail(GQA_ERR_BAD_ARG,
                   "gqa_decode: chunk_len %d is too small for batch %d and capacity %d "
@@ -587,11 +646,18 @@ void gqa_decode_release_workspace(void) {
   for (Workspace& w : g_workspaces) {
     if (hipSetDevice(w.device) == hipSuccess) {
       (void)hipDeviceSynchronize();
-      (void)hipFree(w.ptr);
+      if (w.ptr) (void)hipFree(w.ptr);
       if (w.tickets) (void)hipFree(w.tickets);
     }
   }
+  for (Retired& r : g_retired) {
+    if (hipSetDevice(r.device) == hipSuccess) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(r.ptr);
+    }
+  }
   g_workspaces.clear();
+  g_retired.clear();
   if (prev >= 0) (void)hipSetDevice(prev);
   (void)hipGetLastError();
 }

@@ -46,7 +46,9 @@
 //   16 db + 4 G4 .. +3, so each lane rescales its accumulators by its own
 //   head's factor. Weights are split into fp16 high and low parts (two MFMAs)
 //   so the sum keeps fp32-level accuracy; the denominator sums the fp32
-//   weights.
+//   weights. fp16 weights are formed up to 2^15 instead of 1 (a reference
+//   15 below the running maximum), so that their low parts stay normal fp16
+//   numbers; the factor cancels between numerator and denominator.
 //   LDS reads of a stage are issued from asm blocks with their own waits: the
 //   compiler cannot tell the two stages apart and would otherwise wait for the
 //   next tile's loads, which are in flight by design.
@@ -586,7 +588,8 @@ __device__ __forceinline__ unsigned lds_addr(const e16_t* p) {
 struct WaveAcc {
   float4_t O[8];     // O^T accumulators (D layout): lane (G4, j), reg r = head j,
                      // output column 16 db + 4 G4 + r
-  float m;           // running max of head j (same in the 4 lane groups)
+  float m;           // head j's weight reference (weight_ref: the running max,
+                     // or 15 below it for fp16 weights; same in the 4 lane groups)
   float l;           // this lane group's share of head j's denominator
 };
 
@@ -765,6 +768,24 @@ __device__ __forceinline__ half8_t e4m3x8_to_f16(uint2 x) {
   return (half8_t){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// Reference point of a tile's softmax weights (base 2): the weights are
+// exp2(s - ref). The wave state, the wave merge and the partials carry this
+// reference in place of the running maximum; any reference gives the same
+// normalised result, since numerator and denominator share the factor
+// exp2(max - ref). kBias (fp16 weight pairs): ref lies 15 below the running
+// maximum, so weights reach 2^15 and their fp16 low parts stay normal down
+// to 2^-18 of the largest (see split_weight). The bias is taken only while
+// |mx| < 2^20, where the fp32 rounding of mx - 15 is at most 2^-4, so no
+// weight exceeds 2^15.07 < 65504 (the fp16 maximum); beyond that the score
+// magnitudes already carry fp32 rounding errors far above the split's.
+// The reference never decreases (fmaxf), so rescale factors stay <= 1.
+template <bool kBias>
+__device__ __forceinline__ float weight_ref(float ref_old, float mx) {
+  if constexpr (!kBias) return fmaxf(ref_old, mx);
+  const float bias = __builtin_fabsf(mx) < 1048576.0f ? 15.0f : 0.0f;
+  return fmaxf(ref_old, mx - bias);
+}
+
 // Element-type specific steps: MFMAs on fp16 or bf16 operands (raw 16-bit
 // patterns in registers), the two-part rounding of the softmax weights, and
 // the round-to-nearest-even output conversion.
@@ -788,7 +809,14 @@ __device__ __forceinline__ float4_t mfma_pv(short4_t a, short4_t b, float4_t c) 
 }
 
 // p = hi + lo with hi = p rounded to the element type and lo = the rest,
-// rounded again: the pair carries 22 (fp16) or 16 (bf16) significant bits.
+// rounded again. bf16 (8 exponent bits): the pair carries 16 significant
+// bits for any weight. fp16: hi carries 11 bits and lo 11 more while lo is a
+// normal fp16 number, i.e. for p >= 2^-3; below that lo lies in fp16's
+// subnormal range, whose fixed spacing 2^-24 bounds the pair's absolute
+// error by 2^-25. fp16 weights are therefore formed up to 2^15 rather than
+// up to 1 (weight_ref): the pair then has 22 bits for weights down to 2^-18
+// of the largest, and an absolute error of at most 2^-40 of the largest
+// below that.
 template <bool kBf16>
 __device__ __forceinline__ void split_weight(float p, short& hi, short& lo) {
   if constexpr (kBf16) {
@@ -913,8 +941,8 @@ __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
   for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = max_over_row_groups(mx);
   // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
-  // tile, where acc.m is still -inf.
-  const float m_new = fmaxf(acc.m, mx);
+  // tile, where acc.m is still -inf. acc.m holds the weights' reference.
+  const float m_new = weight_ref<true>(acc.m, mx);
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
@@ -1005,8 +1033,8 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = max_over_row_groups(mx);
   // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
-  // tile, where acc.m is still -inf.
-  const float m_new = fmaxf(acc.m, mx);
+  // tile, where acc.m is still -inf. acc.m holds the weights' reference.
+  const float m_new = weight_ref<true>(acc.m, mx);
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
@@ -1073,8 +1101,8 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[r]);
   mx = max_over_row_groups(mx);
   // Row t is below hi, so mx (and m_new) is finite; alpha is 0 on the first
-  // tile, where acc.m is still -inf.
-  const float m_new = fmaxf(acc.m, mx);
+  // tile, where acc.m is still -inf. acc.m holds the weights' reference.
+  const float m_new = weight_ref<!kBf16>(acc.m, mx);
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
@@ -1636,32 +1664,42 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
 }
 
 // ---------------------------------------------------------------- kernel 2
-// Two-launch form: one workgroup per segment (b, g), or per (segment, query
+// Two-launch form: one work unit per segment (b, g), or per (segment, query
 // head) when segments are few (P.combine_per_head); if kernel 1 cut the
-// segment into several pieces, merge their partials, else exit. Per segment
-// for many segments: G x fewer waves to dispatch, and most exit at once.
-// Per head for few segments: G x more subsets share a segment's partials,
-// so each thread folds G x fewer of them in sequence.
+// segment into several pieces, merge their partials, else skip it. Per
+// segment for many segments: G x fewer waves to dispatch, and most skip at
+// once. Per head for few segments: G x more subsets share a segment's
+// partials, so each thread folds G x fewer of them in sequence.
+// Workgroup w takes units w, w + grid, ... (the grid is capped at
+// kCombineMaxGrid workgroups, so any batch stays within one dispatch's
+// 32-bit work-item count).
 // The leading arguments repeat fields of P (preloaded, as for kernel 1).
 template <int F, bool kG4>
 __global__ __launch_bounds__(kThreads) void gqa_decode_combine(const int2* seg_desc, int per_head,
                                                                int group_arg, Params P) {
   __shared__ __attribute__((aligned(16))) CombineLds lds;
   const int group = kG4 ? 4 : group_arg;
-  const int seg = per_head ? blockIdx.x / group : blockIdx.x;
-  // A vector load (the index is hidden in a vector register): it is issued
-  // at once, without waiting for the scalar loads of the other arguments.
-  int vseg = seg;
-  asm volatile("" : "+v"(vseg));
-  const int2 desc = seg_desc[vseg];
-  const int b = seg / P.kv_heads, g = seg - b * P.kv_heads;
-  const int n = desc.y >> 1;
-  if (n <= 1) return;                  // empty (zero rows) or finished by kernel 1
-  if (per_head)
-    combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1,
-                                               blockIdx.x - seg * group, 1, lds);
-  else
-    combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1, 0, group, lds);
+  const long long units = (long long)P.batch * P.kv_heads * (per_head ? group : 1);
+  bool merged = false;
+  for (long long u = blockIdx.x; u < units; u += gridDim.x) {
+    const int seg = (int)(per_head ? u / group : u);
+    // A vector load (the index is hidden in a vector register): it is
+    // issued at once, without waiting for the scalar loads of the other
+    // arguments.
+    int vseg = seg;
+    asm volatile("" : "+v"(vseg));
+    const int2 desc = seg_desc[vseg];
+    const int b = seg / P.kv_heads, g = seg - b * P.kv_heads;
+    const int n = desc.y >> 1;
+    if (n <= 1) continue;              // empty (zero rows) or finished by kernel 1
+    if (merged) __syncthreads();       // the previous merge's LDS reads are done
+    merged = true;
+    if (per_head)
+      combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1,
+                                                 (int)(u - (long long)seg * group), 1, lds);
+    else
+      combine_segment<F == kFmtBf16, false, kG4>(P, b, g, desc.x, n, desc.y & 1, 0, group, lds);
+  }
 }
 
 }  // namespace
@@ -1714,14 +1752,14 @@ size_t segment_bytes_for_batch(int batch, int kv_heads) {
 }
 
 template <int F, bool kPaged, bool kG4>
-hipError_t launch_kernels(const Params& P, long long grid, int batch, hipStream_t stream,
-                          hipEvent_t* events) {
+hipError_t launch_kernels(const Params& P, long long grid, int batch, long long combine_cap,
+                          hipStream_t stream, hipEvent_t* events) {
   // The combine only depends on the output type: fp16 for every format but bf16.
   constexpr int kCombineF = F == kFmtBf16 ? kFmtBf16 : kFmtF16;
   hipError_t err = hipSuccess;
+  const long long units = (long long)batch * P.kv_heads * (P.combine_per_head ? P.group : 1);
   const dim3 pieces_grid((unsigned)grid),
-      combine_grid((unsigned)(batch * P.kv_heads * (P.combine_per_head ? P.group : 1))),
-      block(kThreads);
+      combine_grid((unsigned)(units < combine_cap ? units : combine_cap)), block(kThreads);
   if (events) {
     // Start/stop events attached to the dispatches: they time each kernel's
     // execution without extra packets between the kernels.
@@ -1807,10 +1845,10 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   const bool paged = layout.block_table != nullptr;
   const bool g4 = group == 4;
 #define GQA_LAUNCH(F)                                                              \
-  (paged ? (g4 ? launch_kernels<F, true, true>(P, grid, batch, stream, events)      \
-               : launch_kernels<F, true, false>(P, grid, batch, stream, events))    \
-         : (g4 ? launch_kernels<F, false, true>(P, grid, batch, stream, events)     \
-               : launch_kernels<F, false, false>(P, grid, batch, stream, events)))
+  (paged ? (g4 ? launch_kernels<F, true, true>(P, grid, batch, cfg.combine_max_grid, stream, events)      \
+               : launch_kernels<F, true, false>(P, grid, batch, cfg.combine_max_grid, stream, events))    \
+         : (g4 ? launch_kernels<F, false, true>(P, grid, batch, cfg.combine_max_grid, stream, events)     \
+               : launch_kernels<F, false, false>(P, grid, batch, cfg.combine_max_grid, stream, events)))
   switch (elem) {
     case ElemType::kBf16:
       return GQA_LAUNCH(kFmtBf16);

@@ -34,6 +34,7 @@ struct SplitConfig {
   int forced_piece;   // > 0: fixed piece length; the grid then covers batch*capacity rows
   int seg_cost;       // automatic split: fixed cost units per (sequence, KV head) segment
   int row_align;      // 1, or 16 for paged caches (pieces and segments 16-row aligned)
+  int combine_max_grid;   // combine kernel: workgroups at most (each takes segments in turns)
 };
 
 // Workgroups of the pieces kernel that fit on one CU at once (the fewest

@@ -7,8 +7,8 @@
  *   - section 1 (docstring): q is a contiguous FP16 [batch, 32, 128] tensor,
  *     kv is a contiguous FP16 stacked cache [batch, 2, 8, capacity, 128],
  *     sequence lengths are a contiguous device int32 [batch] tensor, the
- *     output has q's shape and is owned by the caller, and q_scale is an
- *     extra query scale applied before the standard 1/sqrt(128);
+ *     output has q's shape and is owned by the caller, and the scores are
+ *     multiplied by q_scale as well as by 1/sqrt(128);
  *   - section 2: 32 query heads, 8 KV heads, head dim 128, 4:1 grouping;
  *   - section 3 (benchmark): the result equals PyTorch SDPA with a boolean
  *     length mask, scale 1/sqrt(128) and enable_gqa=True.
@@ -107,12 +107,18 @@ typedef enum gqa_status {
  * across workgroups, and for the single launch an int array of 8 * batch
  * tickets, zeroed when allocated and left zero by every call. Both are
  * allocated on first need, so the first call on a new stream, or one needing
- * a larger workspace or batch, must not be under graph capture; later calls
- * allocate nothing and can be captured. Calls on one stream are ordered by
- * the stream; calls on different streams use different workspaces. A call
- * captured into a graph keeps the workspace of the stream it was captured
- * on: replays must not overlap other calls on that stream (or other replays
- * of graphs captured on it).
+ * a larger workspace or batch, must not be under graph capture (such a call
+ * returns GQA_ERR_ALLOC with nothing enqueued); later calls allocate nothing
+ * and can be captured. Calls on one stream are ordered by the stream; calls
+ * on different streams use different workspaces.
+ * Graphs: a call captured into a graph keeps the workspace and tickets of
+ * the stream it was captured on. A later, larger eager call on that stream
+ * gets new buffers and leaves those in place (they are freed only by
+ * gqa_decode_release_workspace), so the graph stays valid; replays must not
+ * overlap calls that use the same buffers (other replays of graphs captured
+ * on that stream, or eager calls on it of a size the captured buffers
+ * serve). gqa_decode_release_workspace invalidates every graph captured
+ * before it.
  *
  * Returns GQA_OK, or a negative gqa_status with nothing enqueued.
  */
@@ -311,14 +317,22 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity);
  * Environment: GQA_DECODE_WORKSPACE_LIMIT=<bytes> caps the workspace the
  * library allocates; a call that would need a larger one on its (device,
  * stream) fails with GQA_ERR_ALLOC and enqueues nothing (workspaces already
- * large enough are reused). GQA_DECODE_LAUNCH_FORM sets the initial launch
- * form (see gqa_decode_set_launch_form).
+ * large enough are reused). A workspace that grows is allocated at twice
+ * its previous size or more (below the limit, if one is set).
+ * GQA_DECODE_LAUNCH_FORM sets the initial launch form (see
+ * gqa_decode_set_launch_form). GQA_DECODE_COMBINE_MAX_GRID=<n> (1 .. 65536,
+ * default 65536) caps the workgroups of the combine kernel, which then
+ * take the segments in turns; results do not depend on it (used to test
+ * those turns at small sizes).
  */
 
 /*
- * gqa_decode_release_workspace -- free every cached workspace (all devices
- * and streams). Synchronises each device that held one. Safe to call at any
- * time no decode is in flight on another host thread.
+ * gqa_decode_release_workspace -- free every cached workspace and ticket
+ * array (all devices and streams), including buffers kept alive for graphs
+ * captured earlier: every graph that captured a decode call before this
+ * call must not be replayed afterwards. Synchronises each device that held
+ * one. Safe to call at any time no decode is in flight on another host
+ * thread.
  */
 void gqa_decode_release_workspace(void);
 

@@ -7,8 +7,8 @@ path (no kernels, headers, helpers, tables or pre/post-processing).
 
 What it computes is the plain definition of the decode fixed by the
 FlashInfer PR #5052 analysis page ("SM110 FP16 GQA decode"): the
-``sm110_gqa_decode`` docstring in section 1 (shapes, q_scale applied before
-the standard 1/sqrt(128)), the 32/8/128 specialisation with 4:1 grouping in
+``sm110_gqa_decode`` docstring in section 1 (shapes, and q_scale as an extra
+factor on the scores beside 1/sqrt(128)), the 32/8/128 specialisation with 4:1 grouping in
 section 2, and the benchmark's PyTorch SDPA comparator in section 3
 (boolean length mask, scale 1/sqrt(128), ``enable_gqa=True``).
 

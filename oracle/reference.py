@@ -3,8 +3,8 @@
 Source: FlashInfer PR #5052 analysis page ("SM110 FP16 GQA decode").
   * Section 1, the ``sm110_gqa_decode`` docstring: q is ``[batch, 32, 128]``,
     the stacked cache ``kv`` is ``[batch, 2, 8, capacity, 128]``, lengths are
-    int32 ``[batch]``, and ``q_scale`` is applied before the standard
-    ``1/sqrt(128)`` attention scale.
+    int32 ``[batch]``, and the scores are multiplied by ``q_scale`` on top of
+    the usual ``1/sqrt(128)``.
   * Section 2: fixed 32 query heads, 8 KV heads, head dim 128 (4:1 grouping).
   * Section 3: the PyTorch SDPA comparator -- a boolean mask over the
     capacity axis, ``scale = 1/sqrt(128)`` and ``enable_gqa=True``.

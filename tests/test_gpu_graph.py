@@ -103,3 +103,85 @@ def test_two_streams_decode_concurrently():
     for oa, ob in zip(outs_a, outs_b):
         assert np.array_equal(_bits(oa), ref_a)
         assert np.array_equal(_bits(ob), ref_b)
+
+
+@pytest.mark.parametrize("form", ["two", "single"])
+def test_graph_survives_workspace_growth_on_its_stream(form):
+    # A graph captured on stream s holds s's workspace (and, in the single
+    # launch, its ticket array). A later, larger eager call on s needs
+    # bigger buffers: the library must leave the captured ones allocated, so
+    # replays still write where the graph expects, and must not hand them to
+    # anyone else (torch allocations made meanwhile are filled with NaN to
+    # catch such reuse).
+    torch = _torch()
+    g = _g()
+    g.set_launch_form(form)
+    try:
+        small = workloads.build(f"grow small {form}", 120, 256, [256, 37, 200])
+        big = workloads.build(f"grow big {form}", 121, 256,
+                              lambda r: r.integers(1, 256, 200, endpoint=True))
+        qs, kvs = small.q_to_device(DEV), small.kv_to_device(DEV)
+        ls = torch.from_numpy(small.seq_lens).to(DEV)
+        qb, kvb = big.q_to_device(DEV), big.kv_to_device(DEV)
+        lb = torch.from_numpy(big.seq_lens).to(DEV)
+        out_s = torch.empty_like(qs)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            # a fresh stream: its first call sizes the buffers for the small batch
+            g.gqa_decode(qs, kvs, ls, out=out_s, q_scale=small.q_scale)
+        s.synchronize()
+        eager_small = _bits(out_s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                g.gqa_decode(qs, kvs, ls, out=out_s, q_scale=small.q_scale)
+        torch.cuda.synchronize()
+        # a larger batch on the same stream: new, larger buffers
+        with torch.cuda.stream(s):
+            out_b = g.gqa_decode(qb, kvb, lb, q_scale=big.q_scale)
+        s.synchronize()
+        eager_big = _bits(out_b)
+        junk = [torch.full((n,), float("nan"), device=DEV) for n in (1 << 12, 1 << 16, 1 << 20)]
+        for rep in range(3):
+            out_s.fill_(float("nan"))
+            with torch.cuda.stream(s):
+                graph.replay()
+                out_b2 = g.gqa_decode(qb, kvb, lb, q_scale=big.q_scale)
+            s.synchronize()
+            assert np.array_equal(_bits(out_s), eager_small), f"{form}: replay {rep}"
+            assert np.array_equal(_bits(out_b2), eager_big), f"{form}: eager after replay {rep}"
+        del junk
+    finally:
+        g.set_launch_form("auto")
+
+
+def test_growth_under_capture_is_refused_with_nothing_enqueued():
+    # A call under capture that needs a larger workspace than its stream has
+    # fails with GQA_ERR_ALLOC before enqueuing anything; the stream's
+    # buffers stay usable for calls of the size they serve.
+    torch = _torch()
+    g = _g()
+    small = workloads.build("capture small", 122, 1024, [1024, 3])
+    big = workloads.build("capture big", 123, 1024,
+                          lambda r: r.integers(1, 1024, 300, endpoint=True))
+    qs, kvs, ls = small.q_to_device(DEV), small.kv_to_device(DEV), torch.from_numpy(small.seq_lens).to(DEV)
+    qb, kvb, lb = big.q_to_device(DEV), big.kv_to_device(DEV), torch.from_numpy(big.seq_lens).to(DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ref = g.gqa_decode(qs, kvs, ls, q_scale=small.q_scale)
+    s.synchronize()
+    ref_bits = _bits(ref)
+    out_b = torch.empty_like(qb)
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(g.GqaDecodeError) as err:
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                g.gqa_decode(qb, kvb, lb, out=out_b, q_scale=big.q_scale)
+    assert err.value.status == -7, str(err.value)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        again = g.gqa_decode(qs, kvs, ls, q_scale=small.q_scale)
+    s.synchronize()
+    assert np.array_equal(_bits(again), ref_bits)

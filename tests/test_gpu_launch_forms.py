@@ -170,3 +170,30 @@ def test_single_launch_in_a_graph_with_lengths_changed_on_the_device():
     ref = g.gqa_decode(q, kv, torch.tensor(new_lens, dtype=torch.int32, device=DEV))
     torch.cuda.synchronize()
     assert np.array_equal(_bits(out), _bits(ref))
+
+
+@pytest.mark.parametrize("cap", ["1", "3", "7"])
+@pytest.mark.parametrize("spec", [
+    # many segments, each cut into a few pieces: one combine unit per segment
+    ("batch 40", 125, 8192, lambda r: r.integers(1, 8192, 40, endpoint=True)),
+    # few long segments: one combine unit per (segment, query head)
+    ("two long", 126, 65536, [65536, 40000]),
+])
+def test_combine_workgroups_taking_units_in_turns_match_bitwise(monkeypatch, cap, spec):
+    # The combine kernel's grid is capped (at most 65536 workgroups; any
+    # batch then stays within one dispatch); each workgroup takes units
+    # w, w + grid, ... A tiny cap makes every workgroup take many units in
+    # turn, with the barrier between turns.
+    torch = _torch()
+    g = _g()
+    name, seed, cap_rows, lens = spec
+    w = workloads.build(f"turns {name}", seed, cap_rows, lens, fill="nan")
+    q, kv, ln = w.q_to_device(DEV), w.kv_to_device(DEV), torch.from_numpy(w.seq_lens).to(DEV)
+    g.set_launch_form("two")
+    ref = _bits(g.gqa_decode(q, kv, ln, q_scale=w.q_scale))
+    torch.cuda.synchronize()
+    monkeypatch.setenv("GQA_DECODE_COMBINE_MAX_GRID", cap)
+    out = torch.full_like(q, float("nan"))
+    g.gqa_decode(q, kv, ln, out=out, q_scale=w.q_scale)
+    torch.cuda.synchronize()
+    _assert_same(ref, _bits(out), f"{name}, combine grid {cap}")

@@ -1,0 +1,147 @@
+"""Softmax-weight precision of the MFMA paths on attention-sink inputs.
+
+The fp16, E4M3 and FP4 kernels split every softmax weight into two fp16
+parts for the PV matrix product. A weight far below its wave's running
+maximum would lose its low part to fp16's subnormal range (a fixed spacing of
+2^-24) if weights were formed up to 1; the kernels therefore form them up to
+2^15 (a reference 15 below the running maximum, cancelling in every ratio).
+These inputs put a dominant ("sink") key, some 17 nats above the others, in
+every wave's first tile (rows 0, 16, 32, 48), either once or every 128 rows,
+over a long run of small weights whose V rows are large (c up to 10^4), with
+V = 0 on the sinks: the output is c times the small share of the non-sink
+rows, so any error in those weights shows as a relative error of the output.
+
+Bar: the page's absolute bar (max |d| <= 2e-3, mean <= 2e-4) and, element by
+element, |gpu - fp16(oracle)| <= 2^-10 |fp16(oracle)| + 2^-24 (one fp16
+rounding of a result that is accurate to far better than 2^-11, relative;
+2^-24 is fp16's subnormal spacing, for outputs below 2^-14).
+
+The CPU test at the end checks that these inputs do expose the split's floor:
+a model of the per-wave weights split into fp16 parts without the 2^15
+factor misses the relative bar, with it meets it.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle.reference import decode_ragged, round_fp16
+import workloads
+
+DEV = "cuda:0"
+MAX_TOL, MEAN_TOL = 2e-3, 2e-4
+REL_TOL, ABS_FLOOR = 2.0 ** -10, 2.0 ** -24
+
+# (lengths, sink period): the sinks once in the first 64 rows, or every 128
+PATTERNS = {"first": ([4096], 0), "periodic": ([4096, 3001], 128)}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _g():
+    import gqa_token_decode_amd as g
+    return g
+
+
+def _widen(w):
+    """K and V per (b, g) as the values they stand for (before the scales)."""
+    if w.elem == "f16":
+        return w.k_valid, w.v_valid
+    from oracle.formats import e4m3_to_f64, nvfp4_to_f64
+    if w.elem == "e4m3":
+        return ([e4m3_to_f64(k) for k in w.k_valid], [e4m3_to_f64(v) for v in w.v_valid])
+    return ([nvfp4_to_f64(k, s) for k, s in zip(w.k_valid, w.k_scales)],
+            [nvfp4_to_f64(v, s) for v, s in zip(w.v_valid, w.v_scales)])
+
+
+def _run(w, chunk_len):
+    torch = _torch()
+    g = _g()
+    q = w.q_to_device(DEV)
+    lens = torch.from_numpy(w.seq_lens).to(DEV)
+    kv = w.kv_to_device(DEV)
+    if w.elem == "nvfp4":
+        out = g.gqa_decode_fp4(q, kv, w.scales_to_device(DEV), lens, q_scale=w.q_scale,
+                               k_scale=w.k_scale, v_scale=w.v_scale, chunk_len=chunk_len)
+    else:
+        out = g.gqa_decode(q, kv, lens, q_scale=w.q_scale, k_scale=w.k_scale,
+                           v_scale=w.v_scale, chunk_len=chunk_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _check(got, ref64, label):
+    ref16 = round_fp16(ref64).astype(np.float64)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    d = np.abs(got - ref16)
+    excess = d - (REL_TOL * np.abs(ref16) + ABS_FLOOR)
+    rel = d / np.maximum(np.abs(ref16), 2.0 ** -14)
+    print(f"{label}: max|d|={d.max():.3e} mean|d|={d.mean():.3e} max rel={rel.max():.3e} "
+          f"|out| in [{np.abs(ref16).min():.3e}, {np.abs(ref16).max():.3e}]", flush=True)
+    assert d.max() <= MAX_TOL, f"{label}: max |d| {d.max():.3e}"
+    assert d.mean() <= MEAN_TOL, f"{label}: mean |d| {d.mean():.3e}"
+    i = np.unravel_index(excess.argmax(), d.shape)
+    assert excess.max() <= 0, (f"{label}: |d| {d[i]:.3e} exceeds 2^-10 |ref| + 2^-24 at {i} "
+                               f"(ref {ref16[i]:.6e}, gpu {got[i]:.6e})")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", [1.0, 100.0, 1000.0, 10000.0])
+@pytest.mark.parametrize("chunk", ["whole", "auto"])
+@pytest.mark.parametrize("pattern", sorted(PATTERNS))
+@pytest.mark.parametrize("elem", ["f16", "e4m3", "nvfp4"])
+def test_sink_keys_over_long_small_weight_runs(elem, pattern, chunk, c):
+    if elem != "f16" and c > 1000.0:
+        pytest.skip("the 1-byte caches carry c in v_scale; 1000 already covers them")
+    lens, period = PATTERNS[pattern]
+    label = f"sink {elem} {pattern} chunk={chunk} c={c:g}"
+    print(f"case {label}", flush=True)
+    w = workloads.build_sink(f"sink-{pattern}", 77, 4096, lens, sink_period=period, c=c,
+                             elem=elem)
+    chunk_len = max(lens) if chunk == "whole" else 0
+    k, v = _widen(w)
+    ref = decode_ragged(w.q, k, v, w.q_scale, k_scale=w.k_scale, v_scale=w.v_scale)
+    _check(_run(w, chunk_len), ref, label)
+
+
+# ------------------------------------------------------------------ CPU
+def _model_out(w, bias):
+    """Output of one KV group (head 0 of each group) as the fp16 kernel forms
+    it for the "first" pattern in one piece: wave v takes rows 16 v + 64 k;
+    each wave's weights are taken against its own maximum score (base 2)
+    minus `bias`, rounded to an fp16 pair (hi, lo); numerators sum the pairs
+    times V, denominators the unrounded weights; waves merge by their
+    maxima. Everything else in float64."""
+    scale = w.q_scale / math.sqrt(128.0) * math.log2(math.e)
+    K = w.k_valid[0].astype(np.float64)
+    V = w.v_valid[0].astype(np.float64)
+    L = K.shape[1]
+    outs = []
+    for g in range(K.shape[0]):
+        t = (K[g] @ w.q[0, 4 * g].astype(np.float64)) * scale
+        waves = [np.concatenate([np.arange(r, min(r + 16, L)) for r in range(16 * v, L, 64)])
+                 for v in range(4)]
+        m = [t[rows].max() - bias for rows in waves]
+        M = max(m)
+        num = np.zeros(V.shape[2])
+        den = 0.0
+        for rows, mv in zip(waves, m):
+            p = np.exp2(t[rows] - mv)
+            hi = p.astype(np.float16).astype(np.float64)
+            lo = (p - hi).astype(np.float16).astype(np.float64)
+            f = 2.0 ** (mv - M)
+            num += f * ((hi + lo) @ V[g, rows])
+            den += f * p.sum()
+        outs.append(num / den)
+    return np.array(outs)
+
+
+def test_sink_inputs_expose_the_fp16_split_floor():
+    w = workloads.build_sink("sink-first", 77, 4096, [4096], sink_period=0, c=1000.0)
+    ref = decode_ragged(w.q, w.k_valid, w.v_valid, w.q_scale)[0, ::4]   # head 0 of each group
+    rel = {bias: np.max(np.abs(_model_out(w, bias) - ref) / np.abs(ref)) for bias in (0.0, 15.0)}
+    assert rel[0.0] > 2 ** -6, rel          # weights up to 1: the low parts go subnormal
+    assert rel[15.0] < 2 ** -14, rel        # weights up to 2^15: both parts stay normal

@@ -324,6 +324,75 @@ def build(
                     k_valid, v_valid, fill, elem, kv_scale, kv_scale, k_scales, v_scales)
 
 
+def build_sink(
+    name: str,
+    seed: int,
+    capacity: int,
+    lengths: List[int],
+    *,
+    sink_period: int,
+    sink_rows: tuple = (0, 16, 32, 48),
+    c: float = 1.0,
+    elem: str = "f16",
+    sigma_k: float = 0.25,
+    sink_gain: float = 1.5,
+    q_scale: float = 1.0,
+) -> Workload:
+    """Attention-sink inputs: long runs of keys with small scores under a
+    few dominant ("sink") keys, the shape of a decode whose first tokens
+    take most of the attention.
+
+    Every query head of a KV group uses one query vector u ~ N(0, 1) (fp16).
+    Key row i of a sequence is a sink when i % sink_period is in sink_rows
+    (sink_period = 0: only the rows in sink_rows themselves); a sink key is
+    sink_gain * u, so with sink_gain 1.5 its score, about
+    sink_gain * |u|^2 / sqrt(128), lies some 17 nats above the other keys,
+    which are N(0, sigma_k^2). V is 0 on sink rows and c * U(0.5, 1.5)
+    elsewhere, so the output is c times the small share of the non-sink
+    rows. Encodings: "f16" stores the values as fp16 (v_scale 1); "e4m3"
+    stores K / 2^-4 and V / (c 2^-4) as E4M3 codes with k_scale 2^-4 and
+    v_scale c 2^-4; "nvfp4" stores K and V / c as block-scaled FP4 with
+    v_scale c.
+    """
+    import torch
+
+    assert elem in ("f16", "e4m3", "nvfp4"), elem
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lengths, dtype=np.int64)
+    B, Hq, Hkv = int(lens.shape[0]), NUM_Q_HEADS, NUM_KV_HEADS
+    G = Hq // Hkv
+    u = rng.standard_normal((B, Hkv, HEAD_DIM), dtype=np.float32).astype(np.float16)
+    q = np.repeat(u, G, axis=1)                      # heads 4g .. 4g + 3 share u[b, g]
+    k_valid, v_valid = [], []
+    k_scales, v_scales = ([], []) if elem == "nvfp4" else (None, None)
+    v_div = 1.0 if elem == "f16" else float(c)
+    for b in range(B):
+        L = int(min(max(lens[b], 0), capacity))
+        rows = np.arange(L)
+        sink = np.isin(rows % sink_period if sink_period > 0 else rows, sink_rows)
+        k = rng.standard_normal((Hkv, L, HEAD_DIM), dtype=np.float32) * np.float32(sigma_k)
+        k[:, sink, :] = np.float32(sink_gain) * u[b].astype(np.float32)[:, None, :]
+        v = rng.uniform(0.5, 1.5, (Hkv, L, HEAD_DIM)).astype(np.float32)
+        v *= np.float32(c / v_div)
+        v[:, sink, :] = 0.0
+        if elem == "f16":
+            k_valid.append(k.astype(np.float16))
+            v_valid.append(v.astype(np.float16))
+        elif elem == "e4m3":
+            to8 = lambda x: torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            k_valid.append(to8(k / np.float32(E4M3_SCALE)))
+            v_valid.append(to8(v / np.float32(E4M3_SCALE)))
+        else:
+            for x, vals, scs in ((k, k_valid, k_scales), (v, v_valid, v_scales)):
+                packed, sc = encode_nvfp4(x)
+                vals.append(packed)
+                scs.append(sc)
+    ks = E4M3_SCALE if elem == "e4m3" else 1.0
+    vs = (E4M3_SCALE * c) if elem == "e4m3" else (float(c) if elem == "nvfp4" else 1.0)
+    return Workload(name, q, lens.astype(np.int32), int(capacity), float(q_scale),
+                    k_valid, v_valid, "zero", elem, ks, vs, k_scales, v_scales)
+
+
 def _cfg4_lengths(rng: np.random.Generator) -> np.ndarray:
     # 90% short-prefix sequences, 10% long ones: 58 + 6 of 64, then shuffled.
     short = rng.integers(16, 512, 58, endpoint=True)
