@@ -25,7 +25,8 @@ from typing import Optional
 
 import torch  # must load before the library so both share one HIP runtime
 
-__all__ = ["gqa_decode", "gqa_decode_paged", "gqa_decode_fp4", "workspace_bytes", "release_workspace", "library_path",
+__all__ = ["gqa_decode", "gqa_decode_paged", "gqa_decode_fp4", "gqa_decode_noalloc",
+           "workspace_bytes", "release_workspace", "library_path",
            "load_library", "KernelTimer", "GqaDecodeError",
            "NUM_Q_HEADS", "NUM_KV_HEADS", "HEAD_DIM"]
 
@@ -72,6 +73,9 @@ def load_library():
     lib.gqa_decode_ex.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(_Layout), f32, f32, f32,
                                   i32, i32, i32, vp]
     lib.gqa_decode_ex.restype = i32
+    lib.gqa_decode_ex_noalloc.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(_Layout), f32, f32,
+                                          f32, i32, i32, i32, vp]
+    lib.gqa_decode_ex_noalloc.restype = i32
     lib.gqa_decode_fp4.argtypes = [vp, vp, ctypes.POINTER(_BlockScales), vp, vp,
                                    ctypes.POINTER(_Layout), f32, f32, f32, i32, i32, i32, vp]
     lib.gqa_decode_fp4.restype = i32
@@ -252,6 +256,39 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor
         st = lib.gqa_decode_chunked(*args, float(q_scale), B, C, chunk_len, stream)
     else:
         st = lib.gqa_decode(*args, float(q_scale), B, C, stream)
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def gqa_decode_noalloc(q: torch.Tensor, kv: torch.Tensor, sequence_lengths: torch.Tensor, *,
+                       out: torch.Tensor, q_scale: float = 1.0, chunk_len: int = 0,
+                       k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """gqa_decode through the allocation-free entry point
+    (gqa_decode_ex_noalloc): the library takes its fixed device scratch
+    instead of a cached workspace, and ``out`` must be given. Same tensors,
+    results (bitwise) and errors as gqa_decode, except that shapes whose
+    partial results do not fit the scratch raise GqaDecodeError
+    (GQA_ERR_BAD_SHAPE). Calls on one device must not overlap.
+    """
+    def kv_shape(B):
+        ks = kv.shape
+        if ks[0] != B or ks[1] != 2 or ks[4] != HEAD_DIM:
+            raise ValueError(f"kv must have shape [{B}, 2, kv_heads, capacity, 128], "
+                             f"got {tuple(ks)}")
+
+    if out is None:
+        raise ValueError("gqa_decode_noalloc needs a caller-allocated out")
+    code, _, out = _prepare(q, kv, sequence_lengths, out, kv_shape)
+    _check_chunk(chunk_len)
+    B, C, Hq, Hkv = q.shape[0], kv.shape[3], q.shape[1], kv.shape[2]
+    lay = _Layout(q.stride(0), q.stride(1), kv.stride(0), kv.stride(1), kv.stride(2),
+                  kv.stride(3), None, 0, 0, 0, Hq, Hkv)
+    lib = _lib if _lib is not None else load_library()
+    st = lib.gqa_decode_ex_noalloc(q.data_ptr(), kv.data_ptr(), sequence_lengths.data_ptr(),
+                                   out.data_ptr(), code, ctypes.byref(lay), float(q_scale),
+                                   float(k_scale), float(v_scale), B, C, chunk_len,
+                                   _stream_of(q.device))
     if st != 0:
         _raise(lib, st)
     return out

@@ -465,10 +465,13 @@ int check_alias(const void* q, const void* kv, const int32_t* seq_lens, const vo
   return GQA_OK;
 }
 
+// noalloc: take the fixed device scratch (gqa::scratch_area) instead of the
+// cached per-stream workspace, and allocate nothing (no timing events
+// either); shapes whose partials or tickets do not fit it are rejected.
 int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
                 const int32_t* seq_lens, void* out, int dtype, const gqa_layout* layout,
                 float q_scale, float k_scale, float v_scale, int batch, int capacity,
-                int chunk_len, hipStream_t stream) {
+                int chunk_len, hipStream_t stream, bool noalloc = false) {
   int st = check_args(q, kv, seq_lens, out, batch, capacity, chunk_len);
   if (st != GQA_OK) return st;
   if (dtype != GQA_DTYPE_F16 && dtype != GQA_DTYPE_BF16 && dtype != GQA_DTYPE_E4M3_KV &&
@@ -535,15 +538,42 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
                   "(partials would need %zu bytes)",
                   chunk_len, batch, capacity, pbytes);
       } else {
-        void* ws = get_workspace(dev, stream, pbytes, &st);
         if (g_launch_form < 0)
           g_launch_form = env_int("GQA_DECODE_LAUNCH_FORM", GQA_LAUNCH_AUTO, 0, 2);
         const bool single = g_launch_form == GQA_LAUNCH_SINGLE ||
                             (g_launch_form == GQA_LAUNCH_AUTO &&
                              capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY &&
                              (long long)batch * Hkv * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS);
+        void* ws = nullptr;
         int* tickets = nullptr;
-        if (ws && single) tickets = get_tickets(dev, stream, (size_t)batch * Hkv, &st);
+        if (noalloc) {
+          void* base = nullptr;
+          const size_t ticket_need = (size_t)batch * Hkv * sizeof(int);
+          const size_t room = gqa::kScratchBytes - gqa::kScratchTicketBytes;
+          const hipError_t se = gqa::scratch_area(dev, &base);
+          if (se != hipSuccess) {
+            (void)hipGetLastError();
+            st = fail(GQA_ERR_LAUNCH, "gqa_decode_ex_noalloc: the scratch address of device %d "
+                      "could not be looked up: %s", dev, hipGetErrorString(se));
+          } else if (pbytes > room) {
+            st = fail(GQA_ERR_BAD_SHAPE,
+                      "gqa_decode_ex_noalloc: this call needs %zu bytes of partial results and "
+                      "segment descriptors; the fixed scratch holds %zu (use gqa_decode_ex)",
+                      pbytes, room);
+          } else if (single && ticket_need > gqa::kScratchTicketBytes) {
+            st = fail(GQA_ERR_BAD_SHAPE,
+                      "gqa_decode_ex_noalloc: the single launch needs %zu ticket bytes "
+                      "(batch x KV heads x 4); the fixed scratch holds %zu (use the two-kernel "
+                      "form or gqa_decode_ex)",
+                      ticket_need, gqa::kScratchTicketBytes);
+          } else {
+            tickets = single ? static_cast<int*>(base) : nullptr;
+            ws = static_cast<char*>(base) + gqa::kScratchTicketBytes;
+          }
+        } else {
+          ws = get_workspace(dev, stream, pbytes, &st);
+          if (ws && single) tickets = get_tickets(dev, stream, (size_t)batch * Hkv, &st);
+        }
         if (ws && (tickets || !single)) {
           // Scores are formed as dot * q_scale * k_scale / sqrt(128) * log2(e),
           // so the kernel can use the hardware base-2 exponential.
@@ -551,7 +581,7 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
                                std::sqrt((double)GQA_HEAD_DIM) * 1.4426950408889634;
           hipEvent_t* ev = nullptr;
           hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-          if (g_profiling && hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+          if (!noalloc && g_profiling && hipStreamIsCapturing(stream, &cap) == hipSuccess &&
               cap == hipStreamCaptureStatusNone) {
             if (g_profile_used == g_profile.size()) {
               ProfileRecord rec;
@@ -614,6 +644,16 @@ int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* 
     return fail(GQA_ERR_BAD_ARG, "gqa_decode_ex: an FP4 cache goes through gqa_decode_fp4");
   return decode_impl(q, kv, nullptr, seq_lens, out, dtype, layout, q_scale, k_scale, v_scale,
                      batch, capacity, chunk_len, stream);
+}
+
+int gqa_decode_ex_noalloc(const void* q, const void* kv, const int32_t* seq_lens, void* out,
+                          int dtype, const gqa_layout* layout, float q_scale, float k_scale,
+                          float v_scale, int batch, int capacity, int chunk_len,
+                          hipStream_t stream) {
+  if (dtype == GQA_DTYPE_FP4_KV)
+    return fail(GQA_ERR_BAD_ARG, "gqa_decode_ex_noalloc: an FP4 cache goes through gqa_decode_fp4");
+  return decode_impl(q, kv, nullptr, seq_lens, out, dtype, layout, q_scale, k_scale, v_scale,
+                     batch, capacity, chunk_len, stream, true);
 }
 
 int gqa_decode_fp4(const void* q, const void* kv, const gqa_block_scales* scales,

@@ -60,6 +60,12 @@
 
 #include "launch.h"
 
+// Scratch of the allocation-free entry point: the library's only device
+// memory that is not allocated at run time. Host code never passes this
+// name to a kernel or a copy (on the host it is a stand-in, not a device
+// address); it uses the address that scratch_area() looks up per device.
+static __device__ __align__(256) unsigned char scratch[gqa::kScratchBytes];
+
 namespace gqa {
 namespace {
 
@@ -1703,6 +1709,24 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(const int2* seg_d
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch_ptr[kMaxScratchDevices];   // per device: the scratch's device address
+}  // namespace
+
+hipError_t scratch_area(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int resident_workgroups_per_cu() {
   const void* kernels[16] = {

@@ -52,6 +52,17 @@ size_t partial_bytes_for_grid(long long grid, int group);
 // Bytes of per-segment descriptors for a batch (rounded to 256).
 size_t segment_bytes_for_batch(int batch, int kv_heads);
 
+// Fixed device scratch of the allocation-free entry point (one copy per
+// device, held until the process ends): the single launch's tickets in the
+// first kScratchTicketBytes (zero when the code object loads; every call
+// leaves them zero), then the segment descriptors and partial results.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchTicketBytes = (size_t)1 << 20;
+
+// Device address of the scratch on device `dev`, which must be current
+// (looked up once per device, then cached; the caller serialises calls).
+hipError_t scratch_area(int dev, void** ptr);
+
 // Enqueue the decode. `partials` must hold segment_bytes_for_batch(batch,
 // kv_heads) + partial_bytes_for_grid(grid, group) bytes. With `tickets`
 // (kv_heads * batch ints, zero before the call and left zero by it) one

@@ -250,6 +250,36 @@ int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* 
                   const gqa_layout* layout, float q_scale, float k_scale, float v_scale,
                   int batch, int capacity, int chunk_len, hipStream_t stream);
 
+/*
+ * gqa_decode_ex_noalloc -- gqa_decode_ex that allocates no device memory,
+ * for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops and harnesses that forbid allocation.
+ *
+ * Arguments, layouts, results and errors are those of gqa_decode_ex, and the
+ * result is bitwise the same. Instead of the cached per-stream workspace, the
+ * partial results, segment descriptors and single-launch tickets live in a
+ * fixed 16 MiB device array compiled into the library: each device the
+ * library runs on holds one copy, from the first call on that device until
+ * the process ends. The first 1 MiB holds the tickets, which are zero when
+ * the library is loaded and left zero by every call. The other 15 MiB take
+ * the partials and descriptors: the automatic split needs about
+ * 2 x (resident workgroups) x G x 520 B plus 8 B per (sequence, KV head),
+ * about 2.2 MB at the page's 32/8 heads on an MI355X plus 8 KiB per 128
+ * sequences.
+ * Limits: a call whose partials and descriptors exceed 15 MiB (large
+ * batches, or small chunk_len), or that takes the single launch with more
+ * than 2^18 (sequence, KV head) pairs, returns GQA_ERR_BAD_SHAPE with
+ * nothing enqueued. Calls that overlap on one device share the array and
+ * race: calls on one device must be ordered (one stream, or streams joined
+ * by events), including replays of graphs that captured this call. No
+ * timing events are recorded (gqa_decode_profile_begin does not apply).
+ * dtype: as for gqa_decode_ex (FP4 caches: GQA_ERR_BAD_ARG).
+ */
+int gqa_decode_ex_noalloc(const void* q, const void* kv, const int32_t* seq_lens, void* out,
+                          int dtype, const gqa_layout* layout, float q_scale, float k_scale,
+                          float v_scale, int batch, int capacity, int chunk_len,
+                          hipStream_t stream);
+
 /* E4M3 block scales per 128-element FP4 head row (one per 16 elements). */
 #define GQA_FP4_SCALES_PER_ROW 8
 

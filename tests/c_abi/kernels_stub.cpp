@@ -20,6 +20,11 @@ size_t segment_bytes_for_batch(int batch, int kv_heads) {
   return ((size_t)batch * kv_heads * 8 + 255) & ~(size_t)255;
 }
 
+hipError_t scratch_area(int, void** ptr) {
+  *ptr = nullptr;
+  return hipErrorNoDevice;   // never reached without a device
+}
+
 hipError_t launch_decode(const void*, const void*, const int32_t*, void*, ElemType, const Layout&,
                          float, float, int, int, const SplitConfig&, long long, void*, int*,
                          hipStream_t, hipEvent_t*) {

@@ -52,7 +52,7 @@ def test_header_declares_the_documented_entry_points():
     names = _declared_functions()
     assert names == sorted([
         "gqa_decode", "gqa_decode_chunked", "gqa_decode_typed", "gqa_decode_ex",
-        "gqa_decode_fp4", "gqa_decode_workspace_bytes", "gqa_decode_set_launch_form",
+        "gqa_decode_ex_noalloc", "gqa_decode_fp4", "gqa_decode_workspace_bytes", "gqa_decode_set_launch_form",
         "gqa_decode_release_workspace", "gqa_decode_status_string", "gqa_decode_last_error",
         "gqa_decode_profile_begin", "gqa_decode_profile_end"])
 
@@ -243,6 +243,24 @@ def test_layout_argument_errors(lib):
     assert _call_ex(lib, _layout(q_stride_batch=1 << 20), out=0x10000 + (1 << 20)) == ALIAS
     assert _call_ex(lib, _layout(block_table=0x40000 + 4096, max_pages=4, page_size=16,
                                  num_pages=9)) == ALIAS
+
+
+def test_noalloc_entry_point_argument_errors(lib):
+    # the allocation-free variant validates like gqa_decode_ex, before any
+    # device work or scratch lookup
+    f = lib.gqa_decode_ex_noalloc
+    lay = _layout()
+    args = lambda **k: dict(dict(q=0x10000, kv=0x20000000, lens=0x30000, out=0x40000, dtype=0,
+                                 B=2, C=64, chunk=0), **k)
+    call = lambda a: f(a["q"], a["kv"], a["lens"], a["out"], a["dtype"], ctypes.byref(lay), 1.0,
+                       1.0, 1.0, a["B"], a["C"], a["chunk"], None)
+    assert call(args(q=None)) == NULL
+    assert call(args(B=0)) == BAD_SHAPE
+    assert call(args(out=0x40004)) == MISALIGNED
+    assert call(args(chunk=-1)) == BAD_ARG
+    assert call(args(dtype=3)) == BAD_ARG                       # FP4 goes through gqa_decode_fp4
+    assert "gqa_decode_fp4" in lib.gqa_decode_last_error().decode()
+    assert call(args()) == (MISMATCH if _gpu_visible() else NO_DEVICE)
 
 
 def test_head_count_argument_errors(lib):
