@@ -19,6 +19,10 @@ LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["gqa_decode_kernels.hip", "gqa_decode_api.cpp"]
+# Measurement kernels of bench.py (streaming-read ceiling, VALU load for the
+# counter check): a library of their own, outside the decode ABI.
+BENCH_LIB_PATH = os.path.join(PKG_DIR, "libgqa_bench.so")
+BENCH_SOURCES = ["bench_kernels.hip"]
 
 # Device-code flags. Packed fp32 instructions are switched off: hipcc would
 # otherwise fuse pairs of fp32 FMAs into v_pk_fma_f32.
@@ -42,11 +46,18 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile the library; always rebuilds. Returns the .so path."""
-    tmp = LIB_PATH + ".tmp"
+    """Compile the decode library and the bench kernels' library; always
+    rebuilds. Returns the decode library's path."""
+    _compile(LIB_PATH, SOURCES, verbose, extra_flags)
+    _compile(BENCH_LIB_PATH, BENCH_SOURCES, verbose, None)
+    return LIB_PATH
+
+
+def _compile(out_path, sources, verbose, extra_flags):
+    tmp = out_path + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-shared",
            "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,8 +69,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{diag}")
     if verbose and diag.strip():
         print(diag, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
 
 
 if __name__ == "__main__":

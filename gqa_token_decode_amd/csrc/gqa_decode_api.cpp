@@ -127,14 +127,22 @@ const DeviceInfo& device_info(int dev) {
   return di;
 }
 
-// One equal piece per workgroup that can be resident at once (times an
-// optional factor), so the whole decode runs in a single round.
+// One equal piece per workgroup launched (times an optional factor), all of
+// them resident at once, so the whole decode runs in a single round.
+// Workgroups per CU: one for the 16-bit formats, whose kernels wait on HBM
+// (measured 1-3% faster than two on every workload: fewer, longer streams
+// per CU); as many as fit (two) for the E4M3 and FP4 caches, whose
+// conversion work needs a second wave per SIMD to overlap the loads (FP4:
+// 18-30% slower with one). GQA_DECODE_WG_PER_CU overrides it.
 // row_align (1, or 16 / 32 for paged caches) rounds the piece and cost sizes up.
-gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align) {
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, int dtype) {
   gqa::SplitConfig cfg;
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
   auto up = [row_align](int v) { return (v + row_align - 1) / row_align * row_align; };
-  cfg.pieces = (di.cus > 0 ? di.cus : 256) * (di.resident > 0 ? di.resident : 1) * per_slot;
+  const int resident = di.resident > 0 ? di.resident : 1;
+  const bool wide = dtype == GQA_DTYPE_F16 || dtype == GQA_DTYPE_BF16;
+  const int per_cu = env_int("GQA_DECODE_WG_PER_CU", wide ? 1 : resident, 1, resident);
+  cfg.pieces = (di.cus > 0 ? di.cus : 256) * per_cu * per_slot;
   cfg.min_piece = up(env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30));
   cfg.seg_cost = up(env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20));
   cfg.forced_piece = forced_piece > 0 ? up(forced_piece) : 0;
@@ -522,7 +530,7 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
       st = fail(di.status, "gqa_decode: device %d is %s; this library is built for gfx950", dev,
                 di.arch.c_str());
     } else {
-      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align);
+      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align, dtype);
       const int Hkv = res.lay.kv_heads, group = res.lay.q_heads / res.lay.kv_heads;
       const long long grid = gqa::grid_for(batch, capacity, Hkv, cfg);
       const size_t pbytes =
@@ -674,7 +682,8 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   std::lock_guard<std::mutex> lock(g_mu);
   const DeviceInfo& di = device_info(dev);
   if (di.status != GQA_OK) return 0;
-  const long long grid = gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0, 1));
+  const long long grid =
+      gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0, 1, GQA_DTYPE_F16));
   return gqa::segment_bytes_for_batch(batch, GQA_NUM_KV_HEADS) +
          gqa::partial_bytes_for_grid(grid, GQA_NUM_Q_HEADS / GQA_NUM_KV_HEADS);
 }

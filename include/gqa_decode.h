@@ -263,9 +263,9 @@ int gqa_decode_ex(const void* q, const void* kv, const int32_t* seq_lens, void* 
  * the process ends. The first 1 MiB holds the tickets, which are zero when
  * the library is loaded and left zero by every call. The other 15 MiB take
  * the partials and descriptors: the automatic split needs about
- * 2 x (resident workgroups) x G x 520 B plus 8 B per (sequence, KV head),
- * about 2.2 MB at the page's 32/8 heads on an MI355X plus 8 KiB per 128
- * sequences.
+ * 2 x (workgroups launched) x G x 520 B plus 8 B per (sequence, KV head);
+ * on an MI355X (256 or 512 workgroups, by element type) that is at most
+ * about 2.2 MB at the page's 32/8 heads plus 8 KiB per 128 sequences.
  * Limits: a call whose partials and descriptors exceed 15 MiB (large
  * batches, or small chunk_len), or that takes the single launch with more
  * than 2^18 (sequence, KV head) pairs, returns GQA_ERR_BAD_SHAPE with
