@@ -142,7 +142,17 @@ gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_al
   const int resident = di.resident > 0 ? di.resident : 1;
   const bool wide = dtype == GQA_DTYPE_F16 || dtype == GQA_DTYPE_BF16;
   const int per_cu = env_int("GQA_DECODE_WG_PER_CU", wide ? 1 : resident, 1, resident);
-  cfg.pieces = (di.cus > 0 ? di.cus : 256) * per_cu * per_slot;
+  const int cus = di.cus > 0 ? di.cus : 256;
+  cfg.pieces = cus * per_cu * per_slot;
+  // With more than one workgroup per CU, the first `cus` of the grid (one per
+  // CU, dispatched first) take longer pieces than the rest, which share their
+  // CU with an older workgroup (see the kernel's piece_lens).
+  cfg.pieces_first = per_cu >= 2 && per_slot == 1 ? cus : cfg.pieces;
+  // FP4: the younger workgroups take 40/64 of the older ones' rows (3-8%
+  // faster on the long workloads, measured; the kernel keeps equal pieces
+  // when they are short). E4M3 measured no gain.
+  cfg.second_share =
+      env_int("GQA_DECODE_SECOND_SHARE", dtype == GQA_DTYPE_FP4_KV ? 40 : 64, 1, 64);
   cfg.min_piece = up(env_int("GQA_DECODE_MIN_PIECE", kMinPieceDefault, 1, 1 << 30));
   cfg.seg_cost = up(env_int("GQA_DECODE_SEG_COST", kSegCostDefault, 0, 1 << 20));
   cfg.forced_piece = forced_piece > 0 ? up(forced_piece) : 0;

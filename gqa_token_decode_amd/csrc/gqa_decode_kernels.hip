@@ -140,7 +140,10 @@ struct Params {
   int q_heads;         // Hq (rows of out per sequence)
   int wave_planner;    // 1: batch <= 64 and every cost total fits 32 bits
   int combine_per_head;   // combine kernel: one workgroup per (segment, head)
-  int pieces;          // automatic split: number of equal pieces
+  int pieces;          // automatic split: number of pieces (one per workgroup)
+  int pieces_first;    // automatic split: pieces 0 .. pieces_first - 1 are Qa units
+                       // long, the others Qb (all equal when pieces_first == pieces)
+  int second_share;    // Qb / Qa in 1/64ths (64: equal pieces)
   int min_piece;       // automatic split: lower bound on the piece length
   int forced_piece;    // > 0: fixed piece length
   int seg_cost;        // fixed cost units per segment (c0)
@@ -290,12 +293,81 @@ __device__ __forceinline__ unsigned wave_incl_scan(unsigned v) {
   return v;
 }
 
-// Piece length Q for this call (total < 2^32: 32-bit division).
-__device__ __forceinline__ long long piece_len32(const Params& P, unsigned total) {
-  if (P.forced_piece > 0) return P.forced_piece;
-  unsigned Q = total / (unsigned)P.pieces + (total % (unsigned)P.pieces != 0);
-  Q = Q < (unsigned)P.min_piece ? (unsigned)P.min_piece : Q;
-  return cost_len(P, Q);
+// The cost line of a call is cut into P.pieces pieces, one per workgroup:
+// pieces 0 .. G1 - 1 are Qa units long, the others Qb. With G1 == pieces (or
+// a forced length) all are equal. Otherwise the workgroups that share a CU
+// with an older one (ids >= G1, the second round of the dispatch) get the
+// shorter pieces: on a CU the older workgroup's waves win instruction issue,
+// which slows the younger ones by up to 1.6x in the compute-heavier kernels
+// (FP4: 1.53 vs 0.94 us per tile, measured with per-wave clocks), and the
+// CU's last stretch, with only the younger workgroup left, runs one wave
+// per SIMD.
+struct Pieces {
+  long long Qa, Qb, G1;
+};
+constexpr long long kTwoRateMinUnits = 1024;   // cost units per piece, on average
+
+__device__ __forceinline__ long long piece_start(const Pieces& pc, long long w) {
+  return w < pc.G1 ? w * pc.Qa : pc.G1 * pc.Qa + (w - pc.G1) * pc.Qb;
+}
+
+__device__ __forceinline__ long long piece_length(const Pieces& pc, long long w) {
+  return w < pc.G1 ? pc.Qa : pc.Qb;
+}
+
+// x / q for cost positions (both non-negative).
+__device__ __forceinline__ long long div_cost(const Params& P, long long x, long long q) {
+  return P.wave_planner ? (long long)((unsigned)x / (unsigned)q) : x / q;
+}
+
+// Index of the piece holding cost position x (below the total).
+__device__ __forceinline__ long long piece_of(const Params& P, const Pieces& pc, long long x) {
+  const long long a = pc.G1 * pc.Qa;
+  return x < a ? div_cost(P, x, pc.Qa) : pc.G1 + div_cost(P, x - a, pc.Qb);
+}
+
+// Piece lengths for a cost total (32-bit arithmetic where the planner keeps
+// every total below 2^32). Equal pieces: Q = ceil(total / pieces), at least
+// min_piece, rounded up to the row alignment. Two lengths: Qb = ceil(Qa *
+// share / 64) (at least min_piece, aligned) and Qa the smallest aligned
+// length that covers the total, G1 Qa + (pieces - G1) Qb >= total (a double
+// estimate, then exact upward steps).
+__device__ __forceinline__ Pieces piece_lens(const Params& P, long long total) {
+  Pieces pc;
+  pc.G1 = P.pieces;
+  if (P.forced_piece > 0) {
+    pc.Qa = pc.Qb = P.forced_piece;
+    return pc;
+  }
+  // Two lengths only for long pieces: on short ones (a few tiles per wave)
+  // the call is latency-bound and the longer pieces would set its end.
+  if (P.pieces_first >= P.pieces || total < (long long)P.pieces * kTwoRateMinUnits) {
+    long long Q;
+    if (P.wave_planner) {
+      const unsigned t = (unsigned)total;
+      Q = t / (unsigned)P.pieces + (t % (unsigned)P.pieces != 0);
+    } else {
+      Q = (total + P.pieces - 1) / P.pieces;
+    }
+    Q = Q < P.min_piece ? P.min_piece : Q;
+    pc.Qa = pc.Qb = cost_len(P, Q);
+    return pc;
+  }
+  const long long G1 = P.pieces_first, G2 = P.pieces - G1;
+  auto qb_of = [&](long long qa) {
+    long long qb = (qa * P.second_share + 63) / 64;
+    qb = qb < P.min_piece ? P.min_piece : qb;
+    return cost_len(P, qb);
+  };
+  const double den = (double)G1 + (double)G2 * (double)P.second_share * (1.0 / 64.0);
+  long long qa = (long long)((double)total / den);
+  qa = cost_len(P, qa < P.min_piece ? P.min_piece : qa);
+  while (G1 * qa + G2 * qb_of(qa) < total) qa += P.row_align;
+  const long long qb = qb_of(qa);
+  pc.G1 = G1;
+  pc.Qa = qa < qb ? qb : qa;
+  pc.Qb = qb;
+  return pc;
 }
 
 // Small batches (<= 64): raw_len is lane b's seq_lens[b] (loaded at kernel
@@ -306,7 +378,7 @@ __device__ __forceinline__ long long piece_len32(const Params& P, unsigned total
 // the piece starts past it. *lens_v keeps the clamped lengths (lane b holds
 // sequence b's), so later segment steps read them with readlane instead of a
 // dependent memory load.
-__device__ long long wave_plan(const Params& P, int raw_len, long long* p_out, long long* q_out,
+__device__ long long wave_plan(const Params& P, int raw_len, long long* p_out, Pieces* pc_out,
                                long long* found, int* found_b, int* lens_v) {
   const int lane = threadIdx.x & 63;
   const long long len = lane < P.batch ? clamp_len(raw_len, P.capacity) : 0;
@@ -316,10 +388,10 @@ __device__ long long wave_plan(const Params& P, int raw_len, long long* p_out, l
       len > 0 ? (unsigned)P.kv_heads * (unsigned)(cost_len(P, len) + P.seg_cost) : 0u;
   const unsigned incl = wave_incl_scan(cost);
   const unsigned total = (unsigned)__builtin_amdgcn_readlane((int)incl, 63);
-  const long long Q = piece_len32(P, total);
-  const long long p = (long long)blockIdx.x * Q;
+  const Pieces pc = piece_lens(P, total);
+  const long long p = piece_start(pc, blockIdx.x);
   *p_out = p;
-  *q_out = Q;
+  *pc_out = pc;
   const long long lo = (long long)(incl - cost);
   const unsigned long long hit = __ballot(cost > 0 && p >= lo && p < (long long)incl);
   if (hit == 0) {
@@ -343,11 +415,24 @@ __device__ __forceinline__ int vchunk(int r, int c) { return c ^ (2 * (r & 7)); 
 
 // Rows [lo, hi) of segment (b, g) that lie in this workgroup's piece; row i
 // of the segment sits at cost position off + i (its fixed-cost units are
-// [off - c0, off)). Wave-uniform.
+// [off - c0, off)). Wave-uniform. The byte offsets of the segment's blocks
+// (set by seg_bases when the walk enters the segment) spare the tile loads
+// their 64-bit products: kvo is K row 0 of (b, g) relative to P.kv (paged
+// caches: the head's offset inside a page), sco the same for the FP4 block
+// scales, qo the group's first q row relative to P.q.
 struct Seg {
   int b, g, len, lo, hi;
   long long off;
+  long long kvo, sco, qo;
 };
+
+template <int F, bool kPaged>
+__device__ __forceinline__ void seg_bases(const Params& P, Seg& s) {
+  s.kvo = (kPaged ? 0 : (long long)s.b * P.kv_sb) + (long long)s.g * P.kv_sh;
+  if constexpr (F == kFmtFp4)
+    s.sco = (kPaged ? 0 : (long long)s.b * P.sc_sb) + (long long)s.g * P.sc_sh;
+  s.qo = (long long)s.b * P.q_sb + (long long)(s.g * P.group) * P.q_sh;
+}
 
 __device__ __forceinline__ void seg_set_range(Seg& s, long long p_begin, long long p_end) {
   const long long b = p_begin - s.off, e = p_end - s.off;
@@ -369,6 +454,9 @@ __device__ __forceinline__ int seq_len_of(const Params& P, int lens_v, int b) {
 
 // Advance to the next segment (next KV head of b, else the next non-empty
 // sequence). Only called while rows remain below p_end, so one exists.
+// kBases: also set the block offsets (the tile walk; the segment walk of the
+// merges needs only b and g).
+template <int F, bool kPaged, bool kBases>
 __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_end, int lens_v) {
   const long long end = s.off + cost_len(P, s.len) + P.seg_cost;
   if (s.g + 1 < P.kv_heads) {
@@ -386,31 +474,32 @@ __device__ __forceinline__ void seg_next(const Params& P, Seg& s, long long p_en
   }
   s.off = end;
   seg_set_range(s, end, p_end);
+  if constexpr (kBases) seg_bases<F, kPaged>(P, s);
 }
 
 // Move (s, t) to this wave's next tile in the piece: the next 16-row tile of
 // the wave in s, else its first tile in a later segment. Returns false when
 // the piece has no more tiles for this wave.
-template <int kRows>
+template <int F, bool kPaged>
 __device__ __forceinline__ bool tile_next(const Params& P, Seg& s, int& t, long long p_end, int wv,
                                           int lens_v) {
-  t += kWaves * kRows;
+  t += kWaves * tile_rows<F>();
   while (t >= s.hi) {
     if (!more_segments(P, s, p_end)) return false;
-    seg_next(P, s, p_end, lens_v);
-    t = s.lo + kRows * wv;
+    seg_next<F, kPaged, true>(P, s, p_end, lens_v);
+    t = s.lo + tile_rows<F>() * wv;
   }
   return true;
 }
 
 // First tile of this wave at or after (s, t) (t = s.lo + kRows * wv).
-template <int kRows>
+template <int F, bool kPaged>
 __device__ __forceinline__ bool tile_first(const Params& P, Seg& s, int& t, long long p_end, int wv,
                                            int lens_v) {
   while (t >= s.hi) {
     if (!more_segments(P, s, p_end)) return false;
-    seg_next(P, s, p_end, lens_v);
-    t = s.lo + kRows * wv;
+    seg_next<F, kPaged, true>(P, s, p_end, lens_v);
+    t = s.lo + tile_rows<F>() * wv;
   }
   return true;
 }
@@ -426,11 +515,14 @@ __device__ __forceinline__ int swz8(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (
 __device__ __forceinline__ int sw4(int r) { return (r >> 1) & 3; }
 
 // Buffer resource over rows [row0, row0 + nrows) of one K or V block that
-// starts at `base` (row stride kv_sr bytes); rows past nrows read as zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, long long row0,
-                                                            int nrows, long long sr) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + row0 * sr), 0,
-                                           nrows > 0 ? (int)(nrows * sr) : 0, kBufferFlags);
+// starts at `base` (row stride sr bytes); rows past nrows read as zeros.
+// Offsets inside a block fit 31 bits (the host keeps row stride x capacity,
+// or x page size, below 2^31), so they are formed in 32-bit arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int row0, int nrows,
+                                                            long long sr) {
+  const int sr32 = (int)sr;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (unsigned)(row0 * sr32)), 0,
+                                           nrows > 0 ? nrows * sr32 : 0, kBufferFlags);
 }
 
 // Page holding row i of sequence b (paged caches): the page id, or -1 if it
@@ -493,7 +585,7 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
   constexpr int kRows = tile_rows<F>();
   const int lane = threadIdx.x & 63;
   const int group = group_of<kG4>(P);
-  const char* qg = reinterpret_cast<const char*>(P.q) + s.b * P.q_sb + (s.g * group) * P.q_sh;
+  const char* qg = reinterpret_cast<const char*>(P.q) + s.qo;
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       (void*)qg, 0, live && live_q ? (int)((group - 1) * P.q_sh + 2 * kDim) : 0, kBufferFlags);
   // q: load u (one, or two in the general form) gives lane l 16 B of the
@@ -521,17 +613,16 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
       __amdgpu_buffer_rsrc_t rc, rs;
       if constexpr (kPaged) {
         const int psz_mask = (1 << P.page_shift) - 1;
-        const char* blk = reinterpret_cast<const char*>(P.kv) + kind * P.kv_sk + s.g * P.kv_sh;
-        const char* sblk = reinterpret_cast<const char*>(P.kv_scales) + kind * P.sc_sk +
-                           s.g * P.sc_sh;
+        const char* blk = reinterpret_cast<const char*>(P.kv) + kind * P.kv_sk + s.kvo;
+        const char* sblk = reinterpret_cast<const char*>(P.kv_scales) + kind * P.sc_sk + s.sco;
         const int n = pb.p0 < 0 ? 0 : (nrows < 32 ? nrows : 32);   // the tile's rows, one page
         rc = rows_rsrc(blk + (pb.p0 < 0 ? 0 : pb.p0), t & psz_mask, n, P.kv_sr);
         rs = rows_rsrc(sblk + (pb.s0 < 0 ? 0 : pb.s0), t & psz_mask, n, P.sc_sr);
       } else {
-        rc = rows_rsrc(reinterpret_cast<const char*>(P.kv) + s.b * P.kv_sb + kind * P.kv_sk +
-                           s.g * P.kv_sh, t, nrows, P.kv_sr);
-        rs = rows_rsrc(reinterpret_cast<const char*>(P.kv_scales) + s.b * P.sc_sb +
-                           kind * P.sc_sk + s.g * P.sc_sh, t, nrows, P.sc_sr);
+        rc = rows_rsrc(reinterpret_cast<const char*>(P.kv) + s.kvo + kind * P.kv_sk, t, nrows,
+                       P.kv_sr);
+        rs = rows_rsrc(reinterpret_cast<const char*>(P.kv_scales) + s.sco + kind * P.sc_sk, t,
+                       nrows, P.sc_sr);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -553,7 +644,7 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
   for (int kind = 0; kind < 2; ++kind) {
     __amdgpu_buffer_rsrc_t r0, r1;   // rows [0, 16) and [16, 32) of the tile
     if constexpr (kPaged) {
-      const char* blk = reinterpret_cast<const char*>(P.kv) + kind * P.kv_sk + s.g * P.kv_sh;
+      const char* blk = reinterpret_cast<const char*>(P.kv) + kind * P.kv_sk + s.kvo;
       const int psz_mask = (1 << P.page_shift) - 1;
       r0 = rows_rsrc(blk + (pb0 < 0 ? 0 : pb0), t & psz_mask, pb0 < 0 ? 0 : (nrows < 16 ? nrows : 16),
                      P.kv_sr);
@@ -562,8 +653,7 @@ __device__ __forceinline__ void issue_tile(const Params& P, const Seg& s, int t,
         r1 = rows_rsrc(blk + (pb1 < 0 ? 0 : pb1), (t + 16) & psz_mask,
                        pb1 < 0 ? 0 : (nrows - 16 < 16 ? nrows - 16 : 16), P.kv_sr);
     } else {
-      const char* blk = reinterpret_cast<const char*>(P.kv) + s.b * P.kv_sb + kind * P.kv_sk +
-                        s.g * P.kv_sh;
+      const char* blk = reinterpret_cast<const char*>(P.kv) + s.kvo + kind * P.kv_sk;
       r0 = rows_rsrc(blk, t, nrows, P.kv_sr);
       r1 = r0;
     }
@@ -1289,28 +1379,11 @@ __device__ __forceinline__ void merge_waves(const WaveAcc& acc, int group, int p
   if constexpr (!kG4) lds_barrier();
 }
 
-// x / q for cost positions (both non-negative).
-__device__ __forceinline__ long long div_cost(const Params& P, long long x, long long q) {
-  return P.wave_planner ? (long long)((unsigned)x / (unsigned)q) : x / q;
-}
-
 // Partial slot of a segment in piece w: 2w for the piece's first segment,
 // 2w + 1 for a segment that starts strictly inside the piece (at most one of
 // those is cut by the piece's end).
 __device__ __forceinline__ long long slot_of(long long seg_off, long long piece_start, int w) {
   return 2LL * w + (seg_off > piece_start ? 1 : 0);
-}
-
-// Piece length Q for this call.
-__device__ __forceinline__ long long piece_len(const Params& P, long long total) {
-  if (P.forced_piece > 0) return P.forced_piece;
-  long long Q = (total + P.pieces - 1) / P.pieces;
-  Q = Q < P.min_piece ? P.min_piece : Q;
-  return cost_len(P, Q);
-}
-
-__device__ long long this_piece_start(const Params& P, long long total) {
-  return (long long)blockIdx.x * piece_len(P, total);
 }
 
 // Empty sequences get zero rows and empty segment descriptors (workgroup w
@@ -1482,17 +1555,19 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   const int G = lane >> 4, j = lane & 15;
   const int w = blockIdx.x;
 
-  long long total, p0, found, Qw = 0;
+  long long total, p0, found;
+  Pieces pcw;
   int found_b, found_len = 0;
   int lens_v = 0;
   if (P.wave_planner) {
-    total = wave_plan(P, raw_len, &p0, &Qw, &found, &found_b, &lens_v);
+    total = wave_plan(P, raw_len, &p0, &pcw, &found, &found_b, &lens_v);
   } else {
     long long part = 0;
     for (int b = tid; b < P.batch; b += kThreads)
       part += seq_cost(P, clamp_len(P.seq_lens[b], P.capacity));
     total = block_sum(part, red);
-    p0 = this_piece_start(P, total);
+    pcw = piece_lens(P, total);
+    p0 = piece_start(pcw, w);
     found_b = -1;
     if (p0 < total) {
       locate(p0, P, red, &sh_found, &sh_found_b, &sh_found_len);
@@ -1510,8 +1585,12 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   }
   found = uniform64(found);
   found_b = __builtin_amdgcn_readfirstlane(found_b);
-  const long long Q = P.wave_planner ? uniform64(Qw) : piece_len(P, total);
-  const long long p1 = p0 + Q < total ? p0 + Q : total;
+  Pieces pc;
+  pc.Qa = uniform64(pcw.Qa);
+  pc.Qb = uniform64(pcw.Qb);
+  pc.G1 = uniform64(pcw.G1);
+  const long long len_w = piece_length(pc, w);
+  const long long p1 = p0 + len_w < total ? p0 + len_w : total;
 
   Seg s;
   s.b = found_b;
@@ -1527,6 +1606,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   while (s.g < P.kv_heads - 1 && (long long)(s.g + 1) * stride <= rel) ++s.g;
   s.off = found + (long long)s.g * stride + P.seg_cost;
   seg_set_range(s, p0, p1);
+  seg_bases<F, kPaged>(P, s);
   if (s.hi <= s.lo) {                               // only fixed-cost units in this piece
     zero_empty_sequences(P, lens_v, w);
     return;
@@ -1539,7 +1619,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   const LdsReads la = lds_reads<F>(st0);
   Seg pf = s;
   int pt = s.lo + kRows * wv;
-  const bool pf_ok = tile_first<kRows>(P, pf, pt, p1, wv, lens_v);
+  const bool pf_ok = tile_first<F, kPaged>(P, pf, pt, p1, wv, lens_v);
   PageBases pbs;                                    // paged: pages of the issued tile
   if constexpr (kPaged) pbs = page_bases<F>(P, pf, pt, pf_ok);
   issue_tile<F, kPaged, kG4>(P, pf, pt, pf_ok, true, st0, qslot, pbs);
@@ -1560,7 +1640,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
     for (int t = s.lo + kRows * wv; t < s.hi; t += kWaves * kRows) {
       Seg nf = pf;
       int nt = pt;
-      const bool n_ok = tile_next<kRows>(P, nf, nt, p1, wv, lens_v);
+      const bool n_ok = tile_next<F, kPaged>(P, nf, nt, p1, wv, lens_v);
       if constexpr (kPaged) pbs = page_bases<F>(P, nf, nt, n_ok);
       tile_step<F, kPaged, kG4>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
                 nf.off != s.off, pbs, t, s.hi, qb, acc);
@@ -1580,11 +1660,12 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
     // segment starts before p0 (ends after p1); only then a division, in 32
     // bits when every cost total fits them.
     const long long seg_end = s.off + s.len;
-    const long long first_w = s.off >= p0 ? w : div_cost(P, s.off, Q);
-    const long long last_w = seg_end <= p1 ? w : div_cost(P, seg_end - 1, Q);
+    const long long first_w = s.off >= p0 ? w : piece_of(P, pc, s.off);
+    const long long last_w = seg_end <= p1 ? w : piece_of(P, pc, seg_end - 1);
     // 2 * (pieces holding rows of the segment) + (it starts inside its first
     // piece, whose second slot then holds its partial)
-    const int n2 = (int)(2 * (last_w - first_w + 1)) + (s.off > first_w * Q ? 1 : 0);
+    const int n2 =
+        (int)(2 * (last_w - first_w + 1)) + (s.off > piece_start(pc, first_w) ? 1 : 0);
     if (!P.fused && first_w == w && tid == 0)        // the segment starts in this piece
       P.seg_desc[seg_id] = make_int2(w, n2);
     if (first_w == last_w) {                         // the segment lies in this piece
@@ -1623,7 +1704,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
     }
 
     if (!more_segments(P, s, p1)) break;
-    seg_next(P, s, p1, lens_v);
+    seg_next<F, kPaged, false>(P, s, p1, lens_v);
   }
 
   // Single launch: take a ticket for each cut segment; the piece that
@@ -1653,17 +1734,18 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
       const int seg = __builtin_amdgcn_readfirstlane(sh_cut[i][0]);
       const int fw = __builtin_amdgcn_readfirstlane(sh_cut[i][1]);
       const int n2 = __builtin_amdgcn_readfirstlane(sh_cut[i][2]);
+      // the merge reads pieces fw .. fw + n - 1 only, all inside the grid
+      const int nm = min(n2 >> 1, max(P.pieces - fw, 0));
       // the same subsets as the combine kernel: per head when it splits heads
       CombineLds& clds = *reinterpret_cast<CombineLds*>(&stages[0][0][0]);
       const int sb = seg / P.kv_heads, sg = seg % P.kv_heads;
       if (P.combine_per_head) {
         for (int h = 0; h < group_of<kG4>(P); ++h) {
           if (h > 0) __syncthreads();              // the previous head's LDS reads are done
-          combine_segment<kBf16, true, kG4>(P, sb, sg, fw, n2 >> 1, n2 & 1, h, 1, clds);
+          combine_segment<kBf16, true, kG4>(P, sb, sg, fw, nm, n2 & 1, h, 1, clds);
         }
       } else {
-        combine_segment<kBf16, true, kG4>(P, sb, sg, fw, n2 >> 1, n2 & 1, 0, group_of<kG4>(P),
-                                          clds);
+        combine_segment<kBf16, true, kG4>(P, sb, sg, fw, nm, n2 & 1, 0, group_of<kG4>(P), clds);
       }
     }
   }
@@ -1696,7 +1778,8 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_combine(const int2* seg_d
     asm volatile("" : "+v"(vseg));
     const int2 desc = seg_desc[vseg];
     const int b = seg / P.kv_heads, g = seg - b * P.kv_heads;
-    const int n = desc.y >> 1;
+    // at most the pieces after the first (a descriptor is never beyond the grid)
+    const int n = min(desc.y >> 1, max(P.pieces - desc.x, 0));
     if (n <= 1) continue;              // empty (zero rows) or finished by kernel 1
     if (merged) __syncthreads();       // the previous merge's LDS reads are done
     merged = true;
@@ -1830,6 +1913,9 @@ hipError_t launch_decode(const void* q, const void* kv, const int32_t* seq_lens,
   P.q_heads = layout.q_heads;
   P.group = group;
   P.pieces = (int)grid;
+  P.pieces_first = cfg.pieces_first > 0 && cfg.pieces_first < grid ? cfg.pieces_first : (int)grid;
+  P.second_share = cfg.second_share > 0 && cfg.second_share <= 64 ? cfg.second_share : 64;
+  if (P.second_share == 64) P.pieces_first = (int)grid;
   P.min_piece = cfg.min_piece;
   P.forced_piece = cfg.forced_piece;
   P.seg_cost = cfg.forced_piece > 0 ? 0 : cfg.seg_cost;

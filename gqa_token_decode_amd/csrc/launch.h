@@ -29,7 +29,9 @@ struct Layout {
 
 // How the device-side planner cuts the valid rows into pieces.
 struct SplitConfig {
-  int pieces;         // automatic split: number of equal pieces (one workgroup each)
+  int pieces;         // automatic split: number of pieces (one workgroup each)
+  int pieces_first;   // automatic split: the first pieces_first pieces are the longer ones
+  int second_share;   // automatic split: length of the others, in 1/64ths of the first (64: equal)
   int min_piece;      // automatic split: lower bound on the piece length (rows)
   int forced_piece;   // > 0: fixed piece length; the grid then covers batch*capacity rows
   int seg_cost;       // automatic split: fixed cost units per (sequence, KV head) segment
