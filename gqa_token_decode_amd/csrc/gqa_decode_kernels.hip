@@ -761,7 +761,10 @@ __device__ __forceinline__ LdsReads lds_reads(const e16_t* stage0) {
 #pragma unroll
     for (int rd = 0; rd < 4; ++rd)
       r.v[rd] = vbase + row * (kDim / 2) + 16 * (rd ^ sw4(row)) + 8 * (j >> 3);
-    r.v[4] = sbase + 32 * kFp4ScaleBytes + 4 * G * kFp4ScaleBytes;
+    // V scales, converted once per wave (fp4_v_scales): lane (rp, dq) =
+    // (lane / 4, lane % 4) reads the scale dword (blocks 4(dq / 2) .. +3) of
+    // rows 2rp and 2rp + 1.
+    r.v[4] = sbase + 32 * kFp4ScaleBytes + (lane >> 2) * 2 * kFp4ScaleBytes + 4 * ((lane & 3) >> 1);
 #pragma unroll
     for (int i = 5; i < 8; ++i) r.v[i] = 0;
 #pragma unroll
@@ -926,6 +929,35 @@ __device__ __forceinline__ void split_weight(float p, short& hi, short& lo) {
   }
 }
 
+// fp16 split of two weights at once: hi = (p0, p1) rounded to fp16, lo =
+// (p - hi) rounded again, the same bits as split_weight<false> on each. p - hi
+// is exact in fp32, so a fused multiply-add with mixed operands (hi as fp16,
+// p as fp32) rounds it once: one instruction per lo half (v_fma_mixlo_f16 and
+// v_fma_mixhi_f16 write the low and the high half) instead of a conversion
+// back to fp32, a subtraction and a conversion.
+__device__ __forceinline__ void split_weight_pair(float p0, float p1, unsigned& hi,
+                                                  unsigned& lo) {
+  const half2_t h = {(_Float16)p0, (_Float16)p1};
+  hi = __builtin_bit_cast(unsigned, h);
+  unsigned l;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(l)
+      : "v"(hi), "v"(p0), "v"(p1));
+  lo = l;
+}
+
+// Weights p[0..7] of an 8-row K = 32 operand as fp16 hi and lo parts.
+__device__ __forceinline__ void split_weights8(const float (&p)[8], half8_t& ph, half8_t& pl) {
+  unsigned h0, h1, h2, h3, l0, l1, l2, l3;
+  split_weight_pair(p[0], p[1], h0, l0);
+  split_weight_pair(p[2], p[3], h1, l1);
+  split_weight_pair(p[4], p[5], h2, l2);
+  split_weight_pair(p[6], p[7], h3, l3);
+  ph = __builtin_bit_cast(half8_t, ((uint4_t){h0, h1, h2, h3}));
+  pl = __builtin_bit_cast(half8_t, ((uint4_t){l0, l1, l2, l3}));
+}
+
 template <bool kBf16>
 __device__ __forceinline__ e16_t to_elem(float x) {
   if constexpr (kBf16)
@@ -935,31 +967,28 @@ __device__ __forceinline__ e16_t to_elem(float x) {
 }
 
 // Read the FP4 operands of one stage (byte offset OFF from stage 0): K codes
-// (2 x 16 B), K scales (2 x 2 B), V codes transposed (4 x 8 B) and V scales
-// (4 x 16 B: the 8 scale bytes of rows rowE(G, 0..7), two rows per read).
+// (2 x 16 B), K scales (2 x 2 B), V codes transposed (4 x 8 B) and one V
+// scale dword of each of two rows (the lane's share of the conversion in
+// fp4_v_scales).
 template <int OFF>
 __device__ __forceinline__ void read_stage_fp4(const LdsReads& a, uint4_t (&k)[2],
-                                               unsigned (&ks)[2], uint2 (&v)[4],
-                                               uint4_t (&vs)[4]) {
+                                               unsigned (&ks)[2], uint2 (&v)[4], uint2& vs) {
   asm volatile(
-      "ds_read_b128 %0, %12 offset:%19\n\t"
-      "ds_read_b128 %1, %13 offset:%19\n\t"
-      "ds_read_u16 %2, %14 offset:%19\n\t"
-      "ds_read_u16 %3, %15 offset:%19\n\t"
-      "ds_read_b64_tr_b4 %4, %16 offset:%19\n\t"
-      "ds_read_b64_tr_b4 %5, %17 offset:%19\n\t"
-      "ds_read_b64_tr_b4 %6, %18 offset:%19\n\t"
-      "ds_read_b64_tr_b4 %7, %20 offset:%19\n\t"
-      "ds_read_b128 %8, %21 offset:%19\n\t"
-      "ds_read_b128 %9, %21 offset:%22\n\t"
-      "ds_read_b128 %10, %21 offset:%23\n\t"
-      "ds_read_b128 %11, %21 offset:%24\n\t"
+      "ds_read_b128 %0, %10 offset:%17\n\t"
+      "ds_read_b128 %1, %11 offset:%17\n\t"
+      "ds_read_u16 %2, %12 offset:%17\n\t"
+      "ds_read_u16 %3, %13 offset:%17\n\t"
+      "ds_read_b64_tr_b4 %4, %14 offset:%17\n\t"
+      "ds_read_b64_tr_b4 %5, %15 offset:%17\n\t"
+      "ds_read_b64_tr_b4 %6, %16 offset:%17\n\t"
+      "ds_read_b64_tr_b4 %7, %18 offset:%17\n\t"
+      "ds_read_b32 %8, %19 offset:%17\n\t"
+      "ds_read_b32 %9, %19 offset:%20\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(ks[0]), "=&v"(ks[1]), "=&v"(v[0]), "=&v"(v[1]),
-        "=&v"(v[2]), "=&v"(v[3]), "=&v"(vs[0]), "=&v"(vs[1]), "=&v"(vs[2]), "=&v"(vs[3])
+        "=&v"(v[2]), "=&v"(v[3]), "=&v"(vs.x), "=&v"(vs.y)
       : "v"(a.k[0]), "v"(a.k[1]), "v"(a.k[2]), "v"(a.k[3]), "v"(a.v[0]), "v"(a.v[1]),
-        "v"(a.v[2]), "n"(OFF), "v"(a.v[3]), "v"(a.v[4]), "n"(OFF + 16), "n"(OFF + 128),
-        "n"(OFF + 144)
+        "v"(a.v[2]), "n"(OFF), "v"(a.v[3]), "v"(a.v[4]), "n"(OFF + kFp4ScaleBytes)
       : "memory");
 }
 
@@ -985,6 +1014,22 @@ __device__ __forceinline__ half8_t fp4x8_to_f16(unsigned x, half2_t s0, half2_t 
   return (half8_t){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// The V block scales of an FP4 tile as fp16 pairs, converted once per wave
+// rather than by each of the 16 lanes that use them. Lane (rp, dq) = (lane /
+// 4, lane % 4) holds, in vraw, the scale dword (blocks 4(dq / 2) .. +3) of
+// rows 2rp (x) and 2rp + 1 (y); one byte permute pairs the two rows' scales
+// of blocks 2dq and 2dq + 1, two conversions give (s[2rp][b], s[2rp + 1][b])
+// for b = 2dq, 2dq + 1, stored as entry 4rp + dq = lane of the wave's
+// 64-entry area. The PV operands pair exactly these rows.
+__device__ __forceinline__ void fp4_v_scales(uint2 vraw, uint2* vsh) {
+  const int lane = threadIdx.x & 63;
+  const unsigned c = 2u * ((unsigned)lane & 1u);   // byte of block 2dq in its dword
+  const unsigned sel = c | ((4u + c) << 8) | ((c + 1u) << 16) | ((5u + c) << 24);
+  const unsigned w = __builtin_amdgcn_perm(vraw.y, vraw.x, sel);
+  vsh[lane] = make_uint2(__builtin_bit_cast(unsigned, e4m3x2_to_f16<false>(w)),
+                         __builtin_bit_cast(unsigned, e4m3x2_to_f16<true>(w)));
+}
+
 // Fold tile rows [t, t + 32) of an FP4 tile held in LDS stage `par` into
 // acc. K: lane (G, j) holds depth 32G .. 32G + 31 of row 16h + j (q is read
 // in the same depth order); each depth block of 16 has its own scale. QK
@@ -994,17 +1039,18 @@ __device__ __forceinline__ half8_t fp4x8_to_f16(unsigned x, half2_t s0, half2_t 
 // those rows has its own scale for c's block, applied per element pair.
 __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
                                                  const uint4_t (&qb)[4], int t, int hi,
-                                                 float scale_log2, WaveAcc& acc) {
+                                                 float scale_log2, uint2* vsh, WaveAcc& acc) {
   const int lane = threadIdx.x & 63, G = lane >> 4;
   const float kNegInf = -__builtin_inff();
   uint4_t kd[2];
   unsigned ks[2];
   uint2 vt[4];
-  uint4_t vsc[4];
+  uint2 vraw;
   if (par)
-    read_stage_fp4<stage_bytes<kFmtFp4>()>(la, kd, ks, vt, vsc);
+    read_stage_fp4<stage_bytes<kFmtFp4>()>(la, kd, ks, vt, vraw);
   else
-    read_stage_fp4<0>(la, kd, ks, vt, vsc);
+    read_stage_fp4<0>(la, kd, ks, vt, vraw);
+  fp4_v_scales(vraw, vsh);
 
   float4_t sc[2];
 #pragma unroll
@@ -1042,17 +1088,15 @@ __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
-  half8_t ph, pl;
+  float p[8];
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = exp2_hw(sv[e] - m_new);      // 0 for rows out of range (score -inf)
-    psum += p;
-    short hs, ls;
-    split_weight<false>(p, hs, ls);
-    ph[e] = __builtin_bit_cast(_Float16, hs);
-    pl[e] = __builtin_bit_cast(_Float16, ls);
+    p[e] = exp2_hw(sv[e] - m_new);               // 0 for rows out of range (score -inf)
+    psum += p[e];
   }
+  half8_t ph, pl;
+  split_weights8(p, ph, pl);
   acc.l = acc.l * alpha + psum;
 
   // alpha is exactly 1 in every lane once no running maximum grows; the
@@ -1061,22 +1105,24 @@ __device__ __forceinline__ void compute_tile_fp4(const LdsReads& la, int par,
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc.O[db] *= alpha;
   }
-  // V scales: rows rowE(G, 2m) and rowE(G, 2m + 1) are consecutive rows;
-  // dword 2e + (db / 4) of vsc (e = local row) holds row e's scales of
-  // blocks 4 (db / 4) .. +3. For each row pair and block pair (db, db + 1)
-  // one byte permute gathers the four scale bytes, two conversions give the
-  // fp16 pairs.
-  const unsigned* vw = reinterpret_cast<const unsigned*>(vsc);
+  // V scales as fp16 pairs (fp4_v_scales): entry 4rp + k holds those of
+  // rows 2rp, 2rp + 1 for blocks 2k (x) and 2k + 1 (y); the lane's local rows
+  // 2m, 2m + 1 are the row pair rp = 2G + m (m < 2) or 8 + 2G + (m - 2).
+  uint2 sp[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int rp = (m < 2 ? 2 * G : 8 + 2 * G) + (m & 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sp[m][k] = vsh[4 * rp + k];
+  }
 #pragma unroll
   for (int rd = 0; rd < 4; ++rd) {
-    const int db = 2 * rd, hw = db >> 2, c = db & 3;
-    const unsigned sel = (unsigned)c | ((4u + c) << 8) | ((c + 1u) << 16) | ((5u + c) << 24);
+    const int db = 2 * rd;
     half2_t p0[4], p1[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const unsigned w = __builtin_amdgcn_perm(vw[2 * (2 * m + 1) + hw], vw[2 * (2 * m) + hw], sel);
-      p0[m] = e4m3x2_to_f16<false>(w);
-      p1[m] = e4m3x2_to_f16<true>(w);
+      p0[m] = __builtin_bit_cast(half2_t, sp[m][rd].x);
+      p1[m] = __builtin_bit_cast(half2_t, sp[m][rd].y);
     }
     const half8_t va0 = fp4x8_to_f16(vt[rd].x, p0[0], p0[1], p0[2], p0[3]);
     const half8_t va1 = fp4x8_to_f16(vt[rd].y, p1[0], p1[1], p1[2], p1[3]);
@@ -1134,17 +1180,15 @@ __device__ __forceinline__ void compute_tile8(const LdsReads& la, int par, const
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
-  half8_t ph, pl;
+  float p[8];
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = exp2_hw(sv[e] - m_new);      // 0 for rows out of range (score -inf)
-    psum += p;
-    short hs, ls;
-    split_weight<false>(p, hs, ls);
-    ph[e] = __builtin_bit_cast(_Float16, hs);
-    pl[e] = __builtin_bit_cast(_Float16, ls);
+    p[e] = exp2_hw(sv[e] - m_new);               // 0 for rows out of range (score -inf)
+    psum += p[e];
   }
+  half8_t ph, pl;
+  split_weights8(p, ph, pl);
   acc.l = acc.l * alpha + psum;
 
   // O^T = V^T P^T: every accumulator of this lane belongs to head j.
@@ -1202,16 +1246,28 @@ __device__ __forceinline__ void compute_tile(const LdsReads& la, int par, const 
   const float alpha = exp2_hw(acc.m - m_new);
   acc.m = m_new;
 
-  short4_t ph, pl;
+  float p[4];
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float p = exp2_hw(sv[r] - m_new);      // 0 for rows out of range (score -inf)
-    psum += p;
-    short h, l;
-    split_weight<kBf16>(p, h, l);
-    ph[r] = h;
-    pl[r] = l;
+    p[r] = exp2_hw(sv[r] - m_new);               // 0 for rows out of range (score -inf)
+    psum += p[r];
+  }
+  short4_t ph, pl;
+  if constexpr (kBf16) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      short h, l;
+      split_weight<true>(p[r], h, l);
+      ph[r] = h;
+      pl[r] = l;
+    }
+  } else {
+    unsigned h0, h1, l0, l1;
+    split_weight_pair(p[0], p[1], h0, l0);
+    split_weight_pair(p[2], p[3], h1, l1);
+    ph = __builtin_bit_cast(short4_t, make_uint2(h0, h1));
+    pl = __builtin_bit_cast(short4_t, make_uint2(l0, l1));
   }
   acc.l = acc.l * alpha + psum;
 
@@ -1241,7 +1297,7 @@ __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, i
                                           e16_t* nxt, e16_t* qslot, bool first,
                                           bool has_next, const Seg& nseg, int nt,
                                           bool next_new_seg, const PageBases& npb, int t, int hi,
-                                          uint4_t (&qb)[4], WaveAcc& acc) {
+                                          uint2* vsh, uint4_t (&qb)[4], WaveAcc& acc) {
   if (first) {
     // the q loads (the first 1 or 2 of the group) landed
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<F, kG4>() - (kG4 ? 1 : 2))
@@ -1251,7 +1307,7 @@ __device__ __forceinline__ void tile_step(const Params& P, const LdsReads& la, i
   issue_tile<F, kPaged, kG4>(P, nseg, nt, has_next, next_new_seg, nxt, qslot, npb);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(loads_per_tile<F, kG4>()) : "memory");   // K, V landed
   if constexpr (F == kFmtFp4)
-    compute_tile_fp4(la, par, qb, t, hi, P.scale_log2, acc);
+    compute_tile_fp4(la, par, qb, t, hi, P.scale_log2, vsh, acc);
   else if constexpr (F == kFmtE4m3)
     compute_tile8(la, par, qb, t, hi, P.scale_log2, acc);
   else
@@ -1549,6 +1605,8 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   if constexpr (kG4) rows4 = &rows4_lds;
   __shared__ int sh_last[2];
   __shared__ int sh_cut[2][3];   // single launch: (Hkv * b + g, first piece, n2) of cut segments
+  // FP4: each wave's V block scales as fp16 pairs (fp4_v_scales)
+  __shared__ __attribute__((aligned(16))) uint2 vscales[F == kFmtFp4 ? kWaves * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
@@ -1616,6 +1674,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
   e16_t* st0 = stages[wv][0];
   e16_t* st1 = stages[wv][1];
   e16_t* qslot = qslots[wv];
+  uint2* vsh = F == kFmtFp4 ? vscales + 64 * wv : vscales;
   const LdsReads la = lds_reads<F>(st0);
   Seg pf = s;
   int pt = s.lo + kRows * wv;
@@ -1643,7 +1702,7 @@ void gqa_decode_pieces(const int32_t* seq_lens, int batch, int wave_planner, Par
       const bool n_ok = tile_next<F, kPaged>(P, nf, nt, p1, wv, lens_v);
       if constexpr (kPaged) pbs = page_bases<F>(P, nf, nt, n_ok);
       tile_step<F, kPaged, kG4>(P, la, par, par ? st0 : st1, qslot, t == s.lo + kRows * wv, n_ok, nf, nt,
-                nf.off != s.off, pbs, t, s.hi, qb, acc);
+                nf.off != s.off, pbs, t, s.hi, vsh, qb, acc);
       pf = nf;
       pt = nt;
       par ^= 1;
