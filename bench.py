@@ -36,7 +36,9 @@ Both kinds of sample wait behind GPU work, so host launch time stays out.
 Read ceiling (read_ceiling): a plain streaming-read kernel (libgqa_bench.so)
 reads the same number of bytes, rotating over copies like the decode steps;
 its median time is the fastest these bytes stream on this GPU, and
-frac_of_read_ceiling = that time / the pieces kernel's time.
+frac_of_read_ceiling = that time / the pieces kernel's time (for the
+headline and, as read_ceiling_us / frac_of_read_ceiling, for each entry of
+`workloads`).
 
 Prints ONE JSON line:
   value       KV-read throughput: sum(L_b) * 4096 B / step time (GB/s)
@@ -749,6 +751,11 @@ def main(argv=None):
             "pieces_frac": round(kb / (to["pieces_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_copies_rotated": so["rot"],
         }
+        if not args.no_read_ceiling:
+            c = read_ceiling(kb, dev)
+            if c:
+                others[name]["read_ceiling_us"] = c["us"]
+                others[name]["frac_of_read_ceiling"] = round(c["us"] / to["pieces_us"], 4)
         del so, wo
         torch.cuda.empty_cache()
 
