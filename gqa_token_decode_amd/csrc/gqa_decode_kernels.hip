@@ -424,10 +424,14 @@ struct Seg {
   int b, g, len, lo, hi;
   long long off;
   long long kvo, sco, qo;
+  const __attribute__((address_space(4))) int32_t* btr;   // paged caches: b's block-table row
 };
 
 template <int F, bool kPaged>
 __device__ __forceinline__ void seg_bases(const Params& P, Seg& s) {
+  if constexpr (kPaged)
+    s.btr = (const __attribute__((address_space(4))) int32_t*)P.block_table +
+            (long long)s.b * P.max_pages;
   s.kvo = (kPaged ? 0 : (long long)s.b * P.kv_sb) + (long long)s.g * P.kv_sh;
   if constexpr (F == kFmtFp4)
     s.sco = (kPaged ? 0 : (long long)s.b * P.sc_sb) + (long long)s.g * P.sc_sh;
@@ -525,14 +529,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
                                            nrows > 0 ? nrows * sr32 : 0, kBufferFlags);
 }
 
-// Page holding row i of sequence b (paged caches): the page id, or -1 if it
-// is outside [0, num_pages) (its rows then read as zeros instead of
-// faulting). Uniform: one scalar load.
-__device__ __forceinline__ int page_id(const Params& P, int b, int i) {
-  const __attribute__((address_space(4))) int32_t* bt =
-      (const __attribute__((address_space(4))) int32_t*)P.block_table;
-  const int page = bt[(size_t)b * P.max_pages + (i >> P.page_shift)];
-  return (page >= 0 && page < P.num_pages) ? page : -1;
+// Page holding row i of the segment's sequence (paged caches; btr = that
+// sequence's block-table row): the page id, or -1 if it is outside [0,
+// num_pages) (its rows then read as zeros instead of faulting). Uniform:
+// one scalar load.
+__device__ __forceinline__ int page_id(const Params& P,
+                                       const __attribute__((address_space(4))) int32_t* btr,
+                                       int i) {
+  const int page = btr[(unsigned)i >> P.page_shift];
+  return (unsigned)page < (unsigned)P.num_pages ? page : -1;
 }
 
 // Byte offsets of the pages holding rows t and t + 16 of a tile of segment
@@ -548,7 +553,7 @@ __device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, i
   PageBases pb;
   const int nrows = live ? s.hi - t : 0;
   if (nrows > 0) {
-    const int id = page_id(P, s.b, t);
+    const int id = page_id(P, s.btr, t);
     if (id >= 0) {
       pb.p0 = (long long)id * P.kv_sb;
       if constexpr (F == kFmtFp4) pb.s0 = (long long)id * P.sc_sb;
@@ -556,7 +561,7 @@ __device__ __forceinline__ PageBases page_bases(const Params& P, const Seg& s, i
   }
   if constexpr (F == kFmtE4m3) {
     if (nrows > 16) {
-      const int id = page_id(P, s.b, t + 16);
+      const int id = page_id(P, s.btr, t + 16);
       if (id >= 0) pb.p1 = (long long)id * P.kv_sb;
     }
   }
