@@ -32,6 +32,12 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy()
 
 
+@pytest.fixture(autouse=True)
+def _restore_auto_form():
+    yield
+    _g().set_launch_form("auto")
+
+
 @pytest.mark.parametrize("elem", ["f16", "e4m3"])
 def test_graph_replays_match_eager_bitwise(elem):
     torch = _torch()
@@ -80,9 +86,14 @@ def test_graph_replays_match_eager_bitwise(elem):
     assert np.array_equal(_bits(outs[0]), _bits(ref))
 
 
-def test_two_streams_decode_concurrently():
+@pytest.mark.parametrize("form", ["two", "single"])
+def test_two_streams_decode_concurrently(form):
+    # Each stream has its own workspace (and, in the single launch, its own
+    # segment tickets): interleaved calls on two streams must not see each
+    # other's partials or tickets.
     torch = _torch()
     g = _g()
+    g.set_launch_form(form)
     a = workloads.get("b8_c4096_nanfill")
     b = workloads.build("stream b", 95, 8192, [8192, 100, 4000, 1, 7000, 3, 8000, 2], elem="f16")
     qa, kva, la = a.q_to_device(DEV), a.kv_to_device(DEV), torch.from_numpy(a.seq_lens).to(DEV)
