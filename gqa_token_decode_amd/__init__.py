@@ -423,7 +423,8 @@ def set_launch_form(form: str) -> None:
     """Select how later calls run the combine step: "single" (one kernel; the
     last workgroup of each cut segment merges it), "two" (pieces kernel, then
     combine kernel) or "auto" (single launch for capacities up to 512 with at
-    most 131072 cache rows, batch x KV heads x capacity, in all). The forms
+    most 131072 cache rows, batch x KV heads x capacity, in all, or up to 1024
+    with at most 32768 rows). The forms
     return the same bits."""
     if form not in _LAUNCH_FORMS:
         raise ValueError(f"launch form must be one of {sorted(_LAUNCH_FORMS)}, got {form!r}")

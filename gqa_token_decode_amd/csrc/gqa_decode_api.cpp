@@ -558,10 +558,13 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
       } else {
         if (g_launch_form < 0)
           g_launch_form = env_int("GQA_DECODE_LAUNCH_FORM", GQA_LAUNCH_AUTO, 0, 2);
-        const bool single = g_launch_form == GQA_LAUNCH_SINGLE ||
-                            (g_launch_form == GQA_LAUNCH_AUTO &&
-                             capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY &&
-                             (long long)batch * Hkv * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS);
+        const long long rows = (long long)batch * Hkv * capacity;
+        const bool single =
+            g_launch_form == GQA_LAUNCH_SINGLE ||
+            (g_launch_form == GQA_LAUNCH_AUTO &&
+             ((capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY && rows <= GQA_SINGLE_LAUNCH_MAX_ROWS) ||
+              (capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY_FEW_ROWS &&
+               rows <= GQA_SINGLE_LAUNCH_MAX_FEW_ROWS)));
         void* ws = nullptr;
         int* tickets = nullptr;
         if (noalloc) {

@@ -370,6 +370,8 @@ void gqa_decode_release_workspace(void);
 typedef enum gqa_launch_form {
   GQA_LAUNCH_AUTO = 0,    /* single launch when capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY
                              and batch * KV heads * capacity <= GQA_SINGLE_LAUNCH_MAX_ROWS,
+                             or capacity <= GQA_SINGLE_LAUNCH_MAX_CAPACITY_FEW_ROWS and
+                             batch * KV heads * capacity <= GQA_SINGLE_LAUNCH_MAX_FEW_ROWS;
                              else two kernels (the default)                                  */
   GQA_LAUNCH_SINGLE = 1,  /* one kernel: the last workgroup to finish a cut (sequence, KV
                              head) segment merges its partial results, found through a
@@ -378,9 +380,12 @@ typedef enum gqa_launch_form {
 } gqa_launch_form;
 
 /* Bounds within which GQA_LAUNCH_AUTO picks the single launch (short
- * caches, where saving the second launch outweighs the ticket round trips). */
+ * caches, where saving the second launch outweighs the ticket round trips;
+ * with few rows in all, caches up to twice as long). */
 #define GQA_SINGLE_LAUNCH_MAX_CAPACITY 512
 #define GQA_SINGLE_LAUNCH_MAX_ROWS 131072
+#define GQA_SINGLE_LAUNCH_MAX_CAPACITY_FEW_ROWS 1024
+#define GQA_SINGLE_LAUNCH_MAX_FEW_ROWS 32768
 
 /*
  * gqa_decode_set_launch_form -- select the launch form of later calls (all
