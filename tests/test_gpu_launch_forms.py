@@ -197,3 +197,43 @@ def test_combine_workgroups_taking_units_in_turns_match_bitwise(monkeypatch, cap
     g.gqa_decode(q, kv, ln, out=out, q_scale=w.q_scale)
     torch.cuda.synchronize()
     _assert_same(ref, _bits(out), f"{name}, combine grid {cap}")
+
+
+# (batch, capacity, q heads, KV heads): on both sides of each bound of the
+# automatic choice (capacity <= 512 with at most 131072 cache rows, or
+# capacity <= 1024 with at most 32768 rows; rows = batch x KV heads x capacity)
+AUTO_SHAPES = [
+    (1, 512, 32, 8), (32, 512, 32, 8), (33, 512, 32, 8),
+    (4, 1024, 32, 8), (5, 1024, 32, 8), (1, 1025, 32, 8), (1, 2048, 32, 8),
+    (32, 1024, 8, 1), (33, 1024, 8, 1), (3, 999, 24, 3),
+]
+
+
+def _auto_single(batch, capacity, kv_heads):
+    rows = batch * kv_heads * capacity
+    return (capacity <= 512 and rows <= 131072) or (capacity <= 1024 and rows <= 32768)
+
+
+@pytest.mark.parametrize("batch,capacity,hq,hkv", AUTO_SHAPES)
+def test_auto_form_follows_its_documented_bounds(batch, capacity, hq, hkv):
+    # A single launch runs no combine kernel, so the library's kernel timer
+    # records no combine time for it; a two-kernel call always records some.
+    torch = _torch()
+    g = _g()
+    gen = torch.Generator(device=DEV).manual_seed(batch * 10007 + capacity)
+    q = torch.randn(batch, hq, 128, device=DEV, generator=gen).half()
+    kv = torch.randn(batch, 2, hkv, capacity, 128, device=DEV, generator=gen).half()
+    lens = torch.full((batch,), capacity, dtype=torch.int32, device=DEV)
+    g.set_launch_form("auto")
+    g.gqa_decode(q, kv, lens)                    # workspace and tickets exist
+    torch.cuda.synchronize()
+    with g.KernelTimer() as t:
+        out = g.gqa_decode(q, kv, lens)
+        torch.cuda.synchronize()
+    want_single = _auto_single(batch, capacity, hkv)
+    assert t.calls == 1
+    assert (t.combine_ms == 0.0) == want_single, (
+        f"B={batch} C={capacity} Hkv={hkv}: combine {t.combine_ms * 1e3:.2f} us, "
+        f"expected {'single launch' if want_single else 'two kernels'}")
+    g.set_launch_form("single" if want_single else "two")
+    _assert_same(_bits(g.gqa_decode(q, kv, lens)), _bits(out), f"B={batch} C={capacity}")
