@@ -1,7 +1,9 @@
 """GPU parity through the C ABI from a plain C program (no Python, no torch
 in the decoding process): tests/c_abi/decode_from_c.c reads q, kv and the
 lengths from files, calls gqa_decode with HIP runtime memory and writes the
-output, which is checked against the CPU oracle with the page's bar.
+output, which is checked against the CPU oracle with the page's bar. The
+program first runs the same decode through gqa_decode_ex_noalloc and exits
+with status 4 unless both outputs are byte for byte the same.
 """
 import importlib.util
 import os
@@ -39,6 +41,7 @@ def test_c_program_matches_oracle(spec, tmp_path):
                           str(w.batch), str(w.capacity), repr(float(w.q_scale))],
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
+    assert "output identical to gqa_decode" in res.stdout
     got = np.fromfile(files["out"], dtype=np.float16).reshape(w.q.shape).astype(np.float64)
     ref = round_fp16(decode_ragged(w.q, w.k_valid, w.v_valid, w.q_scale)).astype(np.float64)
     d = np.abs(got - ref)
