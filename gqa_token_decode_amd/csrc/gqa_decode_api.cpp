@@ -131,18 +131,24 @@ const DeviceInfo& device_info(int dev) {
 // them resident at once, so the whole decode runs in a single round.
 // Workgroups per CU: one for the 16-bit formats, whose kernels wait on HBM
 // (measured 1-3% faster than two on every workload: fewer, longer streams
-// per CU); as many as fit (two) for the E4M3 and FP4 caches, whose
-// conversion work needs a second wave per SIMD to overlap the loads (FP4:
-// 18-30% slower with one). GQA_DECODE_WG_PER_CU overrides it.
+// per CU); as many as fit (two) for the FP4 cache, whose conversion work
+// needs a second wave per SIMD to overlap the loads (18-30% slower with
+// one). E4M3 cache: one while there are no more (sequence, KV head)
+// segments than CUs (measured 1-4% faster: each workgroup then holds at
+// most about two segments), else two, which overlap one workgroup's
+// segment-end merges with the other's tiles (5-33% faster on many short
+// segments). GQA_DECODE_WG_PER_CU overrides it.
 // row_align (1, or 16 / 32 for paged caches) rounds the piece and cost sizes up.
-gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, int dtype) {
+gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, int dtype,
+                              long long segments) {
   gqa::SplitConfig cfg;
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
   auto up = [row_align](int v) { return (v + row_align - 1) / row_align * row_align; };
   const int resident = di.resident > 0 ? di.resident : 1;
-  const bool wide = dtype == GQA_DTYPE_F16 || dtype == GQA_DTYPE_BF16;
-  const int per_cu = env_int("GQA_DECODE_WG_PER_CU", wide ? 1 : resident, 1, resident);
   const int cus = di.cus > 0 ? di.cus : 256;
+  const bool wide = dtype == GQA_DTYPE_F16 || dtype == GQA_DTYPE_BF16;
+  const bool one = wide || (dtype == GQA_DTYPE_E4M3_KV && segments <= cus);
+  const int per_cu = env_int("GQA_DECODE_WG_PER_CU", one ? 1 : resident, 1, resident);
   cfg.pieces = cus * per_cu * per_slot;
   // With more than one workgroup per CU, the first `cus` of the grid (one per
   // CU, dispatched first) take longer pieces than the rest, which share their
@@ -540,8 +546,9 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
       st = fail(di.status, "gqa_decode: device %d is %s; this library is built for gfx950", dev,
                 di.arch.c_str());
     } else {
-      const gqa::SplitConfig cfg = split_config(di, chunk_len, res.row_align, dtype);
       const int Hkv = res.lay.kv_heads, group = res.lay.q_heads / res.lay.kv_heads;
+      const gqa::SplitConfig cfg =
+          split_config(di, chunk_len, res.row_align, dtype, (long long)batch * Hkv);
       const long long grid = gqa::grid_for(batch, capacity, Hkv, cfg);
       const size_t pbytes =
           grid > 0 ? gqa::segment_bytes_for_batch(batch, Hkv) +
@@ -696,7 +703,8 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   const DeviceInfo& di = device_info(dev);
   if (di.status != GQA_OK) return 0;
   const long long grid =
-      gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS, split_config(di, 0, 1, GQA_DTYPE_F16));
+      gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS,
+                    split_config(di, 0, 1, GQA_DTYPE_F16, (long long)batch * GQA_NUM_KV_HEADS));
   return gqa::segment_bytes_for_batch(batch, GQA_NUM_KV_HEADS) +
          gqa::partial_bytes_for_grid(grid, GQA_NUM_Q_HEADS / GQA_NUM_KV_HEADS);
 }
