@@ -31,6 +31,7 @@ constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
 constexpr int kMinPieceDefault = 128;      // cost units: two 64-row steps of a workgroup
 constexpr int kSegCostDefault = 128;       // fixed cost of a segment, in row units
 constexpr int kCombineMaxGrid = 1 << 16;   // combine workgroups, at most
+constexpr int kShortCapacity = 256;        // 16-bit caches up to this many rows: two workgroups per CU
 // Forced chunk lengths may not make the workspace exceed this.
 constexpr size_t kMaxForcedWorkspace = (size_t)4 << 30;
 
@@ -129,25 +130,27 @@ const DeviceInfo& device_info(int dev) {
 
 // One equal piece per workgroup launched (times an optional factor), all of
 // them resident at once, so the whole decode runs in a single round.
-// Workgroups per CU: one for the 16-bit formats, whose kernels wait on HBM
-// (measured 1-3% faster than two on every workload: fewer, longer streams
-// per CU); as many as fit (two) for the FP4 cache, whose conversion work
-// needs a second wave per SIMD to overlap the loads (18-30% slower with
-// one). E4M3 cache: one while there are no more (sequence, KV head)
-// segments than CUs (measured 1-4% faster: each workgroup then holds at
-// most about two segments), else two, which overlap one workgroup's
-// segment-end merges with the other's tiles (5-33% faster on many short
-// segments). GQA_DECODE_WG_PER_CU overrides it.
+// Workgroups per CU: as many as fit (two) where segments are short or the
+// tiles' arithmetic is heavy, so that one workgroup's segment-end merges
+// and tile compute overlap the other's loads; one elsewhere (fewer, longer
+// streams per CU). Measured: 16-bit formats, one is 1-3% faster on every
+// workload with caches of 384 rows or more, two are 4-24% faster on
+// random lengths up to 256 (capacity <= 256); FP4 cache, two (one is
+// 18-30% slower); E4M3 cache, one while there are no more (sequence, KV
+// head) segments than CUs (1-4% faster: each workgroup then holds at most
+// about two segments), else two (5-33% faster on many short segments).
+// GQA_DECODE_WG_PER_CU overrides it.
 // row_align (1, or 16 / 32 for paged caches) rounds the piece and cost sizes up.
 gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, int dtype,
-                              long long segments) {
+                              long long segments, int capacity) {
   gqa::SplitConfig cfg;
   const int per_slot = env_int("GQA_DECODE_PIECES_PER_SLOT", kPiecesPerSlotDefault, 1, 64);
   auto up = [row_align](int v) { return (v + row_align - 1) / row_align * row_align; };
   const int resident = di.resident > 0 ? di.resident : 1;
   const int cus = di.cus > 0 ? di.cus : 256;
   const bool wide = dtype == GQA_DTYPE_F16 || dtype == GQA_DTYPE_BF16;
-  const bool one = wide || (dtype == GQA_DTYPE_E4M3_KV && segments <= cus);
+  const bool one = (wide && capacity > kShortCapacity) ||
+                   (dtype == GQA_DTYPE_E4M3_KV && segments <= cus);
   const int per_cu = env_int("GQA_DECODE_WG_PER_CU", one ? 1 : resident, 1, resident);
   cfg.pieces = cus * per_cu * per_slot;
   // With more than one workgroup per CU, the first `cus` of the grid (one per
@@ -548,7 +551,7 @@ int decode_impl(const void* q, const void* kv, const gqa_block_scales* scales,
     } else {
       const int Hkv = res.lay.kv_heads, group = res.lay.q_heads / res.lay.kv_heads;
       const gqa::SplitConfig cfg =
-          split_config(di, chunk_len, res.row_align, dtype, (long long)batch * Hkv);
+          split_config(di, chunk_len, res.row_align, dtype, (long long)batch * Hkv, capacity);
       const long long grid = gqa::grid_for(batch, capacity, Hkv, cfg);
       const size_t pbytes =
           grid > 0 ? gqa::segment_bytes_for_batch(batch, Hkv) +
@@ -704,7 +707,8 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity) {
   if (di.status != GQA_OK) return 0;
   const long long grid =
       gqa::grid_for(batch, capacity, GQA_NUM_KV_HEADS,
-                    split_config(di, 0, 1, GQA_DTYPE_F16, (long long)batch * GQA_NUM_KV_HEADS));
+                    split_config(di, 0, 1, GQA_DTYPE_F16, (long long)batch * GQA_NUM_KV_HEADS,
+                                 capacity));
   return gqa::segment_bytes_for_batch(batch, GQA_NUM_KV_HEADS) +
          gqa::partial_bytes_for_grid(grid, GQA_NUM_Q_HEADS / GQA_NUM_KV_HEADS);
 }
