@@ -31,7 +31,7 @@ constexpr int kPiecesPerSlotDefault = 1;   // one piece per resident workgroup
 constexpr int kMinPieceDefault = 128;      // cost units: two 64-row steps of a workgroup
 constexpr int kSegCostDefault = 128;       // fixed cost of a segment, in row units
 constexpr int kCombineMaxGrid = 1 << 16;   // combine workgroups, at most
-constexpr int kShortCapacity = 256;        // 16-bit caches up to this many rows: two workgroups per CU
+constexpr int kShortCapacity = 256;        // caches of at most this many rows count as short
 // Forced chunk lengths may not make the workspace exceed this.
 constexpr size_t kMaxForcedWorkspace = (size_t)4 << 30;
 
@@ -135,11 +135,15 @@ const DeviceInfo& device_info(int dev) {
 // and tile compute overlap the other's loads; one elsewhere (fewer, longer
 // streams per CU). Measured: 16-bit formats, one is 1-3% faster on every
 // workload with caches of 384 rows or more, two are 4-24% faster on
-// random lengths up to 256 (capacity <= 256); FP4 cache, two (one is
-// 18-30% slower); E4M3 cache, one while there are no more (sequence, KV
-// head) segments than CUs (1-4% faster: each workgroup then holds at most
-// about two segments), else two (5-33% faster on many short segments).
-// GQA_DECODE_WG_PER_CU overrides it.
+// caches of at most 256 rows when (sequence, KV head) segments outnumber
+// the CUs; FP4 cache, two (one is 18-30% slower); E4M3 cache, one for
+// caches of more than 256 rows with no more segments than CUs (1-12%
+// faster: each workgroup then holds at most about two segments), else two
+// (5-33% faster on many short segments). With few segments of at most 256
+// rows, the better choice depends on the lengths (full lengths: one
+// workgroup holds whole segments, two cut each in two; random lengths:
+// two spread the work wider), so both formats keep their earlier choice
+// there. GQA_DECODE_WG_PER_CU overrides it.
 // row_align (1, or 16 / 32 for paged caches) rounds the piece and cost sizes up.
 gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_align, int dtype,
                               long long segments, int capacity) {
@@ -149,8 +153,9 @@ gqa::SplitConfig split_config(const DeviceInfo& di, int forced_piece, int row_al
   const int resident = di.resident > 0 ? di.resident : 1;
   const int cus = di.cus > 0 ? di.cus : 256;
   const bool wide = dtype == GQA_DTYPE_F16 || dtype == GQA_DTYPE_BF16;
-  const bool one = (wide && capacity > kShortCapacity) ||
-                   (dtype == GQA_DTYPE_E4M3_KV && segments <= cus);
+  const bool short_cache = capacity <= kShortCapacity, few = segments <= cus;
+  const bool one = (wide && !(short_cache && !few)) ||
+                   (dtype == GQA_DTYPE_E4M3_KV && few && !short_cache);
   const int per_cu = env_int("GQA_DECODE_WG_PER_CU", one ? 1 : resident, 1, resident);
   cfg.pieces = cus * per_cu * per_slot;
   // With more than one workgroup per CU, the first `cus` of the grid (one per
