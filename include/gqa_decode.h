@@ -351,7 +351,7 @@ size_t gqa_decode_workspace_bytes(int batch, int capacity);
  * its previous size or more (below the limit, if one is set).
  * GQA_DECODE_LAUNCH_FORM sets the initial launch form (see
  * gqa_decode_set_launch_form). GQA_DECODE_COMBINE_MAX_GRID=<n> (1 .. 65536,
- * default 65536) caps the workgroups of the combine kernel, which then
+ * default 1024) caps the workgroups of the combine kernel, which then
  * take the segments in turns; results do not depend on it (used to test
  * those turns at small sizes).
  */

@@ -180,10 +180,10 @@ def test_single_launch_in_a_graph_with_lengths_changed_on_the_device():
     ("two long", 126, 65536, [65536, 40000]),
 ])
 def test_combine_workgroups_taking_units_in_turns_match_bitwise(monkeypatch, cap, spec):
-    # The combine kernel's grid is capped (at most 65536 workgroups; any
-    # batch then stays within one dispatch); each workgroup takes units
-    # w, w + grid, ... A tiny cap makes every workgroup take many units in
-    # turn, with the barrier between turns.
+    # The combine kernel's grid is capped (1024 workgroups by default, 65536
+    # at most; any batch then stays within one dispatch); each workgroup
+    # takes units w, w + grid, ... A tiny cap makes every workgroup take
+    # many units in turn, with the barrier between turns.
     torch = _torch()
     g = _g()
     name, seed, cap_rows, lens = spec
