@@ -97,7 +97,10 @@ def test_ragged_lengths_odd_capacity_and_clamping(chunk_len):
 @pytest.mark.parametrize("batch,cap,lo,hi", [(100, 512, 0, 300), (300, 128, 1, 64), (1000, 64, 0, 40)])
 def test_large_batches_use_the_block_level_plan(batch, cap, lo, hi):
     # Batches above 64 locate their rows with workgroup-wide scans (and
-    # above 256 with several passes over the lengths).
+    # above 256 with several passes over the lengths). The two short caches
+    # (128 and 64 rows, 2400 and 8000 segments) also run two workgroups per
+    # CU, and their combine kernels take more segments than workgroups
+    # (each workgroup merges several in turn).
     w = workloads.build(f"batch{batch}", 42 + batch, cap,
                         lambda r: r.integers(lo, hi, batch, endpoint=True), fill="nan")
     got = run(w)
